@@ -1,0 +1,91 @@
+"""Test-side helpers: paging contiguous K/V into a pool, and a contiguous
+brute-force attention used to pin the oracle.
+
+Nothing here is used by the GPU library or by the oracle itself.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from paged_gqa_decode_block_amd import workload as W
+
+
+def brute_force(q, Kc, Vc, scale, G):
+    """Contiguous fp64 attention, matrix form, no block table.
+
+    q: float [B, Hq, D]; Kc, Vc: lists (per sequence) of float64 [Hkv, L_b, D].
+    Returns float64 [B, Hq, D] (zeros for an empty sequence).
+    """
+    B, Hq, D = q.shape
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        if Kc[b].shape[1] == 0:
+            continue
+        for h in range(Hq):
+            kh = Kc[b][h // G]
+            vh = Vc[b][h // G]
+            s = float(scale) * (kh @ q[b, h].astype(np.float64))
+            w = np.exp(s - s.max())
+            out[b, h] = (w @ vh) / w.sum()
+    return out
+
+
+def paged_case(rng, *, B, Hq, Hkv, D, bs, kv_dtype, seqlens, layout="HND", spare=3, kv_std=1.0,
+               scale=None, q=None):
+    """Draw contiguous K/V per sequence, cut each sequence into pages of ``bs``
+    tokens and place the pages on randomly chosen distinct physical blocks.
+
+    Returns (case, Kc, Vc) where Kc/Vc are the contiguous float64 values (after
+    rounding to the storage type) that the paged pool holds.
+    """
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    pages = [-(-int(L) // bs) for L in seqlens]
+    NB = sum(pages) + spare
+    MBS = max(1, max(pages) + int(rng.integers(0, 3)))
+    ids = rng.permutation(NB).astype(np.int32)
+    table = np.full((B, MBS), -1, dtype=np.int32)
+    pool_dtype = np.float32 if kv_dtype == "f32" else np.uint16
+    shape = (NB + 1, Hkv, bs, D) if layout == "HND" else (NB + 1, bs, Hkv, D)
+    nan = np.float32(np.nan) if kv_dtype == "f32" else np.uint16(0x7FC0 if kv_dtype == "bf16" else 0x7E00)
+    k_store = np.full(shape, nan, dtype=pool_dtype)
+    v_store = np.full(shape, nan, dtype=pool_dtype)
+    if q is None:
+        q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    Kc, Vc = [], []
+    pos = 0
+    for b in range(B):
+        L = int(seqlens[b])
+        kb = W.to_storage((rng.standard_normal((Hkv, L, D)) * kv_std).astype(np.float32), kv_dtype)
+        vb = W.to_storage((rng.standard_normal((Hkv, L, D)) * kv_std).astype(np.float32), kv_dtype)
+        Kc.append(W.from_storage(kb, kv_dtype).astype(np.float64))
+        Vc.append(W.from_storage(vb, kv_dtype).astype(np.float64))
+        n = pages[b]
+        table[b, :n] = ids[pos:pos + n]
+        pos += n
+        for j in range(n):
+            lo, hi = j * bs, min(L, (j + 1) * bs)
+            blk = 1 + table[b, j]
+            if layout == "HND":
+                k_store[blk, :, : hi - lo, :] = kb[:, lo:hi, :]
+                v_store[blk, :, : hi - lo, :] = vb[:, lo:hi, :]
+            else:
+                k_store[blk, : hi - lo, :, :] = kb[:, lo:hi, :].transpose(1, 0, 2)
+                v_store[blk, : hi - lo, :, :] = vb[:, lo:hi, :].transpose(1, 0, 2)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    case = W.Case(
+        name="paged_random", kv_dtype=kv_dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, MBS=MBS,
+        seqlens=seqlens, block_table=table, q=q, k_store=k_store, v_store=v_store, layout=layout,
+        scale=float(np.float32(scale)),
+    )
+    return case, Kc, Vc
+
+
+def run_oracle(case, **kw):
+    from oracle import oracle as O
+
+    return O.paged_attn_decode(
+        case.q, case.k_pool, case.v_pool, case.block_table, case.seqlens, case.scale,
+        kv_dtype=case.kv_dtype, block_size=case.bs, num_kv_heads=case.Hkv, layout=case.layout, **kw)
