@@ -1,0 +1,169 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged GQA decode-attention library.
+ *
+ * The operation (page "Paged Attention Kernel Architecture for BI-V100", section 1
+ * "Problem Definition"): for each sequence b and query head h,
+ *
+ *     out[b,h,:] = softmax_t( scale * q[b,h,:] . K[t,:] ) . V[t,:],   0 <= t < L_b,
+ *
+ * where L_b = cache_seqlens[b] and token t of sequence b is stored in physical
+ * block block_table[b][t / block_size] at offset t % block_size (same page,
+ * section 3 "Paged K/V Gather"; the decode-path example of the transformers
+ * "Paged attention" docs page, where the table has shape (batch,
+ * max_blocks_per_seq) and -1 marks an unassigned entry). Query head h reads KV
+ * head h / G, G = num_q_heads / num_kv_heads: G consecutive query heads share one
+ * KV head (same page, section 4 "GQA Handling"). One query token per sequence.
+ *
+ * The work is split into KV partitions of partition_size tokens; each partition
+ * keeps a running softmax state (max, sum, unnormalised output) and a second
+ * kernel merges the partitions with the max-rescaling combine (same page,
+ * section 2 and section 6 "Kernel Launch Configuration"; page
+ * "v10_triton_paged_gqa", core principle, for the per-tile update).
+ *
+ * Conventions for every entry point:
+ *   - All array pointers given to paged_attn_decode are DEVICE pointers owned by
+ *     the caller; the library never frees or keeps them after the call returns.
+ *   - Nothing here allocates device memory. Partial results live in a caller
+ *     workspace of paged_attn_workspace_size() bytes.
+ *   - Functions return PA_OK (0) or a negative PA_E_* code; on error nothing is
+ *     launched and nothing aborts. paged_attn_strerror() names the code.
+ *   - Sizes are in elements unless they say bytes.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+/* Element type of the K and V caches. q and out are always float32. */
+typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype;
+
+/* Which partition kernel runs: VALU (vector ALU dot products and reductions) or
+ * MFMA (matrix-core micro-GEMMs for the G x d . d x N scores and the P . V
+ * product). AUTO picks per dtype and shape. MFMA needs f16 or bf16 K/V. */
+typedef enum pa_path { PA_PATH_AUTO = 0, PA_PATH_VALU = 1, PA_PATH_MFMA = 2 } pa_path;
+
+/* Status codes. */
+#define PA_OK 0
+#define PA_E_NULL (-1)        /* a required pointer is NULL                          */
+#define PA_E_SHAPE (-2)       /* sizes <= 0, batch or num_q_heads > 65535,           */
+                              /* num_q_heads % num_kv_heads != 0, or G beyond what   */
+                              /* the selected path supports (VALU: G <= 8, MFMA:     */
+                              /* G <= 16)                                            */
+#define PA_E_HEAD_DIM (-3)    /* head_dim not 64, 128 or 256                         */
+#define PA_E_BLOCK_SIZE (-4)  /* block_size not a power of two in [1, 1024]          */
+#define PA_E_DTYPE (-5)       /* kv_dtype not a pa_dtype                             */
+#define PA_E_STRIDE (-6)      /* a stride <= 0, token stride < head_dim, or a stride */
+                              /* that is not a multiple of 16 bytes                  */
+#define PA_E_ALIGN (-7)       /* q, out, k_cache or v_cache not 16-byte aligned      */
+#define PA_E_PARTITION (-8)   /* partition_size not 0 and not a multiple of 32 in    */
+                              /* [32, 16384], or spanning more than 1024 blocks       */
+#define PA_E_WORKSPACE (-9)   /* workspace NULL or smaller than required             */
+#define PA_E_PATH (-10)       /* path not a pa_path, or MFMA asked for f32 K/V        */
+#define PA_E_LAUNCH (-11)     /* the HIP runtime refused a launch                    */
+#define PA_E_TABLE (-12)      /* (check_inputs) an entry read for an attended token  */
+                              /* is outside [0, num_blocks)                           */
+#define PA_E_SEQLEN (-13)     /* (check_inputs) a cache length < 0 or > MBS * bs     */
+
+/* Bits the kernels OR into the optional device status word. */
+#define PA_STATUS_BAD_BLOCK 1   /* an attended token's table entry was outside [0, NB) */
+                                /* (that token was skipped, never dereferenced)        */
+#define PA_STATUS_BAD_SEQLEN 2  /* a cache length was < 0 or > MBS * bs (clamped)     */
+
+/*
+ * Shape and layout of one decode call.
+ *
+ * K and V caches: element (blk, head, off, i) of K is at
+ *   k_cache + blk * k_stride_block + head * k_stride_head + off * k_stride_token + i
+ * (same for V with the v_ strides), for blk < num_blocks, head < num_kv_heads,
+ * off < block_size, i < head_dim. head_dim is innermost and contiguous. The
+ * default layout [num_blocks, num_kv_heads, block_size, head_dim] has strides
+ * (H_kv*bs*d, bs*d, d); the token-major layout [num_blocks, block_size,
+ * num_kv_heads, head_dim] has (bs*H_kv*d, d, H_kv*d).
+ */
+typedef struct pa_desc {
+  int32_t batch;              /* B, number of sequences (0 is a no-op)            */
+  int32_t num_q_heads;        /* H_q                                              */
+  int32_t num_kv_heads;       /* H_kv; G = H_q / H_kv                             */
+  int32_t head_dim;           /* d: 64, 128 or 256                                */
+  int32_t block_size;         /* tokens per physical block, power of two <= 1024  */
+  int32_t num_blocks;         /* NB, physical blocks in the pool                  */
+  int32_t max_blocks_per_seq; /* MBS, columns of block_table                      */
+  int32_t kv_dtype;           /* pa_dtype                                         */
+  int64_t k_stride_block, k_stride_head, k_stride_token; /* elements              */
+  int64_t v_stride_block, v_stride_head, v_stride_token; /* elements              */
+  int32_t partition_size;     /* tokens per KV partition; 0 = library's choice    */
+  int32_t path;               /* pa_path                                          */
+} pa_desc;
+
+/*
+ * Decode attention for one batch, enqueued on `stream` (a hipStream_t; NULL is
+ * the default stream). Returns once two kernels are enqueued; it never
+ * synchronises the device.
+ *
+ *   q              float32 [B, H_q, d], contiguous, 16-byte aligned
+ *   k_cache,
+ *   v_cache        pools as described at pa_desc, 16-byte aligned
+ *   block_table    int32 [B, max_blocks_per_seq], row-major. Only the entries
+ *                  j < ceil(L_b / block_size) are read; -1 marks an unassigned
+ *                  entry and must not appear in that range.
+ *   cache_seqlens  int32 [B], L_b in [0, max_blocks_per_seq * block_size]
+ *   scale          multiplies q . k before the softmax (usually 1/sqrt(d))
+ *   out            float32 [B, H_q, d], contiguous, 16-byte aligned; L_b = 0
+ *                  gives zeros
+ *   workspace      device memory of at least paged_attn_workspace_size(desc)
+ *                  bytes (may be NULL when that size is 0), 256-byte aligned
+ *   status         optional device int32; the kernels OR PA_STATUS_* bits into
+ *                  it when a table entry or cache length is invalid. The caller
+ *                  clears it. NULL disables the report (invalid entries are still
+ *                  never dereferenced).
+ *
+ * Values inside the device arrays are not checked on the host (that would need a
+ * synchronisation); use paged_attn_check_inputs on host copies to vet them.
+ * Calls that share a workspace must be ordered on one stream.
+ */
+int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table,
+                      const int32_t* cache_seqlens, float scale, float* out, void* workspace,
+                      size_t workspace_bytes, int32_t* status, void* stream);
+
+/* Bytes of workspace paged_attn_decode needs for this descriptor: the partial
+ * (max, sum, output) of every possible partition, sized from
+ * max_blocks_per_seq * block_size. 0 when one partition always suffices.
+ * Returns 0 for an invalid descriptor too; call paged_attn_validate first. */
+size_t paged_attn_workspace_size(const pa_desc* desc);
+
+/* Checks the descriptor alone (host only, no device access). PA_OK or PA_E_*. */
+int paged_attn_validate(const pa_desc* desc);
+
+/* The partition size paged_attn_decode will use (tokens), or a negative PA_E_*. */
+int paged_attn_partition_size(const pa_desc* desc);
+
+/* The path paged_attn_decode will run (PA_PATH_VALU or PA_PATH_MFMA), or a
+ * negative PA_E_* when the descriptor is invalid. */
+int paged_attn_resolved_path(const pa_desc* desc);
+
+/* Host-side, synchronous check of the device arrays' VALUES on host copies:
+ * every cache length in [0, MBS * bs] and every table entry read for an
+ * attended token in [0, num_blocks). Returns PA_OK, PA_E_SEQLEN or PA_E_TABLE
+ * (or a descriptor error). Touches no device. */
+int paged_attn_check_inputs(const pa_desc* desc, const int32_t* block_table_host,
+                            const int32_t* cache_seqlens_host);
+
+/* Static text for a status code. */
+const char* paged_attn_strerror(int status);
+
+/* PA_ABI_VERSION of the built library. */
+int paged_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

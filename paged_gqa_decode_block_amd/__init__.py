@@ -1,1 +1,103 @@
-"""Placeholder; the binding is written next."""
+"""Paged GQA decode attention for MI355X (gfx950).
+
+``paged_attn_decode`` computes, for every sequence b and query head h, the
+softmax-weighted sum of V over the ``cache_seqlens[b]`` tokens the block table
+maps into a paged K/V pool, with G = H_q / H_kv query heads sharing each KV head.
+The work runs in the HIP kernels of ``libpagedattn.so`` (C ABI in
+``include/paged_attn.h``); this package only marshals torch tensors into that
+call. Build the library with ``python -m paged_gqa_decode_block_amd.build``.
+"""
+from __future__ import annotations
+
+from ._lib import (  # noqa: F401
+    EXPORTED, LIB_PATH, PA_DTYPE, PA_PATH, PA_STATUS_BAD_BLOCK, PA_STATUS_BAD_SEQLEN, PATH_NAME,
+    PaDesc, PagedAttnError, check_inputs, decode_raw, load_library, make_desc, partition_size,
+    resolved_path, strerror, validate, workspace_size,
+)
+
+_TORCH_DTYPE_NAME = {"torch.float32": "f32", "torch.float16": "f16", "torch.bfloat16": "bf16"}
+_ws_cache: dict = {}
+
+
+def _kv_dtype(t) -> str:
+    name = str(t.dtype)
+    if name not in _TORCH_DTYPE_NAME:
+        raise TypeError(f"K/V dtype {t.dtype} is not float32, float16 or bfloat16")
+    return _TORCH_DTYPE_NAME[name]
+
+
+def desc_for(q, k_cache, v_cache, block_table, *, layout="HND", partition_size=0, path="auto"):
+    """Descriptor for torch tensors. ``k_cache``/``v_cache`` are [NB, H_kv, bs, d]
+    ("HND") or [NB, bs, H_kv, d] ("NHD"), any strides with d contiguous."""
+    B, Hq, D = q.shape
+    if layout == "HND":
+        NB, Hkv, bs, D2 = k_cache.shape
+        ks = (k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
+        vs = (v_cache.stride(0), v_cache.stride(1), v_cache.stride(2))
+    elif layout == "NHD":
+        NB, bs, Hkv, D2 = k_cache.shape
+        ks = (k_cache.stride(0), k_cache.stride(2), k_cache.stride(1))
+        vs = (v_cache.stride(0), v_cache.stride(2), v_cache.stride(1))
+    else:
+        raise ValueError(f"layout must be 'HND' or 'NHD', got {layout!r}")
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q, k_cache and v_cache disagree on shape")
+    if k_cache.stride(3) != 1 or v_cache.stride(3) != 1:
+        raise ValueError("head_dim must be the contiguous axis of k_cache and v_cache")
+    return make_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                     num_blocks=NB, max_blocks_per_seq=block_table.shape[1],
+                     kv_dtype=_kv_dtype(k_cache), k_strides=ks, v_strides=vs,
+                     partition_size=partition_size, path=path)
+
+
+def workspace_for(desc: PaDesc, device):
+    """A cached device workspace of at least workspace_size(desc) bytes."""
+    import torch
+
+    n = workspace_size(desc)
+    if n == 0:
+        return None
+    key = (str(device),)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < n:
+        ws = torch.empty(n, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, out=None, *,
+                      layout="HND", partition_size=0, path="auto", workspace=None, status=None,
+                      stream=None):
+    """Single-query paged GQA attention; returns ``out`` (float32 [B, H_q, d]).
+
+    q float32 [B, H_q, d]; block_table int32 [B, MBS]; cache_seqlens int32 [B];
+    all on one GPU. Enqueued on ``stream`` (default: torch's current stream).
+    ``status`` is an optional int32 device tensor the kernels OR error bits into.
+    """
+    import torch
+
+    if not q.is_cuda:
+        raise ValueError("paged_attn_decode runs on the GPU; q is on the CPU")
+    for name, t, dt in (("q", q, torch.float32), ("block_table", block_table, torch.int32),
+                        ("cache_seqlens", cache_seqlens, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    desc = desc_for(q, k_cache, v_cache, block_table, layout=layout,
+                    partition_size=partition_size, path=path)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = workspace_for(desc, q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = decode_raw(
+        desc, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        cache_seqlens.data_ptr(), float(scale), out.data_ptr(),
+        workspace.data_ptr() if workspace is not None else 0,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        status.data_ptr() if status is not None else 0, int(stream))
+    if rc != 0:
+        raise PagedAttnError(rc, "paged_attn_decode: ")
+    return out

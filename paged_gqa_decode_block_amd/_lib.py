@@ -1,0 +1,148 @@
+"""ctypes binding of libpagedattn.so (the C ABI in include/paged_attn.h).
+
+Argument marshalling only: every step of the decode runs in the library's HIP
+kernels. PyTorch supplies device memory and the current stream. If the library
+is not built this module raises on first use; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpagedattn.so")
+
+PA_DTYPE = {"f32": 0, "f16": 1, "bf16": 2}
+PA_PATH = {"auto": 0, "valu": 1, "mfma": 2}
+PATH_NAME = {1: "valu", 2: "mfma"}
+
+PA_OK = 0
+PA_E = {
+    -1: "PA_E_NULL", -2: "PA_E_SHAPE", -3: "PA_E_HEAD_DIM", -4: "PA_E_BLOCK_SIZE",
+    -5: "PA_E_DTYPE", -6: "PA_E_STRIDE", -7: "PA_E_ALIGN", -8: "PA_E_PARTITION",
+    -9: "PA_E_WORKSPACE", -10: "PA_E_PATH", -11: "PA_E_LAUNCH", -12: "PA_E_TABLE",
+    -13: "PA_E_SEQLEN",
+}
+PA_STATUS_BAD_BLOCK = 1
+PA_STATUS_BAD_SEQLEN = 2
+
+EXPORTED = (
+    "paged_attn_decode", "paged_attn_workspace_size", "paged_attn_validate",
+    "paged_attn_partition_size", "paged_attn_resolved_path", "paged_attn_check_inputs",
+    "paged_attn_strerror", "paged_attn_abi_version",
+)
+
+
+class PaDesc(ctypes.Structure):
+    """Mirror of ``pa_desc``."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_stride_block", ctypes.c_int64),
+        ("k_stride_head", ctypes.c_int64),
+        ("k_stride_token", ctypes.c_int64),
+        ("v_stride_block", ctypes.c_int64),
+        ("v_stride_head", ctypes.c_int64),
+        ("v_stride_token", ctypes.c_int64),
+        ("partition_size", ctypes.c_int32),
+        ("path", ctypes.c_int32),
+    ]
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, code: int, where: str = ""):
+        self.code = code
+        super().__init__(f"{where}{PA_E.get(code, code)}: {strerror(code)}")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpagedattn.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m paged_gqa_decode_block_amd.build` "
+            "(hipcc, --offload-arch=gfx950). There is no CPU fallback.")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    dp = ctypes.POINTER(PaDesc)
+    lib.paged_attn_decode.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp, vp]
+    lib.paged_attn_decode.restype = i32
+    lib.paged_attn_workspace_size.argtypes = [dp]
+    lib.paged_attn_workspace_size.restype = sz
+    lib.paged_attn_validate.argtypes = [dp]
+    lib.paged_attn_validate.restype = i32
+    lib.paged_attn_partition_size.argtypes = [dp]
+    lib.paged_attn_partition_size.restype = i32
+    lib.paged_attn_resolved_path.argtypes = [dp]
+    lib.paged_attn_resolved_path.restype = i32
+    lib.paged_attn_check_inputs.argtypes = [dp, vp, vp]
+    lib.paged_attn_check_inputs.restype = i32
+    lib.paged_attn_strerror.argtypes = [i32]
+    lib.paged_attn_strerror.restype = ctypes.c_char_p
+    lib.paged_attn_abi_version.argtypes = []
+    lib.paged_attn_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().paged_attn_strerror(int(code)).decode()
+
+
+def make_desc(*, batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+              max_blocks_per_seq, kv_dtype, k_strides, v_strides=None, partition_size=0,
+              path="auto") -> PaDesc:
+    v_strides = k_strides if v_strides is None else v_strides
+    return PaDesc(
+        int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
+        int(num_blocks), int(max_blocks_per_seq),
+        PA_DTYPE[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype),
+        *[int(x) for x in k_strides], *[int(x) for x in v_strides], int(partition_size),
+        PA_PATH[path] if isinstance(path, str) else int(path))
+
+
+def validate(desc: PaDesc) -> int:
+    return load_library().paged_attn_validate(ctypes.byref(desc))
+
+
+def workspace_size(desc: PaDesc) -> int:
+    return int(load_library().paged_attn_workspace_size(ctypes.byref(desc)))
+
+
+def partition_size(desc: PaDesc) -> int:
+    return int(load_library().paged_attn_partition_size(ctypes.byref(desc)))
+
+
+def resolved_path(desc: PaDesc) -> int:
+    return int(load_library().paged_attn_resolved_path(ctypes.byref(desc)))
+
+
+def check_inputs(desc: PaDesc, block_table_host, seqlens_host) -> int:
+    """Host-side value check of numpy int32 copies of the table and lengths."""
+    import numpy as np
+
+    t = np.ascontiguousarray(block_table_host, dtype=np.int32)
+    s = np.ascontiguousarray(seqlens_host, dtype=np.int32)
+    return load_library().paged_attn_check_inputs(ctypes.byref(desc), t.ctypes.data, s.ctypes.data)
+
+
+def decode_raw(desc: PaDesc, q_ptr: int, k_ptr: int, v_ptr: int, table_ptr: int, seqlens_ptr: int,
+               scale: float, out_ptr: int, ws_ptr: int, ws_bytes: int, status_ptr: int,
+               stream: int) -> int:
+    """Direct call of paged_attn_decode with integer device addresses."""
+    return load_library().paged_attn_decode(
+        ctypes.byref(desc), q_ptr or None, k_ptr or None, v_ptr or None, table_ptr or None,
+        seqlens_ptr or None, ctypes.c_float(scale), out_ptr or None, ws_ptr or None, ws_bytes,
+        status_ptr or None, stream or None)

@@ -1,0 +1,203 @@
+// pa_api.hip -- the extern "C" entry points declared in include/paged_attn.h:
+// descriptor validation, workspace sizing, path and partition-size selection,
+// host-side value checks, and the two launches of a decode call.
+#include <string.h>
+
+#include "../../include/paged_attn.h"
+#include "pa_kernels.h"
+
+namespace {
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+int elem_bytes(int dtype) { return dtype == PA_DTYPE_F32 ? 4 : 2; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t max_tokens(const pa_desc* d) { return (int64_t)d->max_blocks_per_seq * d->block_size; }
+
+// Partition size for a descriptor that passed validation of everything else.
+// Without a caller choice: 512 tokens, halved (down to 64) while the busiest
+// possible grid would hold fewer than 1024 work items.
+int pick_partition(const pa_desc* d) {
+  if (d->partition_size > 0) return d->partition_size;
+  const int64_t T = max_tokens(d);
+  int part = 512;
+  while (part > 64 && (int64_t)d->batch * d->num_kv_heads * ((T + part - 1) / part) < 1024)
+    part >>= 1;
+  // keep within the LDS block-id table
+  while ((part >> ilog2(d->block_size)) + 2 > pa::kTableCap && part > 32) part >>= 1;
+  return part;
+}
+
+int pick_path(const pa_desc* d) {
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (d->path == PA_PATH_VALU) return pa::valu_supports(d->kv_dtype, d->head_dim, G) ? PA_PATH_VALU : PA_E_SHAPE;
+  if (d->path == PA_PATH_MFMA) {
+    if (d->kv_dtype == PA_DTYPE_F32) return PA_E_PATH;
+    return pa::mfma_supports(d->kv_dtype, d->head_dim, G) ? PA_PATH_MFMA : PA_E_SHAPE;
+  }
+  // AUTO: matrix cores for 16-bit K/V, vector ALUs for fp32
+  if (d->kv_dtype != PA_DTYPE_F32 && pa::mfma_supports(d->kv_dtype, d->head_dim, G)) return PA_PATH_MFMA;
+  if (pa::valu_supports(d->kv_dtype, d->head_dim, G)) return PA_PATH_VALU;
+  return PA_E_SHAPE;
+}
+
+int validate(const pa_desc* d) {
+  if (!d) return PA_E_NULL;
+  if (d->batch < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_blocks <= 0 ||
+      d->max_blocks_per_seq <= 0)
+    return PA_E_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads) return PA_E_SHAPE;
+  // grid dimensions y and z carry heads and sequences
+  if (d->batch > 65535 || d->num_q_heads > 65535) return PA_E_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return PA_E_HEAD_DIM;
+  if (!is_pow2(d->block_size) || d->block_size > 1024) return PA_E_BLOCK_SIZE;
+  if (d->kv_dtype != PA_DTYPE_F32 && d->kv_dtype != PA_DTYPE_F16 && d->kv_dtype != PA_DTYPE_BF16)
+    return PA_E_DTYPE;
+  if (max_tokens(d) > (int64_t)1 << 30) return PA_E_SHAPE;
+  const int64_t eb = elem_bytes(d->kv_dtype);
+  const int64_t st[6] = {d->k_stride_block, d->k_stride_head, d->k_stride_token,
+                         d->v_stride_block, d->v_stride_head, d->v_stride_token};
+  for (int i = 0; i < 6; ++i)
+    if (st[i] <= 0 || (st[i] * eb) % 16) return PA_E_STRIDE;
+  if (d->k_stride_token < d->head_dim || d->v_stride_token < d->head_dim) return PA_E_STRIDE;
+  if (d->path != PA_PATH_AUTO && d->path != PA_PATH_VALU && d->path != PA_PATH_MFMA) return PA_E_PATH;
+  if (d->partition_size != 0) {
+    const int ps = d->partition_size;
+    if (ps < 32 || ps > 16384 || ps % 32) return PA_E_PARTITION;
+    if ((ps >> ilog2(d->block_size)) + 2 > pa::kTableCap) return PA_E_PARTITION;
+  }
+  const int path = pick_path(d);
+  return path < 0 ? path : PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_abi_version(void) { return PA_ABI_VERSION; }
+
+int paged_attn_validate(const pa_desc* desc) { return validate(desc); }
+
+int paged_attn_partition_size(const pa_desc* desc) {
+  const int rc = validate(desc);
+  return rc != PA_OK ? rc : pick_partition(desc);
+}
+
+int paged_attn_resolved_path(const pa_desc* desc) {
+  const int rc = validate(desc);
+  return rc != PA_OK ? rc : pick_path(desc);
+}
+
+size_t paged_attn_workspace_size(const pa_desc* desc) {
+  if (validate(desc) != PA_OK) return 0;
+  const int part = pick_partition(desc);
+  const int64_t pmax = (max_tokens(desc) + part - 1) / part;
+  if (pmax <= 1) return 0;
+  const size_t rows = (size_t)desc->batch * desc->num_q_heads * (size_t)pmax;
+  return 2 * align256(rows * sizeof(float)) + align256(rows * desc->head_dim * sizeof(float));
+}
+
+int paged_attn_check_inputs(const pa_desc* desc, const int32_t* table, const int32_t* seqlens) {
+  const int rc = validate(desc);
+  if (rc != PA_OK) return rc;
+  if (desc->batch > 0 && (!table || !seqlens)) return PA_E_NULL;
+  const int64_t lmax = max_tokens(desc);
+  for (int b = 0; b < desc->batch; ++b) {
+    const int L = seqlens[b];
+    if (L < 0 || L > lmax) return PA_E_SEQLEN;
+    const int nblk = (L + desc->block_size - 1) / desc->block_size;
+    const int32_t* row = table + (int64_t)b * desc->max_blocks_per_seq;
+    for (int j = 0; j < nblk; ++j)
+      if (row[j] < 0 || row[j] >= desc->num_blocks) return PA_E_TABLE;
+  }
+  return PA_OK;
+}
+
+const char* paged_attn_strerror(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_E_NULL: return "a required pointer is NULL";
+    case PA_E_SHAPE: return "unsupported or inconsistent sizes (batch, heads, blocks, or G for this path)";
+    case PA_E_HEAD_DIM: return "head_dim must be 64, 128 or 256";
+    case PA_E_BLOCK_SIZE: return "block_size must be a power of two in [1, 1024]";
+    case PA_E_DTYPE: return "kv_dtype must be PA_DTYPE_F32, PA_DTYPE_F16 or PA_DTYPE_BF16";
+    case PA_E_STRIDE: return "K/V strides must be positive multiples of 16 bytes, token stride >= head_dim";
+    case PA_E_ALIGN: return "q, out, k_cache and v_cache must be 16-byte aligned";
+    case PA_E_PARTITION: return "partition_size must be 0 or a multiple of 32 in [32, 16384] spanning <= 1022 blocks";
+    case PA_E_WORKSPACE: return "workspace missing or smaller than paged_attn_workspace_size()";
+    case PA_E_PATH: return "path must be a pa_path; the MFMA path needs f16 or bf16 K/V";
+    case PA_E_LAUNCH: return "the HIP runtime refused a kernel launch";
+    case PA_E_TABLE: return "a block_table entry for an attended token is outside [0, num_blocks)";
+    case PA_E_SEQLEN: return "a cache length is negative or beyond max_blocks_per_seq * block_size";
+  }
+  return "unknown status";
+}
+
+int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* cache_seqlens, float scale,
+                      float* out, void* workspace, size_t workspace_bytes, int32_t* status,
+                      void* stream) {
+  int rc = validate(desc);
+  if (rc != PA_OK) return rc;
+  if (desc->batch == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !cache_seqlens || !out) return PA_E_NULL;
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15) return PA_E_ALIGN;
+  const size_t need = paged_attn_workspace_size(desc);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)))
+    return PA_E_WORKSPACE;
+
+  const int part = pick_partition(desc);
+  const int path = pick_path(desc);
+  pa::Params p;
+  memset(&p, 0, sizeof p);
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.table = block_table;
+  p.seqlens = cache_seqlens;
+  p.out = out;
+  p.status = status;
+  p.ksb = desc->k_stride_block;
+  p.ksh = desc->k_stride_head;
+  p.kst = desc->k_stride_token;
+  p.vsb = desc->v_stride_block;
+  p.vsh = desc->v_stride_head;
+  p.vst = desc->v_stride_token;
+  p.B = desc->batch;
+  p.Hq = desc->num_q_heads;
+  p.Hkv = desc->num_kv_heads;
+  p.G = desc->num_q_heads / desc->num_kv_heads;
+  p.D = desc->head_dim;
+  p.bs_log2 = ilog2(desc->block_size);
+  p.NB = desc->num_blocks;
+  p.MBS = desc->max_blocks_per_seq;
+  p.part = part;
+  p.pmax = (int)((max_tokens(desc) + part - 1) / part);
+  p.qscale = scale * 1.4426950408889634f;  // log2(e): scores in base-2 units
+  if (need > 0) {
+    const size_t rows = (size_t)p.B * p.Hq * (size_t)p.pmax;
+    char* ws = (char*)workspace;
+    p.ws_m = (float*)ws;
+    p.ws_l = (float*)(ws + align256(rows * sizeof(float)));
+    p.ws_acc = (float*)(ws + 2 * align256(rows * sizeof(float)));
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = path == PA_PATH_MFMA ? pa::launch_partition_mfma(p, desc->kv_dtype, s)
+                                      : pa::launch_partition_valu(p, desc->kv_dtype, s);
+  if (e != hipSuccess) return PA_E_LAUNCH;
+  if (p.pmax > 1) {
+    e = pa::launch_combine(p, s);
+    if (e != hipSuccess) return PA_E_LAUNCH;
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

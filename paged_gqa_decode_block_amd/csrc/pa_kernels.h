@@ -1,0 +1,77 @@
+// pa_kernels.h -- internal to the gfx950 library: launch parameters, device
+// helpers and the launcher declarations shared by the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Largest number of physical blocks one partition may span; the partition
+// kernels stage that many block ids in LDS.
+constexpr int kTableCap = 1024;
+
+struct Params {
+  const float* q;           // [B, Hq, D]
+  const void* k;            // pool, element strides below
+  const void* v;
+  const int32_t* table;     // [B, MBS]
+  const int32_t* seqlens;   // [B]
+  float* out;               // [B, Hq, D]
+  float* ws_m;              // [B, Hq, pmax]  running max, base-2 units
+  float* ws_l;              // [B, Hq, pmax]  sum of 2^(s - m)
+  float* ws_acc;            // [B, Hq, pmax, D] unnormalised output
+  int32_t* status;          // optional
+  int64_t ksb, ksh, kst;    // K strides (elements)
+  int64_t vsb, vsh, vst;    // V strides
+  int B, Hq, Hkv, G, D;
+  int bs_log2, NB, MBS;
+  int part;                 // partition size in tokens
+  int pmax;                 // ceil(MBS * bs / part)
+  float qscale;             // scale * log2(e): scores are kept in base-2 units
+};
+
+enum { kStatusBadBlock = 1, kStatusBadSeqlen = 2 };
+
+// Launchers (each returns the launch error, hipSuccess when enqueued).
+hipError_t launch_partition_valu(const Params& p, int dtype, hipStream_t s);
+hipError_t launch_partition_mfma(const Params& p, int dtype, hipStream_t s);
+hipError_t launch_combine(const Params& p, hipStream_t s);
+bool valu_supports(int dtype, int D, int G);
+bool mfma_supports(int dtype, int D, int G);
+
+#if defined(__HIPCC__)
+
+// ---- device helpers --------------------------------------------------------
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cache length of sequence b, clamped to [0, MBS * bs] (a bad value is reported).
+__device__ __forceinline__ int clamped_len(const Params& p, int b, bool report) {
+  int L = p.seqlens[b];
+  const int lmax = p.MBS << p.bs_log2;
+  if (L < 0 || L > lmax) {
+    if (report && p.status) atomicOr(p.status, kStatusBadSeqlen);
+    L = L < 0 ? 0 : lmax;
+  }
+  return L;
+}
+
+// Stage the physical ids of blocks [j0, j1] of sequence b in LDS; an id outside
+// [0, NB) becomes -1 (never dereferenced) and is reported.
+__device__ __forceinline__ void stage_block_ids(const Params& p, int b, int j0, int j1, int* s_ids,
+                                                int tid, int nthreads) {
+  const int32_t* row = p.table + (int64_t)b * p.MBS;
+  for (int j = j0 + tid; j <= j1; j += nthreads) {
+    int id = row[j];
+    if (id < 0 || id >= p.NB) {
+      if (p.status) atomicOr(p.status, kStatusBadBlock);
+      id = -1;
+    }
+    s_ids[j - j0] = id;
+  }
+}
+
+#endif  // __HIPCC__
+
+}  // namespace pa

@@ -1,0 +1,147 @@
+"""The C ABI on the host: the library loads, exports what the header declares, the
+ctypes descriptor matches the C struct, and every argument error is returned
+before any device work (these tests never touch a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import paged_gqa_decode_block_amd as pa
+from paged_gqa_decode_block_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(paged_attn_\w+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = pa.load_library()
+    declared = _header_functions()
+    assert set(declared) == set(_lib.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+    assert lib.paged_attn_abi_version() == 1
+
+
+def test_descriptor_layout_matches_c(tmp_path):
+    fields = [f for f, _ in pa.PaDesc._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "paged_attn.h"\n'
+        "int main(void) { printf(\"%zu\", sizeof(pa_desc));\n"
+        + "".join(f'  printf(" %zu", offsetof(pa_desc, {f}));\n' for f in fields)
+        + "  return 0; }\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(pa.PaDesc)] + [getattr(pa.PaDesc, f).offset for f in fields]
+    assert got == want
+
+
+def _desc(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, num_blocks=64,
+                max_blocks_per_seq=16, kv_dtype="bf16", k_strides=(2 * 16 * 128, 16 * 128, 128),
+                partition_size=0, path="auto")
+    base.update(kw)
+    return pa.make_desc(**base)
+
+
+def test_valid_descriptor_and_resolved_path():
+    assert pa.validate(_desc()) == 0
+    assert pa.PATH_NAME[pa.resolved_path(_desc())] == "mfma"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(kv_dtype="f32", k_strides=(4096, 2048, 128)))] == "valu"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(path="valu"))] == "valu"
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_q_heads=7), -2),                 # H_q % H_kv
+    (dict(batch=-1), -2),
+    (dict(num_blocks=0), -2),
+    (dict(head_dim=96), -3),
+    (dict(block_size=24), -4),
+    (dict(block_size=2048), -4),
+    (dict(kv_dtype=7), -5),
+    (dict(k_strides=(4096, 2048, 100)), -6),   # token stride < head_dim
+    (dict(k_strides=(4096, 2048, 132)), -6),   # not a multiple of 16 bytes
+    (dict(k_strides=(0, 2048, 128)), -6),
+    (dict(partition_size=48), -8),
+    (dict(partition_size=16), -8),
+    (dict(partition_size=32768), -8),
+    (dict(block_size=1, partition_size=2048), -8),  # spans more than the block-id table
+    (dict(path=9), -10),
+    (dict(kv_dtype="f32", k_strides=(4096, 2048, 128), path="mfma"), -10),
+    (dict(num_q_heads=2 * 12, path="valu"), -2),   # G = 12 beyond the VALU path
+    (dict(num_q_heads=2 * 17), -2),                # G = 17 beyond every path
+])
+def test_descriptor_errors(kw, code):
+    d = _desc(**kw)
+    assert pa.validate(d) == code
+    assert pa.workspace_size(d) == 0
+    assert pa.strerror(code) not in ("", "unknown status")
+
+
+def test_partition_size_choice_and_workspace():
+    d = _desc(partition_size=512)
+    assert pa.partition_size(d) == 512
+    # pmax = ceil(16*16 / 512) = 1: no partial states needed
+    assert pa.workspace_size(d) == 0
+    d = _desc(partition_size=64)
+    pmax = 256 // 64
+    rows = 2 * 8 * pmax
+    al = lambda x: (x + 255) // 256 * 256
+    assert pa.workspace_size(d) == 2 * al(rows * 4) + al(rows * 128 * 4)
+    # automatic choice: halves from 512 while the grid would be small
+    auto = pa.partition_size(_desc(batch=1, max_blocks_per_seq=6250, num_blocks=6250))
+    assert auto in (64, 128, 256, 512)
+    big = pa.partition_size(_desc(batch=64, num_kv_heads=8, num_q_heads=64,
+                                  max_blocks_per_seq=2048, num_blocks=50000))
+    assert big == 512
+    # monotone in batch and in max_blocks_per_seq
+    sizes = [pa.workspace_size(_desc(batch=b, partition_size=32)) for b in (1, 2, 4, 8)]
+    assert sizes == sorted(sizes) and sizes[0] > 0
+    sizes = [pa.workspace_size(_desc(max_blocks_per_seq=m, partition_size=32)) for m in (4, 8, 16, 32)]
+    assert sizes == sorted(sizes)
+
+
+def test_check_inputs_on_host_copies():
+    d = _desc(batch=3, max_blocks_per_seq=4, block_size=16, num_blocks=10)
+    table = np.array([[0, 1, -1, -1], [2, -1, -1, -1], [3, 4, 5, 6]], dtype=np.int32)
+    L = np.array([20, 16, 64], dtype=np.int32)
+    assert pa.check_inputs(d, table, L) == 0
+    t2 = table.copy(); t2[0, 1] = -1
+    assert pa.check_inputs(d, t2, L) == -12           # -1 inside the attended range
+    t2 = table.copy(); t2[2, 3] = 10
+    assert pa.check_inputs(d, t2, L) == -12           # id >= num_blocks
+    L2 = L.copy(); L2[2] = 65
+    assert pa.check_inputs(d, table, L2) == -13       # beyond MBS * bs
+    L2 = L.copy(); L2[1] = -1
+    assert pa.check_inputs(d, table, L2) == -13
+    L2 = L.copy(); L2[0] = 0
+    assert pa.check_inputs(d, table, L2) == 0         # empty sequence reads nothing
+
+
+def test_decode_argument_errors_return_before_device_work():
+    d = _desc()
+    good = 1 << 20  # never dereferenced: every call below fails validation first
+    args = dict(q_ptr=good, k_ptr=good, v_ptr=good, table_ptr=good, seqlens_ptr=good, scale=1.0,
+                out_ptr=good, ws_ptr=0, ws_bytes=0, status_ptr=0, stream=0)
+    assert pa.decode_raw(_desc(head_dim=100), **args) == -3
+    assert pa.decode_raw(d, **{**args, "q_ptr": 0}) == -1
+    assert pa.decode_raw(d, **{**args, "out_ptr": good + 8}) == -7
+    dw = _desc(partition_size=64)
+    assert pa.workspace_size(dw) > 0
+    assert pa.decode_raw(dw, **args) == -9                                   # no workspace
+    assert pa.decode_raw(dw, **{**args, "ws_ptr": good, "ws_bytes": 16}) == -9  # too small
+    assert pa.decode_raw(dw, **{**args, "ws_ptr": good + 16,
+                                "ws_bytes": pa.workspace_size(dw)}) == -9    # misaligned
+    assert pa.decode_raw(_desc(batch=0), **{**args, "q_ptr": 0}) == 0        # nothing to do
