@@ -1,0 +1,307 @@
+"""Decode-attention throughput on one MI355X: KV GB/s, % of HBM peak, seq-heads/s.
+
+A step is one decode call (partition kernel + combine kernel) over the whole
+synthetic batch, inputs resident in HBM. Default workload: the 64-sequence
+large-GQA bf16 batch (B=64, H_q=64, H_kv=8, d=128, bs=16, lengths log-uniform in
+[1024, 32768], 10% spare blocks); the 100K-token Qwen3.6-shaped batch (B=1,
+H_q=24, H_kv=4, d=256, partition 512) is measured too and reported under
+"also". Prints one JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--config 4] [--also 3]
+  python bench.py --profile partition   # only partition-kernel launches (for rocprofv3)
+  python bench.py --profile copy        # a 1 GiB device copy (counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8.0 TB/s
+METRIC = "decode attention KV GB/s (% of MI355X HBM peak) + seq-heads/s, 1 GPU"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
+KERNEL_SOURCES = ["paged_gqa_decode_block_amd/csrc/pa_partition_mfma.hip",
+                  "paged_gqa_decode_block_amd/csrc/pa_partition_valu.hip",
+                  "paged_gqa_decode_block_amd/csrc/pa_combine.hip",
+                  "paged_gqa_decode_block_amd/csrc/pa_kernels.h",
+                  "paged_gqa_decode_block_amd/csrc/pa_api.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Workload:
+    """One generated configuration, copied to the GPU once."""
+
+    def __init__(self, k: int, torch, path: str):
+        from paged_gqa_decode_block_amd import workload as W
+        import paged_gqa_decode_block_amd as pa
+
+        t = time.time()
+        self.case = c = W.make_config(k)
+        log(f"[bench] generated config {k} ({c.name}) in {time.time() - t:.1f}s")
+        self.k = k
+        self.torch = torch
+        self.path = path
+
+        def pool(store):
+            if c.kv_dtype == "f32":
+                x = torch.from_numpy(np.ascontiguousarray(store))
+            else:
+                x = torch.from_numpy(np.ascontiguousarray(store).view(np.int16)).view(
+                    torch.bfloat16 if c.kv_dtype == "bf16" else torch.float16)
+            return x.to("cuda")[1:]
+
+        self.q = torch.from_numpy(c.q).to("cuda")
+        self.k_pool = pool(c.k_store)
+        self.v_pool = pool(c.v_store)
+        self.table = torch.from_numpy(c.block_table).to("cuda")
+        self.seqlens = torch.from_numpy(c.seqlens).to("cuda")
+        self.out = torch.empty_like(self.q)
+        self.desc = pa.desc_for(self.q, self.k_pool, self.v_pool, self.table, layout=c.layout,
+                                partition_size=c.partition_size, path=path)
+        n = pa.workspace_size(self.desc)
+        self.ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+        self.part = pa.partition_size(self.desc)
+        self.path_name = pa.PATH_NAME[pa.resolved_path(self.desc)]
+        self.kv_bytes = c.kv_bytes()
+        self.unique_kv_bytes = c.unique_kv_bytes() if c.ref_count is not None else self.kv_bytes
+        self.stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+
+    def call(self, phase="both"):
+        import paged_gqa_decode_block_amd as pa
+
+        rc = pa.decode_raw(self.desc, self.q.data_ptr(), self.k_pool.data_ptr(),
+                           self.v_pool.data_ptr(), self.table.data_ptr(), self.seqlens.data_ptr(),
+                           self.case.scale, self.out.data_ptr(), self.ws.data_ptr(),
+                           self.ws.numel(), 0, self.stream.cuda_stream, phase)
+        if rc != 0:
+            raise pa.PagedAttnError(rc, "bench: ")
+
+    def describe(self) -> dict:
+        c = self.case
+        return {
+            "workload": c.name, "batch": c.B, "num_q_heads": c.Hq, "num_kv_heads": c.Hkv,
+            "head_dim": c.D, "block_size": c.bs, "kv_dtype": c.kv_dtype, "layout": c.layout,
+            "partition_size": self.part, "path": self.path_name,
+            "total_cached_tokens": int(c.seqlens.astype(np.int64).sum()),
+            "num_physical_blocks": c.NB, "seed": 1000 + self.k,
+        }
+
+
+def time_steps(torch, fn, steps: int) -> float:
+    """ms per call of fn over `steps` back-to-back calls, HIP events on the launch stream."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_each(torch, fn, steps: int, flush=None) -> np.ndarray:
+    """Per-call ms with an event pair around each call (optionally after a cache flush)."""
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        if flush is not None:
+            flush()
+        a.record(s)
+        fn()
+        b.record(s)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def measure(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
+    torch = wl.torch
+    for _ in range(warmup):
+        wl.call()
+    ms = time_steps(torch, wl.call, steps)
+    part_ms = time_each(torch, lambda: wl.call("partition"), steps)
+    wl.call()  # leave the workspace of a complete call behind for the combine timing
+    comb_ms = time_each(torch, lambda: wl.call("combine"), steps)
+    cold_ms = time_each(torch, wl.call, max(5, steps // 4), flush=lambda: flush_buf.add_(1))
+    c = wl.case
+    t = ms / 1e3
+    return {
+        "ms_per_step": ms,
+        "kv_gbs": wl.kv_bytes / t / 1e9,
+        "seq_heads_per_s": c.B * c.Hq / t,
+        "partition_kernel_us": float(part_ms.mean() * 1e3),
+        "partition_kernel_us_p10_p90": [float(np.percentile(part_ms, 10) * 1e3),
+                                        float(np.percentile(part_ms, 90) * 1e3)],
+        "combine_kernel_us": float(comb_ms.mean() * 1e3),
+        "cold_ms_median": float(np.median(cold_ms)),
+        "cold_kv_gbs": wl.kv_bytes / (np.median(cold_ms) / 1e3) / 1e9,
+        "kv_bytes": wl.kv_bytes,
+        "unique_kv_bytes": wl.unique_kv_bytes,
+    }
+
+
+def roofline(wl: Workload, r: dict) -> dict:
+    achieved = wl.kv_bytes / (r["partition_kernel_us"] / 1e6) / 1e9
+    out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+           "kernel": f"partition_{wl.path_name}", "algorithmic_bytes_per_launch": wl.kv_bytes}
+    try:
+        with open(COUNTERS_FILE) as f:
+            cnt = json.load(f)
+        entry = cnt.get(wl.case.name, {})
+        if entry.get("kernel_hash") == kernel_hash() and entry.get("path") == wl.path_name:
+            hbm = entry["hbm_bytes_per_launch"]
+            out["traffic"] = round(hbm / (r["partition_kernel_us"] / 1e6) / 1e9, 1)
+            out["traffic_bytes_per_launch"] = hbm
+    except (OSError, ValueError, KeyError):
+        pass
+    return out
+
+
+def cpu_baseline(wl: Workload, budget_s: float) -> dict:
+    """The fp64 oracle on a bounded sample of (sequence, head) pairs of the same
+    workload, extrapolated to the whole batch by cached-token count."""
+    from oracle import oracle as O
+
+    c = wl.case
+    threads = max(1, min(16, os.cpu_count() or 1))
+    rng = np.random.default_rng(0)
+    order = rng.permutation(c.B * c.Hq)
+    pairs_all = np.stack([order // c.Hq, order % c.Hq], axis=1).astype(np.int32)
+    n, used, t_used = threads, 0, 0.0
+    while True:
+        pairs = pairs_all[:n]
+        t0 = time.perf_counter()
+        O.paged_attn_decode(c.q, c.k_pool, c.v_pool, c.block_table, c.seqlens, c.scale,
+                            kv_dtype=c.kv_dtype, block_size=c.bs, num_kv_heads=c.Hkv,
+                            layout=c.layout, pairs=pairs, nthreads=threads)
+        dt = time.perf_counter() - t0
+        used, t_used = n, dt
+        if dt > budget_s / 3 or n >= len(pairs_all):
+            break
+        n = min(len(pairs_all), int(n * max(2.0, budget_s / 3 / max(dt, 1e-3))))
+    tok_sample = int(c.seqlens[pairs_all[:used, 0]].astype(np.int64).sum())
+    tok_all = int(c.seqlens.astype(np.int64).sum()) * c.Hq
+    t_full = t_used * tok_all / tok_sample
+    return {"value": round(wl.kv_bytes / t_full / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{used} of {c.B * c.Hq} (sequence, query head) pairs of {c.name} "
+                      f"({tok_sample} of {tok_all} head-tokens) in {t_used:.2f}s, "
+                      "extrapolated by head-token count",
+            "seq_heads_per_s": round(c.B * c.Hq / t_full, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--also", type=str, default="3", help="comma-separated extra configs ('' for none)")
+    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", choices=["partition", "both", "copy"], default=None)
+    a = ap.parse_args()
+
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (this "
+              "decode path runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    if a.profile == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(a.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes x {a.steps}")
+        return
+
+    wl = Workload(a.config, torch, a.path)
+    if a.profile is not None:
+        for _ in range(a.warmup):
+            wl.call()
+        torch.cuda.synchronize()
+        for _ in range(a.steps):
+            wl.call(a.profile)
+        torch.cuda.synchronize()
+        log(f"[bench] {a.steps} '{a.profile}' launches of {wl.case.name} done")
+        return
+
+    flush_buf = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > 256 MB MALL
+    r = measure(wl, a.steps, a.warmup, flush_buf)
+    log(f"[bench] {wl.case.name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['kv_gbs']:.0f} GB/s")
+    rl = roofline(wl, r)
+    also = {}
+    for k in [int(x) for x in a.also.split(",") if x.strip()]:
+        if k == a.config:
+            continue
+        w2 = Workload(k, torch, a.path)
+        r2 = measure(w2, a.steps, a.warmup, flush_buf)
+        log(f"[bench] {w2.case.name}: {r2['ms_per_step'] * 1e3:.1f} us/step, {r2['kv_gbs']:.0f} GB/s")
+        also[w2.case.name] = {**w2.describe(), **{k2: (round(v, 4) if isinstance(v, float) else v)
+                                                  for k2, v in r2.items()},
+                              "pct_hbm_peak": round(100 * r2["kv_gbs"] / HBM_PEAK_GBS, 2),
+                              "roofline": roofline(w2, r2)}
+        del w2
+        torch.cuda.empty_cache()
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        cpu = cpu_baseline(wl, a.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": round(r["kv_gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.case.kv_dtype,
+        "data": "synthetic (seeded)",
+        "config": wl.describe(),
+        "pct_hbm_peak": round(100 * r["kv_gbs"] / HBM_PEAK_GBS, 2),
+        "seq_heads_per_s": round(r["seq_heads_per_s"], 1),
+        "detail": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()},
+        "roofline": rl,
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

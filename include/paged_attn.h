@@ -133,6 +133,26 @@ int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache,
                       const int32_t* cache_seqlens, float scale, float* out, void* workspace,
                       size_t workspace_bytes, int32_t* status, void* stream);
 
+/*
+ * The two phases of paged_attn_decode, callable separately (same arguments and
+ * rules). paged_attn_partition_phase runs the partition kernel: every
+ * (sequence, KV head, partition) folds its tokens into a running softmax state;
+ * a sequence with one partition gets its normalised output written to out, the
+ * others leave their states in the workspace. paged_attn_combine_phase merges
+ * those states into out with the max-rescaling combine (page "Paged Attention
+ * Kernel Architecture for BI-V100", section 2 level 3 and section 6 phase 2) and
+ * reads only cache_seqlens and the workspace. Calling the partition phase and
+ * then the combine phase on one stream equals paged_attn_decode. The combine
+ * phase is a no-op when paged_attn_workspace_size() is 0.
+ */
+int paged_attn_partition_phase(const pa_desc* desc, const float* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* cache_seqlens, float scale, float* out,
+                               void* workspace, size_t workspace_bytes, int32_t* status,
+                               void* stream);
+int paged_attn_combine_phase(const pa_desc* desc, const int32_t* cache_seqlens, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace paged_attn_decode needs for this descriptor: the partial
  * (max, sum, output) of every possible partition, sized from
  * max_blocks_per_seq * block_size. 0 when one partition always suffices.

@@ -67,12 +67,14 @@ def workspace_for(desc: PaDesc, device):
 
 def paged_attn_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, out=None, *,
                       layout="HND", partition_size=0, path="auto", workspace=None, status=None,
-                      stream=None):
+                      stream=None, phase="both"):
     """Single-query paged GQA attention; returns ``out`` (float32 [B, H_q, d]).
 
     q float32 [B, H_q, d]; block_table int32 [B, MBS]; cache_seqlens int32 [B];
     all on one GPU. Enqueued on ``stream`` (default: torch's current stream).
     ``status`` is an optional int32 device tensor the kernels OR error bits into.
+    ``phase`` "partition" or "combine" runs one of the two kernels alone (the
+    combine phase needs the workspace the partition phase filled).
     """
     import torch
 
@@ -97,7 +99,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, ou
         cache_seqlens.data_ptr(), float(scale), out.data_ptr(),
         workspace.data_ptr() if workspace is not None else 0,
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
-        status.data_ptr() if status is not None else 0, int(stream))
+        status.data_ptr() if status is not None else 0, int(stream), phase)
     if rc != 0:
         raise PagedAttnError(rc, "paged_attn_decode: ")
     return out

@@ -27,8 +27,8 @@ PA_STATUS_BAD_BLOCK = 1
 PA_STATUS_BAD_SEQLEN = 2
 
 EXPORTED = (
-    "paged_attn_decode", "paged_attn_workspace_size", "paged_attn_validate",
-    "paged_attn_partition_size", "paged_attn_resolved_path", "paged_attn_check_inputs",
+    "paged_attn_decode", "paged_attn_partition_phase", "paged_attn_combine_phase",
+    "paged_attn_workspace_size", "paged_attn_validate", "paged_attn_partition_size", "paged_attn_resolved_path", "paged_attn_check_inputs",
     "paged_attn_strerror", "paged_attn_abi_version",
 )
 
@@ -79,6 +79,10 @@ def load_library(path: str = LIB_PATH):
     dp = ctypes.POINTER(PaDesc)
     lib.paged_attn_decode.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp, vp]
     lib.paged_attn_decode.restype = i32
+    lib.paged_attn_partition_phase.argtypes = lib.paged_attn_decode.argtypes
+    lib.paged_attn_partition_phase.restype = i32
+    lib.paged_attn_combine_phase.argtypes = [dp, vp, vp, vp, sz, vp]
+    lib.paged_attn_combine_phase.restype = i32
     lib.paged_attn_workspace_size.argtypes = [dp]
     lib.paged_attn_workspace_size.restype = sz
     lib.paged_attn_validate.argtypes = [dp]
@@ -140,9 +144,16 @@ def check_inputs(desc: PaDesc, block_table_host, seqlens_host) -> int:
 
 def decode_raw(desc: PaDesc, q_ptr: int, k_ptr: int, v_ptr: int, table_ptr: int, seqlens_ptr: int,
                scale: float, out_ptr: int, ws_ptr: int, ws_bytes: int, status_ptr: int,
-               stream: int) -> int:
-    """Direct call of paged_attn_decode with integer device addresses."""
-    return load_library().paged_attn_decode(
+               stream: int, phase: str = "both") -> int:
+    """Direct call of paged_attn_decode (phase "both"), paged_attn_partition_phase
+    ("partition") or paged_attn_combine_phase ("combine") with integer device
+    addresses."""
+    lib = load_library()
+    if phase == "combine":
+        return lib.paged_attn_combine_phase(ctypes.byref(desc), seqlens_ptr or None, out_ptr or None,
+                                            ws_ptr or None, ws_bytes, stream or None)
+    fn = lib.paged_attn_partition_phase if phase == "partition" else lib.paged_attn_decode
+    return fn(
         ctypes.byref(desc), q_ptr or None, k_ptr or None, v_ptr or None, table_ptr or None,
         seqlens_ptr or None, ctypes.c_float(scale), out_ptr or None, ws_ptr or None, ws_bytes,
         status_ptr or None, stream or None)

@@ -74,6 +74,8 @@ int validate(const pa_desc* d) {
     if (ps < 32 || ps > 16384 || ps % 32) return PA_E_PARTITION;
     if ((ps >> ilog2(d->block_size)) + 2 > pa::kTableCap) return PA_E_PARTITION;
   }
+  // the partition index is grid dimension y
+  if ((max_tokens(d) + pick_partition(d) - 1) / pick_partition(d) > 65535) return PA_E_PARTITION;
   const int path = pick_path(d);
   return path < 0 ? path : PA_OK;
 }
@@ -141,23 +143,29 @@ const char* paged_attn_strerror(int status) {
   return "unknown status";
 }
 
-int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache, const void* v_cache,
-                      const int32_t* block_table, const int32_t* cache_seqlens, float scale,
-                      float* out, void* workspace, size_t workspace_bytes, int32_t* status,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared argument checks and parameter set-up of the decode entry points.
+// Returns PA_OK and fills p, or an error code.
+int prepare(const pa_desc* desc, const float* q, const void* k_cache, const void* v_cache,
+            const int32_t* block_table, const int32_t* cache_seqlens, float scale, float* out,
+            void* workspace, size_t workspace_bytes, int32_t* status, bool need_inputs,
+            pa::Params& p) {
   int rc = validate(desc);
   if (rc != PA_OK) return rc;
+  memset(&p, 0, sizeof p);
+  p.B = desc->batch;
   if (desc->batch == 0) return PA_OK;
-  if (!q || !k_cache || !v_cache || !block_table || !cache_seqlens || !out) return PA_E_NULL;
+  if (!cache_seqlens || !out) return PA_E_NULL;
+  if (need_inputs && (!q || !k_cache || !v_cache || !block_table)) return PA_E_NULL;
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15) return PA_E_ALIGN;
   const size_t need = paged_attn_workspace_size(desc);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)))
     return PA_E_WORKSPACE;
 
   const int part = pick_partition(desc);
-  const int path = pick_path(desc);
-  pa::Params p;
-  memset(&p, 0, sizeof p);
   p.q = q;
   p.k = k_cache;
   p.v = v_cache;
@@ -171,7 +179,6 @@ int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache, 
   p.vsb = desc->v_stride_block;
   p.vsh = desc->v_stride_head;
   p.vst = desc->v_stride_token;
-  p.B = desc->batch;
   p.Hq = desc->num_q_heads;
   p.Hkv = desc->num_kv_heads;
   p.G = desc->num_q_heads / desc->num_kv_heads;
@@ -189,15 +196,56 @@ int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache, 
     p.ws_l = (float*)(ws + align256(rows * sizeof(float)));
     p.ws_acc = (float*)(ws + 2 * align256(rows * sizeof(float)));
   }
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = path == PA_PATH_MFMA ? pa::launch_partition_mfma(p, desc->kv_dtype, s)
-                                      : pa::launch_partition_valu(p, desc->kv_dtype, s);
-  if (e != hipSuccess) return PA_E_LAUNCH;
-  if (p.pmax > 1) {
-    e = pa::launch_combine(p, s);
-    if (e != hipSuccess) return PA_E_LAUNCH;
-  }
   return PA_OK;
+}
+
+int run_partition(const pa_desc* desc, const pa::Params& p, hipStream_t s) {
+  const hipError_t e = pick_path(desc) == PA_PATH_MFMA ? pa::launch_partition_mfma(p, desc->kv_dtype, s)
+                                                       : pa::launch_partition_valu(p, desc->kv_dtype, s);
+  return e == hipSuccess ? PA_OK : PA_E_LAUNCH;
+}
+
+int run_combine(const pa::Params& p, hipStream_t s) {
+  if (p.pmax <= 1) return PA_OK;
+  return pa::launch_combine(p, s) == hipSuccess ? PA_OK : PA_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* cache_seqlens, float scale,
+                      float* out, void* workspace, size_t workspace_bytes, int32_t* status,
+                      void* stream) {
+  pa::Params p;
+  int rc = prepare(desc, q, k_cache, v_cache, block_table, cache_seqlens, scale, out, workspace,
+                   workspace_bytes, status, true, p);
+  if (rc != PA_OK || p.B == 0) return rc;
+  rc = run_partition(desc, p, (hipStream_t)stream);
+  if (rc != PA_OK) return rc;
+  return run_combine(p, (hipStream_t)stream);
+}
+
+int paged_attn_partition_phase(const pa_desc* desc, const float* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table,
+                               const int32_t* cache_seqlens, float scale, float* out,
+                               void* workspace, size_t workspace_bytes, int32_t* status,
+                               void* stream) {
+  pa::Params p;
+  const int rc = prepare(desc, q, k_cache, v_cache, block_table, cache_seqlens, scale, out,
+                         workspace, workspace_bytes, status, true, p);
+  if (rc != PA_OK || p.B == 0) return rc;
+  return run_partition(desc, p, (hipStream_t)stream);
+}
+
+int paged_attn_combine_phase(const pa_desc* desc, const int32_t* cache_seqlens, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  pa::Params p;
+  const int rc = prepare(desc, nullptr, nullptr, nullptr, nullptr, cache_seqlens, 1.f, out,
+                         workspace, workspace_bytes, nullptr, false, p);
+  if (rc != PA_OK || p.B == 0) return rc;
+  return run_combine(p, (hipStream_t)stream);
 }
 
 }  // extern "C"

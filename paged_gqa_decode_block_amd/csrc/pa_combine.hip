@@ -10,17 +10,21 @@
 // partitions at once; only p < n is read. Sequences with one partition were
 // already written by the partition kernel and are skipped here.
 //
-// Grid (D / 64, H_q, B), 256 threads: lane = one of 64 dims, wave = a stripe of
-// the partitions (p = wave, wave + 4, ...); the four stripes meet in LDS.
+// Grid (D / 64, H_q, B), 256 threads: thread (stripe s, quad u) owns dims
+// 4u .. 4u+3 of a 64-dim slice (float4 loads) and partitions p = s, s + 16, ...;
+// the 16 stripes meet in LDS.
 #include "pa_kernels.h"
 
 namespace pa {
 namespace {
 
+constexpr int kStripes = 16;
+
 __global__ void __launch_bounds__(256) combine_kernel(Params p) {
   const int b = blockIdx.z, h = blockIdx.y;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int d = blockIdx.x * 64 + lane;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int u = tid & 15, s = tid >> 4;
+  const int d = blockIdx.x * 64 + 4 * u;
   const int L = clamped_len(p, b, false);
   const int n = (L + p.part - 1) / p.part;
   if (n <= 1) return;
@@ -29,27 +33,63 @@ __global__ void __launch_bounds__(256) combine_kernel(Params p) {
   const float* mrow = p.ws_m + row;
   const float* lrow = p.ws_l + row;
 
+  // M = max over all n partitions (every wave computes it)
   float M = -INFINITY;
   for (int i = lane; i < n; i += 64) M = fmaxf(M, mrow[i]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   const float mu = M == -INFINITY ? 0.f : M;
 
-  float a = 0.f, ls = 0.f;
-  for (int i = w; i < n; i += 4) {
-    const float wgt = exp2_fast(mrow[i] - mu);
-    ls += wgt * lrow[i];
-    a += wgt * p.ws_acc[(row + i) * p.D + d];
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  float ls = 0.f;
+  const float* arow = p.ws_acc + row * p.D + d;
+  int i = s;
+  for (; i + 3 * kStripes < n; i += 4 * kStripes) {  // four partitions in flight
+    float4 x[4];
+    float w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[k] = *(const float4*)(arow + (int64_t)(i + k * kStripes) * p.D);
+      w[k] = exp2_fast(mrow[i + k * kStripes] - mu);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ls += w[k] * lrow[i + k * kStripes];
+      a.x += w[k] * x[k].x;
+      a.y += w[k] * x[k].y;
+      a.z += w[k] * x[k].z;
+      a.w += w[k] * x[k].w;
+    }
+  }
+  for (; i < n; i += kStripes) {
+    const float4 x = *(const float4*)(arow + (int64_t)i * p.D);
+    const float w = exp2_fast(mrow[i] - mu);
+    ls += w * lrow[i];
+    a.x += w * x.x;
+    a.y += w * x.y;
+    a.z += w * x.z;
+    a.w += w * x.w;
   }
 
-  __shared__ float s_a[4][64], s_l[4];
-  s_a[w][lane] = a;
-  if (lane == 0) s_l[w] = ls;
+  __shared__ float4 s_a[kStripes][16];
+  __shared__ float s_l[kStripes];
+  s_a[s][u] = a;
+  if (u == 0) s_l[s] = ls;
   __syncthreads();
-  if (w == 0) {
-    const float tot = s_l[0] + s_l[1] + s_l[2] + s_l[3];
-    const float num = s_a[0][lane] + s_a[1][lane] + s_a[2][lane] + s_a[3][lane];
-    p.out[((int64_t)b * p.Hq + h) * p.D + d] = tot > 0.f ? num / tot : 0.f;
+  if (tid < 16) {
+    float tot = 0.f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < kStripes; ++k) {
+      tot += s_l[k];
+      num.x += s_a[k][tid].x;
+      num.y += s_a[k][tid].y;
+      num.z += s_a[k][tid].z;
+      num.w += s_a[k][tid].w;
+    }
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    *(float4*)(p.out + ((int64_t)b * p.Hq + h) * p.D + d) =
+        make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
   }
 }
 

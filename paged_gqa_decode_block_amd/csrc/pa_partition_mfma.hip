@@ -60,11 +60,16 @@ __device__ __forceinline__ void split2(float x, T& hi, T& lo) {
   lo = (T)(x - (float)hi);
 }
 
-// LDS layout of the V chunk: 32 token rows of D elements; the 16-byte column
-// chunks of row R are XOR-permuted by f(R) = 2*((R>>2)&3) + (R&1) so that the
-// transposing 2-byte reads of the P.V operand and the 16-byte writes both spread
-// over the banks.
-__device__ __forceinline__ int vswz(int R) { return (((R >> 2) & 3) << 1) | (R & 1); }
+// LDS layout of the V chunk: 32 token rows of D elements, row-major, with the
+// 16-byte column chunks of row R XOR-permuted by f(R) = 2*(R&3) + ((R>>2)&1).
+// Each group of 8 lanes writing 16-byte chunks of rows 0..7 (or 8..15) then hits
+// 8 different bank groups, and so do the 16 lanes of a quad in the transposing
+// reads below.
+__device__ __forceinline__ int vswz(int R) { return ((R & 3) << 1) | ((R >> 2) & 1); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 
 // Waves per SIMD the register allocation is held to: 2 for d <= 128, 1 for d = 256.
 template <int D>
@@ -78,12 +83,20 @@ partition_mfma_kernel(Params p) {
   typedef typename Mma<T>::vec V8;
   constexpr int KS = D / 32;  // k-steps of a 16-token score tile
   constexpr int MB = D / 16;  // 16-dim output tiles
+  constexpr bool kQInLds = D > 128;  // Q' fragments: LDS for d = 256, registers otherwise
+  // V register sets: two (refill distance 64 tokens) for d <= 128; one for d = 256,
+  // refilled with the next chunk as soon as it is staged in LDS.
+  constexpr int kVDist = D > 128 ? 32 : 64;
 
   __shared__ int s_ids[kTableCap];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[32 * D];
-  __shared__ __attribute__((aligned(16))) V8 s_q[2][KS][64];  // Q' fragments, hi / lo
+  __shared__ __attribute__((aligned(16))) V8 s_q[kQInLds ? 2 : 1][kQInLds ? KS : 1][64];
 
-  const int part = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  // Partition-major grid: x = b * H_kv + hk, y = partition. Consecutive
+  // workgroup ids (which the dispatcher deals round-robin to the XCDs) cover all
+  // (sequence, KV head) pairs of one partition index.
+  const int b = blockIdx.x / p.Hkv, hk = blockIdx.x - (blockIdx.x / p.Hkv) * p.Hkv;
+  const int part = blockIdx.y;
   const int lane = threadIdx.x;
   const int r = lane & 15, q = lane >> 4;
   const int G = p.G;
@@ -108,7 +121,8 @@ partition_mfma_kernel(Params p) {
 
   // Q' = q * scale * log2(e) of head r of the group (zero for padded heads),
   // dims 32*ks + 8*q .. +7: the B-operand fragments of the score MFMAs, split
-  // into hi / lo parts and parked in LDS (one 16-byte slot per lane).
+  // into hi / lo parts.
+  V8 qreg[kQInLds ? 1 : 2][kQInLds ? 1 : KS];
   {
     const bool hv = r < G;
     const float* qp = p.q + ((int64_t)b * p.Hq + hk * G + (hv ? r : 0)) * D + 8 * q;
@@ -125,91 +139,93 @@ partition_mfma_kernel(Params p) {
         hi[e] = h;
         lo[e] = l2;
       }
-      s_q[0][ks][lane] = hi;
-      s_q[1][ks][lane] = lo;
+      if constexpr (kQInLds) {
+        s_q[0][ks][lane] = hi;
+        s_q[1][ks][lane] = lo;
+      } else {
+        qreg[0][ks] = hi;
+        qreg[1][ks] = lo;
+      }
     }
   }
   __syncthreads();
 
   const T* kbase = (const T*)p.k + (int64_t)hk * p.ksh + 8 * q;
   const T* vbase = (const T*)p.v + (int64_t)hk * p.vsh + 8 * q;
-  // V rows are loaded with a 4x4 transpose of r so each 8-lane group writes
-  // 8 different bank groups.
-  const int sig = ((r & 3) << 2) | (r >> 2);
 
   f32x4 acc[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  // K of chunk c for the A operand: lane (q, r) takes token c + 16*tau + r,
-  // dims 32*ks + 8*q .. +7. Returns whether each of its two tokens was loaded.
-  auto load_k = [&](int c, uint4 (&kr)[2][KS], bool (&kv)[2]) {
+  // K or V of chunk c: lane (q, r) takes token c + 16*tau + r, dims
+  // 32*ks + 8*q .. +7 (for K exactly the A-operand fragment of the score MFMA).
+  // Tokens at or past t1, or behind an invalid table entry, are not loaded.
+  auto load_rows = [&](int c, const T* base, int64_t sblk, int64_t stok, uint4 (&dst)[2][KS],
+                       bool (&ok)[2]) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const int tk = c + 16 * tau + r;
-      const int id = tk < t1 ? s_ids[(tk >> p.bs_log2) - j0] : -1;
-      kv[tau] = id >= 0;
+      const int t = c + 16 * tau + r;
+      const int id = t < t1 ? s_ids[(t >> p.bs_log2) - j0] : -1;
+      ok[tau] = id >= 0;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[tau][ks] = make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) dst[tau][ks] = make_uint4(0, 0, 0, 0);
       if (id >= 0) {
-        const T* kp = kbase + (int64_t)id * p.ksb + (int64_t)(tk & bsm) * p.kst;
+        const T* src = base + (int64_t)id * sblk + (int64_t)(t & bsm) * stok;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[tau][ks] = *(const uint4*)(kp + 32 * ks);
-      }
-    }
-  };
-  auto load_v = [&](int c, uint4 (&vr)[2][KS]) {
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int tv = c + 16 * tau + sig;
-      const int id = tv < t1 ? s_ids[(tv >> p.bs_log2) - j0] : -1;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) vr[tau][ks] = make_uint4(0, 0, 0, 0);
-      if (id >= 0) {
-        const T* vp = vbase + (int64_t)id * p.vsb + (int64_t)(tv & bsm) * p.vst;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) vr[tau][ks] = *(const uint4*)(vp + 32 * ks);
+        for (int ks = 0; ks < KS; ++ks) dst[tau][ks] = *(const uint4*)(src + 32 * ks);
       }
     }
   };
 
-  // One chunk: kcur holds its K; knext receives the next chunk's K; vr holds
-  // this chunk's V and then receives the next chunk's V.
-  auto step = [&](int c, uint4 (&kcur)[2][KS], bool (&kval)[2], uint4 (&knext)[2][KS],
-                  bool (&knv)[2], uint4 (&vr)[2][KS]) {
-    const bool more = c + 32 < t1;
-    if (more) load_k(c + 32, knext, knv);
+  // Per-lane pieces of the transposing V reads: lane (q, 4j + k) points at row
+  // 16*tau + 4q + j, columns 16*mb + 4k .. +3.
+  const int tj = r >> 2, tk = r & 3;
+  const int trow = (4 * q + tj) * D + 4 * (tk & 1);
+  const int txor = (tk >> 1) ^ (q & 1);
 
-    // ---- stage V of this chunk in LDS (row-major, swizzled), then refill vr
+  // One 32-token chunk. kr/okr hold its K, vr its V; the K set is refilled with
+  // chunk c + 64 once the scores are formed and the V set with chunk
+  // c + kVDist once it is staged, so about two chunks of loads stay in flight
+  // behind the compute.
+  auto step = [&](int c, uint4 (&kr)[2][KS], bool (&okr)[2], uint4 (&vr)[2][KS]) {
+    const bool refill = c + 64 < t1;
+    // ---- stage V in LDS (row-major, swizzled), then refill vr
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      const int R = 16 * tau + sig;
+      const int R = 16 * tau + r;
       const int f = vswz(R);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int pc = (4 * ks + q) ^ f;
-        *(uint4*)(s_v + R * D + 8 * pc) = vr[tau][ks];
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        *(uint4*)(s_v + R * D + 8 * ((4 * ks + q) ^ f)) = vr[tau][ks];
     }
-    if (more) load_v(c + 32, vr);
+    bool dummy[2];
+    if (c + kVDist < t1) load_rows(c + kVDist, vbase, p.vsb, p.vst, vr, dummy);
 
     // ---- scores: two 16-token tiles, K . Q'hi + K . Q'lo
     f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const V8 qh = s_q[0][ks][lane];
-      const V8 ql = s_q[1][ks][lane];
+      V8 qh, ql;
+      if constexpr (kQInLds) {
+        qh = s_q[0][ks][lane];
+        ql = s_q[1][ks][lane];
+      } else {
+        qh = qreg[0][ks];
+        ql = qreg[1][ks];
+      }
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        const V8 a = __builtin_bit_cast(V8, kcur[tau][ks]);
+        const V8 a = __builtin_bit_cast(V8, kr[tau][ks]);
         st[tau] = Mma<T>::mma(a, qh, st[tau]);
         st[tau] = Mma<T>::mma(a, ql, st[tau]);
       }
     }
     // token 16*tau + x was loaded iff lane x (quad 0) had a valid id for it
-    const uint64_t bal0 = __ballot(kval[0]);
-    const uint64_t bal1 = __ballot(kval[1]);
+    const uint64_t bal0 = __ballot(okr[0]);
+    const uint64_t bal1 = __ballot(okr[1]);
+    if (refill) load_rows(c + 64, kbase, p.ksb, p.kst, kr, okr);
+
     float sv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -247,31 +263,36 @@ partition_mfma_kernel(Params p) {
       plo[j] = lo;
     }
 
-    // ---- O^T += V^T P^T, one MFMA (x2 for hi/lo P) per 16 dims
+    // ---- O^T += V^T P^T: the V^T fragment of slots j = 0..3 / 4..7 comes from
+    // one transposing 64-bit LDS read each (16-lane group semantics: lane i gets
+    // element i%4 of the 8 bytes addressed by lane 4j + i/4, for j = 0..3).
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int col = 16 * mb + r;
-      u16x8 a;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int R = 16 * (j >> 2) + 4 * q + (j & 3);
-        const int pc = (col >> 3) ^ vswz(R);
-        a[j] = s_v[R * D + 8 * pc + (col & 7)];
-      }
-      const V8 av = __builtin_bit_cast(V8, a);
+      const int pc = 2 * (mb ^ tj) + txor;
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s_v + trow + 8 * pc));
+      const s16x4 hi4 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s_v + 16 * D + trow + 8 * pc));
+      const V8 av = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[mb] = Mma<T>::mma(av, phi, acc[mb]);
       acc[mb] = Mma<T>::mma(av, plo, acc[mb]);
     }
   };
 
-  uint4 kA[2][KS], kB[2][KS], vr[2][KS];
-  bool vA[2], vB[2] = {false, false};
-  load_k(t0, kA, vA);
-  load_v(t0, vr);
+  uint4 kA[2][KS], kB[2][KS], vA[2][KS], vB[kVDist == 64 ? 2 : 1][KS];
+  bool okA[2], okB[2] = {false, false};
+  load_rows(t0, vbase, p.vsb, p.vst, vA, okA);
+  load_rows(t0, kbase, p.ksb, p.kst, kA, okA);
+  if (t0 + 32 < t1) {
+    if constexpr (kVDist == 64) load_rows(t0 + 32, vbase, p.vsb, p.vst, vB, okB);
+    load_rows(t0 + 32, kbase, p.ksb, p.kst, kB, okB);
+  }
   for (int c = t0; c < t1; c += 64) {
-    step(c, kA, vA, kB, vB, vr);
+    step(c, kA, okA, vA);
     if (c + 32 >= t1) break;
-    step(c + 32, kB, vB, kA, vA, vr);
+    if constexpr (kVDist == 64)
+      step(c + 32, kB, okB, vB);
+    else
+      step(c + 32, kB, okB, vA);
   }
 
   // l summed over the four quads (each holds its own tokens' share)
@@ -303,7 +324,7 @@ partition_mfma_kernel(Params p) {
 
 template <typename T, int D>
 hipError_t launch_t(const Params& p, hipStream_t s) {
-  dim3 grid(p.pmax, p.Hkv, p.B);
+  dim3 grid(p.B * p.Hkv, p.pmax);
   hipLaunchKernelGGL((partition_mfma_kernel<T, D>), grid, dim3(64), 0, s, p);
   return hipGetLastError();
 }

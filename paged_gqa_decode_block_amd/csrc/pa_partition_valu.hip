@@ -85,7 +85,9 @@ __global__ void __launch_bounds__(256) partition_valu_kernel(Params p) {
   __shared__ float s_m[NW][G], s_l[NW][G];
   __shared__ float s_acc[NW][G][D];
 
-  const int part = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  // partition-major grid: x = b * H_kv + hk, y = partition
+  const int b = blockIdx.x / p.Hkv, hk = blockIdx.x - (blockIdx.x / p.Hkv) * p.Hkv;
+  const int part = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int row = lane / C, cl = lane % C;
   const int slot = w * R + row;
@@ -242,7 +244,7 @@ __global__ void __launch_bounds__(256) partition_valu_kernel(Params p) {
 
 template <typename T, int D, int G>
 hipError_t launch_t(const Params& p, hipStream_t s) {
-  dim3 grid(p.pmax, p.Hkv, p.B);
+  dim3 grid(p.B * p.Hkv, p.pmax);
   hipLaunchKernelGGL((partition_valu_kernel<T, D, G>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
