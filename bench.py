@@ -4,8 +4,8 @@ A step is one decode call (partition kernel + combine kernel) over the whole
 synthetic batch, inputs resident in HBM. Default workload: the 64-sequence
 large-GQA bf16 batch (B=64, H_q=64, H_kv=8, d=128, bs=16, lengths log-uniform in
 [1024, 32768], 10% spare blocks); the 100K-token Qwen3.6-shaped batch (B=1,
-H_q=24, H_kv=4, d=256, partition 512) is measured too and reported under
-"also". Prints one JSON line on stdout; progress goes to stderr.
+H_q=24, H_kv=4, d=256, partition 512) and the prefix-shared 256-sequence batch are
+measured too and reported under "also". Prints one JSON line on stdout; progress goes to stderr.
 
   python bench.py [--steps K] [--warmup W] [--config 4] [--also 3]
   python bench.py --profile partition   # only partition-kernel launches (for rocprofv3)
@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8.0 TB/s
 METRIC = "decode attention KV GB/s (% of MI355X HBM peak) + seq-heads/s, 1 GPU"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
-KERNEL_SOURCES = ["paged_gqa_decode_block_amd/csrc/pa_partition_mfma.hip",
+KERNEL_SOURCES = ["paged_gqa_decode_block_amd/csrc/pa_partition_stream.hip",
+                  "paged_gqa_decode_block_amd/csrc/pa_partition_mfma.hip",
                   "paged_gqa_decode_block_amd/csrc/pa_partition_valu.hip",
                   "paged_gqa_decode_block_amd/csrc/pa_combine.hip",
                   "paged_gqa_decode_block_amd/csrc/pa_kernels.h",
@@ -75,8 +76,12 @@ class Workload:
         self.table = torch.from_numpy(c.block_table).to("cuda")
         self.seqlens = torch.from_numpy(c.seqlens).to("cuda")
         self.out = torch.empty_like(self.q)
+        # the prefix-shared workload's block manager knows blocks are listed by
+        # several sequences (reference counts > 1): keep K/V loads cacheable
+        self.kv_shared = c.ref_count is not None and int(c.ref_count.max()) > 1
+        part = c.partition_size if k == 3 else 0  # the 100K-token workload fixes 512
         self.desc = pa.desc_for(self.q, self.k_pool, self.v_pool, self.table, layout=c.layout,
-                                partition_size=c.partition_size, path=path)
+                                partition_size=part, path=path, kv_shared=self.kv_shared)
         n = pa.workspace_size(self.desc)
         self.ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
         self.part = pa.partition_size(self.desc)
@@ -101,7 +106,7 @@ class Workload:
         return {
             "workload": c.name, "batch": c.B, "num_q_heads": c.Hq, "num_kv_heads": c.Hkv,
             "head_dim": c.D, "block_size": c.bs, "kv_dtype": c.kv_dtype, "layout": c.layout,
-            "partition_size": self.part, "path": self.path_name,
+            "partition_size": self.part, "path": self.path_name, "kv_shared": self.kv_shared,
             "total_cached_tokens": int(c.seqlens.astype(np.int64).sum()),
             "num_physical_blocks": c.NB, "seed": 1000 + self.k,
         }
@@ -219,8 +224,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--also", type=str, default="3", help="comma-separated extra configs ('' for none)")
-    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--also", type=str, default="3,5", help="comma-separated extra configs ('' for none)")
+    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "mfma_grid", "mfma_stream"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", choices=["partition", "both", "copy"], default=None)

@@ -39,15 +39,25 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 /* Element type of the K and V caches. q and out are always float32. */
 typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype;
 
 /* Which partition kernel runs: VALU (vector ALU dot products and reductions) or
  * MFMA (matrix-core micro-GEMMs for the G x d . d x N scores and the P . V
- * product). AUTO picks per dtype and shape. MFMA needs f16 or bf16 K/V. */
-typedef enum pa_path { PA_PATH_AUTO = 0, PA_PATH_VALU = 1, PA_PATH_MFMA = 2 } pa_path;
+ * product). MFMA needs f16 or bf16 K/V and has two kernels: MFMA_STREAM, a
+ * persistent kernel in which each wave streams a contiguous run of partitions
+ * (block_size >= 16, batch <= 1024), and MFMA_GRID, one workgroup per
+ * partition (any block size and batch). PA_PATH_MFMA picks MFMA_STREAM when it
+ * applies, else MFMA_GRID; AUTO picks MFMA for 16-bit K/V and VALU for fp32. */
+typedef enum pa_path {
+  PA_PATH_AUTO = 0,
+  PA_PATH_VALU = 1,
+  PA_PATH_MFMA = 2,
+  PA_PATH_MFMA_GRID = 3,
+  PA_PATH_MFMA_STREAM = 4
+} pa_path;
 
 /* Status codes. */
 #define PA_OK 0
@@ -65,11 +75,19 @@ typedef enum pa_path { PA_PATH_AUTO = 0, PA_PATH_VALU = 1, PA_PATH_MFMA = 2 } pa
 #define PA_E_PARTITION (-8)   /* partition_size not 0 and not a multiple of 32 in    */
                               /* [32, 16384], or spanning more than 1024 blocks       */
 #define PA_E_WORKSPACE (-9)   /* workspace NULL or smaller than required             */
-#define PA_E_PATH (-10)       /* path not a pa_path, or MFMA asked for f32 K/V        */
+#define PA_E_PATH (-10)       /* path not a pa_path, an MFMA path asked for f32 K/V, */
+                              /* or MFMA_STREAM asked for block_size < 16 or batch   */
+                              /* > 1024                                              */
 #define PA_E_LAUNCH (-11)     /* the HIP runtime refused a launch                    */
 #define PA_E_TABLE (-12)      /* (check_inputs) an entry read for an attended token  */
                               /* is outside [0, num_blocks)                           */
 #define PA_E_SEQLEN (-13)     /* (check_inputs) a cache length < 0 or > MBS * bs     */
+
+/* pa_desc.flags bits. */
+#define PA_FLAG_KV_SHARED 1  /* physical blocks may be listed by several sequences   */
+                             /* (prefix sharing): keep K/V loads cacheable so shared */
+                             /* blocks are reused from cache; without it K/V are     */
+                             /* streamed with non-temporal loads                     */
 
 /* Bits the kernels OR into the optional device status word. */
 #define PA_STATUS_BAD_BLOCK 1   /* an attended token's table entry was outside [0, NB) */
@@ -100,6 +118,8 @@ typedef struct pa_desc {
   int64_t v_stride_block, v_stride_head, v_stride_token; /* elements              */
   int32_t partition_size;     /* tokens per KV partition; 0 = library's choice    */
   int32_t path;               /* pa_path                                          */
+  int32_t flags;              /* PA_FLAG_* bits                                   */
+  int32_t reserved;           /* must be 0                                        */
 } pa_desc;
 
 /*
@@ -165,8 +185,8 @@ int paged_attn_validate(const pa_desc* desc);
 /* The partition size paged_attn_decode will use (tokens), or a negative PA_E_*. */
 int paged_attn_partition_size(const pa_desc* desc);
 
-/* The path paged_attn_decode will run (PA_PATH_VALU or PA_PATH_MFMA), or a
- * negative PA_E_* when the descriptor is invalid. */
+/* The kernel paged_attn_decode will run (PA_PATH_VALU, PA_PATH_MFMA_GRID or
+ * PA_PATH_MFMA_STREAM), or a negative PA_E_* when the descriptor is invalid. */
 int paged_attn_resolved_path(const pa_desc* desc);
 
 /* Host-side, synchronous check of the device arrays' VALUES on host copies:

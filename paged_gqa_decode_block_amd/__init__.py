@@ -10,7 +10,7 @@ call. Build the library with ``python -m paged_gqa_decode_block_amd.build``.
 from __future__ import annotations
 
 from ._lib import (  # noqa: F401
-    EXPORTED, LIB_PATH, PA_DTYPE, PA_PATH, PA_STATUS_BAD_BLOCK, PA_STATUS_BAD_SEQLEN, PATH_NAME,
+    EXPORTED, LIB_PATH, PA_DTYPE, PA_FLAG_KV_SHARED, PA_PATH, PA_STATUS_BAD_BLOCK, PA_STATUS_BAD_SEQLEN, PATH_NAME,
     PaDesc, PagedAttnError, check_inputs, decode_raw, load_library, make_desc, partition_size,
     resolved_path, strerror, validate, workspace_size,
 )
@@ -26,9 +26,11 @@ def _kv_dtype(t) -> str:
     return _TORCH_DTYPE_NAME[name]
 
 
-def desc_for(q, k_cache, v_cache, block_table, *, layout="HND", partition_size=0, path="auto"):
+def desc_for(q, k_cache, v_cache, block_table, *, layout="HND", partition_size=0, path="auto",
+             kv_shared=False):
     """Descriptor for torch tensors. ``k_cache``/``v_cache`` are [NB, H_kv, bs, d]
-    ("HND") or [NB, bs, H_kv, d] ("NHD"), any strides with d contiguous."""
+    ("HND") or [NB, bs, H_kv, d] ("NHD"), any strides with d contiguous.
+    ``kv_shared`` says physical blocks may be listed by several sequences."""
     B, Hq, D = q.shape
     if layout == "HND":
         NB, Hkv, bs, D2 = k_cache.shape
@@ -47,7 +49,7 @@ def desc_for(q, k_cache, v_cache, block_table, *, layout="HND", partition_size=0
     return make_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
                      num_blocks=NB, max_blocks_per_seq=block_table.shape[1],
                      kv_dtype=_kv_dtype(k_cache), k_strides=ks, v_strides=vs,
-                     partition_size=partition_size, path=path)
+                     partition_size=partition_size, path=path, kv_shared=kv_shared)
 
 
 def workspace_for(desc: PaDesc, device):
@@ -67,7 +69,7 @@ def workspace_for(desc: PaDesc, device):
 
 def paged_attn_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, out=None, *,
                       layout="HND", partition_size=0, path="auto", workspace=None, status=None,
-                      stream=None, phase="both"):
+                      stream=None, phase="both", kv_shared=False):
     """Single-query paged GQA attention; returns ``out`` (float32 [B, H_q, d]).
 
     q float32 [B, H_q, d]; block_table int32 [B, MBS]; cache_seqlens int32 [B];
@@ -75,6 +77,8 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, ou
     ``status`` is an optional int32 device tensor the kernels OR error bits into.
     ``phase`` "partition" or "combine" runs one of the two kernels alone (the
     combine phase needs the workspace the partition phase filled).
+    ``kv_shared``: blocks may be listed by several sequences (prefix sharing);
+    K/V then stay cacheable instead of being streamed non-temporally.
     """
     import torch
 
@@ -85,7 +89,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, ou
         if t.dtype != dt or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {dt} tensor")
     desc = desc_for(q, k_cache, v_cache, block_table, layout=layout,
-                    partition_size=partition_size, path=path)
+                    partition_size=partition_size, path=path, kv_shared=kv_shared)
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:

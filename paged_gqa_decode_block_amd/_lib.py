@@ -13,8 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpagedattn.so")
 
 PA_DTYPE = {"f32": 0, "f16": 1, "bf16": 2}
-PA_PATH = {"auto": 0, "valu": 1, "mfma": 2}
-PATH_NAME = {1: "valu", 2: "mfma"}
+PA_PATH = {"auto": 0, "valu": 1, "mfma": 2, "mfma_grid": 3, "mfma_stream": 4}
+PATH_NAME = {1: "valu", 3: "mfma_grid", 4: "mfma_stream"}
 
 PA_OK = 0
 PA_E = {
@@ -23,6 +23,7 @@ PA_E = {
     -9: "PA_E_WORKSPACE", -10: "PA_E_PATH", -11: "PA_E_LAUNCH", -12: "PA_E_TABLE",
     -13: "PA_E_SEQLEN",
 }
+PA_FLAG_KV_SHARED = 1
 PA_STATUS_BAD_BLOCK = 1
 PA_STATUS_BAD_SEQLEN = 2
 
@@ -53,6 +54,8 @@ class PaDesc(ctypes.Structure):
         ("v_stride_token", ctypes.c_int64),
         ("partition_size", ctypes.c_int32),
         ("path", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -107,14 +110,15 @@ def strerror(code: int) -> str:
 
 def make_desc(*, batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
               max_blocks_per_seq, kv_dtype, k_strides, v_strides=None, partition_size=0,
-              path="auto") -> PaDesc:
+              path="auto", kv_shared=False) -> PaDesc:
     v_strides = k_strides if v_strides is None else v_strides
     return PaDesc(
         int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
         int(num_blocks), int(max_blocks_per_seq),
         PA_DTYPE[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype),
         *[int(x) for x in k_strides], *[int(x) for x in v_strides], int(partition_size),
-        PA_PATH[path] if isinstance(path, str) else int(path))
+        PA_PATH[path] if isinstance(path, str) else int(path),
+        PA_FLAG_KV_SHARED if kv_shared else 0, 0)
 
 
 def validate(desc: PaDesc) -> int:

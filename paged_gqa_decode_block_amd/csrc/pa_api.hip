@@ -1,6 +1,7 @@
 // pa_api.hip -- the extern "C" entry points declared in include/paged_attn.h:
 // descriptor validation, workspace sizing, path and partition-size selection,
 // host-side value checks, and the two launches of a decode call.
+#include <stdlib.h>
 #include <string.h>
 
 #include "../../include/paged_attn.h"
@@ -22,12 +23,24 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int64_t max_tokens(const pa_desc* d) { return (int64_t)d->max_blocks_per_seq * d->block_size; }
 
+int pick_path(const pa_desc* d);
+int cu_count();
+
 // Partition size for a descriptor that passed validation of everything else.
-// Without a caller choice: 512 tokens, halved (down to 64) while the busiest
-// possible grid would hold fewer than 1024 work items.
+// Without a caller choice: for the streaming kernel, 2048 tokens when there are
+// at least as many (sequence, KV head) streams as waves (each wave then walks
+// whole streams and larger partitions mean fewer partial states), else 512;
+// for the other kernels 512, halved (down to 64) while the busiest possible
+// grid would hold fewer than 1024 work items.
 int pick_partition(const pa_desc* d) {
   if (d->partition_size > 0) return d->partition_size;
   const int64_t T = max_tokens(d);
+  if (pick_path(d) == PA_PATH_MFMA_STREAM) {
+    const int64_t streams = (int64_t)d->batch * d->num_kv_heads;
+    int part = streams >= 8LL * cu_count() ? 2048 : 512;
+    while ((part >> ilog2(d->block_size)) + 2 > pa::kTableCap && part > 32) part >>= 1;
+    return part;
+  }
   int part = 512;
   while (part > 64 && (int64_t)d->batch * d->num_kv_heads * ((T + part - 1) / part) < 1024)
     part >>= 1;
@@ -36,17 +49,66 @@ int pick_partition(const pa_desc* d) {
   return part;
 }
 
+// The kernel a descriptor runs on: PA_PATH_VALU, PA_PATH_MFMA_GRID or
+// PA_PATH_MFMA_STREAM (or an error).
 int pick_path(const pa_desc* d) {
   const int G = d->num_q_heads / d->num_kv_heads;
-  if (d->path == PA_PATH_VALU) return pa::valu_supports(d->kv_dtype, d->head_dim, G) ? PA_PATH_VALU : PA_E_SHAPE;
-  if (d->path == PA_PATH_MFMA) {
-    if (d->kv_dtype == PA_DTYPE_F32) return PA_E_PATH;
-    return pa::mfma_supports(d->kv_dtype, d->head_dim, G) ? PA_PATH_MFMA : PA_E_SHAPE;
+  const bool stream_ok =
+      pa::stream_supports(d->kv_dtype, d->head_dim, G, d->block_size, d->batch);
+  switch (d->path) {
+    case PA_PATH_VALU:
+      return pa::valu_supports(d->kv_dtype, d->head_dim, G) ? PA_PATH_VALU : PA_E_SHAPE;
+    case PA_PATH_MFMA:
+    case PA_PATH_MFMA_GRID:
+    case PA_PATH_MFMA_STREAM:
+      if (d->kv_dtype == PA_DTYPE_F32) return PA_E_PATH;
+      if (!pa::mfma_supports(d->kv_dtype, d->head_dim, G)) return PA_E_SHAPE;
+      if (d->path == PA_PATH_MFMA_GRID) return PA_PATH_MFMA_GRID;
+      if (d->path == PA_PATH_MFMA_STREAM) return stream_ok ? PA_PATH_MFMA_STREAM : PA_E_PATH;
+      return stream_ok ? PA_PATH_MFMA_STREAM : PA_PATH_MFMA_GRID;
   }
   // AUTO: matrix cores for 16-bit K/V, vector ALUs for fp32
-  if (d->kv_dtype != PA_DTYPE_F32 && pa::mfma_supports(d->kv_dtype, d->head_dim, G)) return PA_PATH_MFMA;
+  if (d->kv_dtype != PA_DTYPE_F32 && pa::mfma_supports(d->kv_dtype, d->head_dim, G))
+    return stream_ok ? PA_PATH_MFMA_STREAM : PA_PATH_MFMA_GRID;
   if (pa::valu_supports(d->kv_dtype, d->head_dim, G)) return PA_PATH_VALU;
   return PA_E_SHAPE;
+}
+
+// Ring depth / occupancy variant of the streaming kernel: PAGEDATTN_STREAM_VARIANT
+// (0, 1, 2; read once) for tuning sweeps, 0 otherwise.
+int stream_variant() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("PAGEDATTN_STREAM_VARIANT");
+    v = (e && e[0] >= '0' && e[0] <= '2') ? e[0] - '0' : 0;
+  }
+  return v;
+}
+
+// Non-temporal K/V loads in the streaming kernel (unless the descriptor says
+// blocks are shared): PAGEDATTN_STREAM_NT=0 turns them off for tuning sweeps
+// (read once), on otherwise.
+bool stream_nt() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("PAGEDATTN_STREAM_NT");
+    v = (e && e[0] == '0') ? 0 : 1;
+  }
+  return v == 1;
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 int validate(const pa_desc* d) {
@@ -68,7 +130,8 @@ int validate(const pa_desc* d) {
   for (int i = 0; i < 6; ++i)
     if (st[i] <= 0 || (st[i] * eb) % 16) return PA_E_STRIDE;
   if (d->k_stride_token < d->head_dim || d->v_stride_token < d->head_dim) return PA_E_STRIDE;
-  if (d->path != PA_PATH_AUTO && d->path != PA_PATH_VALU && d->path != PA_PATH_MFMA) return PA_E_PATH;
+  if (d->path < PA_PATH_AUTO || d->path > PA_PATH_MFMA_STREAM) return PA_E_PATH;
+  if ((d->flags & ~PA_FLAG_KV_SHARED) || d->reserved) return PA_E_SHAPE;
   if (d->partition_size != 0) {
     const int ps = d->partition_size;
     if (ps < 32 || ps > 16384 || ps % 32) return PA_E_PARTITION;
@@ -200,8 +263,15 @@ int prepare(const pa_desc* desc, const float* q, const void* k_cache, const void
 }
 
 int run_partition(const pa_desc* desc, const pa::Params& p, hipStream_t s) {
-  const hipError_t e = pick_path(desc) == PA_PATH_MFMA ? pa::launch_partition_mfma(p, desc->kv_dtype, s)
-                                                       : pa::launch_partition_valu(p, desc->kv_dtype, s);
+  hipError_t e;
+  switch (pick_path(desc)) {
+    case PA_PATH_MFMA_STREAM:
+      e = pa::launch_partition_stream(p, desc->kv_dtype, cu_count(), stream_variant(),
+                                      !(desc->flags & PA_FLAG_KV_SHARED) && stream_nt(), s);
+      break;
+    case PA_PATH_MFMA_GRID: e = pa::launch_partition_mfma(p, desc->kv_dtype, s); break;
+    default: e = pa::launch_partition_valu(p, desc->kv_dtype, s); break;
+  }
   return e == hipSuccess ? PA_OK : PA_E_LAUNCH;
 }
 

@@ -11,8 +11,10 @@
 // already written by the partition kernel and are skipped here.
 //
 // Grid (D / 64, H_q, B), 256 threads: thread (stripe s, quad u) owns dims
-// 4u .. 4u+3 of a 64-dim slice (float4 loads) and partitions p = s, s + 16, ...;
-// the 16 stripes meet in LDS.
+// 4u .. 4u+3 of a 64-dim slice (float4 loads) and partitions p = s, s + 16, ....
+// Each thread folds its partitions with the same max-rescaling op, eight
+// partitions' loads in flight per round, so no pass over all maxima has to
+// finish first; the 16 stripes' states then meet in LDS.
 #include "pa_kernels.h"
 
 namespace pa {
@@ -20,9 +22,11 @@ namespace {
 
 constexpr int kStripes = 16;
 
+// kBatch: partitions per thread per round (1, 4 or 8, from the partition count).
+template <int kBatch>
 __global__ void __launch_bounds__(256) combine_kernel(Params p) {
   const int b = blockIdx.z, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int u = tid & 15, s = tid >> 4;
   const int d = blockIdx.x * 64 + 4 * u;
   const int L = clamped_len(p, b, false);
@@ -32,60 +36,70 @@ __global__ void __launch_bounds__(256) combine_kernel(Params p) {
   const int64_t row = ((int64_t)b * p.Hq + h) * p.pmax;
   const float* mrow = p.ws_m + row;
   const float* lrow = p.ws_l + row;
-
-  // M = max over all n partitions (every wave computes it)
-  float M = -INFINITY;
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, mrow[i]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  const float mu = M == -INFINITY ? 0.f : M;
-
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  float ls = 0.f;
   const float* arow = p.ws_acc + row * p.D + d;
-  int i = s;
-  for (; i + 3 * kStripes < n; i += 4 * kStripes) {  // four partitions in flight
-    float4 x[4];
-    float w[4];
+
+  float Ms = -INFINITY, Ls = 0.f;
+  float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = s; i0 < n; i0 += kStripes * kBatch) {
+    float mv[kBatch], lv[kBatch];
+    float4 av[kBatch];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[k] = *(const float4*)(arow + (int64_t)(i + k * kStripes) * p.D);
-      w[k] = exp2_fast(mrow[i + k * kStripes] - mu);
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = i0 + k * kStripes;
+      mv[k] = -INFINITY;
+      lv[k] = 0.f;
+      av[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < n) {
+        mv[k] = mrow[i];
+        lv[k] = lrow[i];
+        av[k] = *(const float4*)(arow + (int64_t)i * p.D);
+      }
     }
+    float bm = Ms;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      ls += w[k] * lrow[i + k * kStripes];
-      a.x += w[k] * x[k].x;
-      a.y += w[k] * x[k].y;
-      a.z += w[k] * x[k].z;
-      a.w += w[k] * x[k].w;
+    for (int k = 0; k < kBatch; ++k) bm = fmaxf(bm, mv[k]);
+    const float bu = bm == -INFINITY ? 0.f : bm;
+    const float sc = exp2_fast(Ms - bu);
+    Ls *= sc;
+    A.x *= sc;
+    A.y *= sc;
+    A.z *= sc;
+    A.w *= sc;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float w = exp2_fast(mv[k] - bu);
+      Ls += w * lv[k];
+      A.x += w * av[k].x;
+      A.y += w * av[k].y;
+      A.z += w * av[k].z;
+      A.w += w * av[k].w;
     }
-  }
-  for (; i < n; i += kStripes) {
-    const float4 x = *(const float4*)(arow + (int64_t)i * p.D);
-    const float w = exp2_fast(mrow[i] - mu);
-    ls += w * lrow[i];
-    a.x += w * x.x;
-    a.y += w * x.y;
-    a.z += w * x.z;
-    a.w += w * x.w;
+    Ms = bm;
   }
 
   __shared__ float4 s_a[kStripes][16];
-  __shared__ float s_l[kStripes];
-  s_a[s][u] = a;
-  if (u == 0) s_l[s] = ls;
+  __shared__ float s_m[kStripes], s_l[kStripes];
+  s_a[s][u] = A;
+  if (u == 0) {
+    s_m[s] = Ms;
+    s_l[s] = Ls;
+  }
   __syncthreads();
   if (tid < 16) {
+    float M = s_m[0];
+#pragma unroll
+    for (int k = 1; k < kStripes; ++k) M = fmaxf(M, s_m[k]);
+    const float mu = M == -INFINITY ? 0.f : M;
     float tot = 0.f;
     float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int k = 0; k < kStripes; ++k) {
-      tot += s_l[k];
-      num.x += s_a[k][tid].x;
-      num.y += s_a[k][tid].y;
-      num.z += s_a[k][tid].z;
-      num.w += s_a[k][tid].w;
+      const float w = exp2_fast(s_m[k] - mu);
+      tot += w * s_l[k];
+      num.x += w * s_a[k][tid].x;
+      num.y += w * s_a[k][tid].y;
+      num.z += w * s_a[k][tid].z;
+      num.w += w * s_a[k][tid].w;
     }
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
     *(float4*)(p.out + ((int64_t)b * p.Hq + h) * p.D + d) =
@@ -97,7 +111,12 @@ __global__ void __launch_bounds__(256) combine_kernel(Params p) {
 
 hipError_t launch_combine(const Params& p, hipStream_t s) {
   dim3 grid(p.D / 64, p.Hq, p.B);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, p);
+  if (p.pmax <= kStripes)
+    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, s, p);
+  else if (p.pmax <= 4 * kStripes)
+    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

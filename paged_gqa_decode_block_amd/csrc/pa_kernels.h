@@ -37,6 +37,12 @@ enum { kStatusBadBlock = 1, kStatusBadSeqlen = 2 };
 hipError_t launch_partition_valu(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_partition_mfma(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_combine(const Params& p, hipStream_t s);
+// Persistent streaming MFMA kernel on a device with `cus` compute units;
+// `variant` picks a ring depth / occupancy pair (0 = default), `nt` the
+// non-temporal cache policy for K/V loads.
+hipError_t launch_partition_stream(const Params& p, int dtype, int cus, int variant, bool nt,
+                                   hipStream_t s);
+bool stream_supports(int dtype, int D, int G, int block_size, int batch);
 bool valu_supports(int dtype, int D, int G);
 bool mfma_supports(int dtype, int D, int G);
 

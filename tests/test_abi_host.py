@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), f"{name} not exported"
-    assert lib.paged_attn_abi_version() == 1
+    assert lib.paged_attn_abi_version() == 2
 
 
 def test_descriptor_layout_matches_c(tmp_path):
@@ -58,7 +58,12 @@ def _desc(**kw):
 
 def test_valid_descriptor_and_resolved_path():
     assert pa.validate(_desc()) == 0
-    assert pa.PATH_NAME[pa.resolved_path(_desc())] == "mfma"
+    assert pa.PATH_NAME[pa.resolved_path(_desc())] == "mfma_stream"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(path="mfma"))] == "mfma_stream"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(path="mfma_grid"))] == "mfma_grid"
+    # the streaming kernel needs block_size >= 16 and at most 1024 sequences
+    assert pa.PATH_NAME[pa.resolved_path(_desc(block_size=8, k_strides=(2048, 1024, 128)))] == "mfma_grid"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(batch=1025))] == "mfma_grid"
     assert pa.PATH_NAME[pa.resolved_path(_desc(kv_dtype="f32", k_strides=(4096, 2048, 128)))] == "valu"
     assert pa.PATH_NAME[pa.resolved_path(_desc(path="valu"))] == "valu"
 
@@ -79,7 +84,11 @@ def test_valid_descriptor_and_resolved_path():
     (dict(partition_size=32768), -8),
     (dict(block_size=1, partition_size=2048), -8),  # spans more than the block-id table
     (dict(path=9), -10),
+    (dict(path=5), -10),
     (dict(kv_dtype="f32", k_strides=(4096, 2048, 128), path="mfma"), -10),
+    (dict(kv_dtype="f32", k_strides=(4096, 2048, 128), path="mfma_stream"), -10),
+    (dict(block_size=8, k_strides=(2048, 1024, 128), path="mfma_stream"), -10),
+    (dict(batch=2000, path="mfma_stream"), -10),
     (dict(num_q_heads=2 * 12, path="valu"), -2),   # G = 12 beyond the VALU path
     (dict(num_q_heads=2 * 17), -2),                # G = 17 beyond every path
 ])
@@ -145,3 +154,13 @@ def test_decode_argument_errors_return_before_device_work():
     assert pa.decode_raw(dw, **{**args, "ws_ptr": good + 16,
                                 "ws_bytes": pa.workspace_size(dw)}) == -9    # misaligned
     assert pa.decode_raw(_desc(batch=0), **{**args, "q_ptr": 0}) == 0        # nothing to do
+
+
+def test_flags_field():
+    assert pa.validate(_desc(kv_shared=True)) == 0
+    d = _desc()
+    d.flags = 4  # unknown bit
+    assert pa.validate(d) == -2
+    d = _desc()
+    d.reserved = 1
+    assert pa.validate(d) == -2

@@ -45,18 +45,27 @@ def to_device(torch, case):
     )
 
 
-def run_gpu(torch, case, dev=None, *, path="auto", partition_size=None, status=None):
+def run_gpu(torch, case, dev=None, *, path="auto", partition_size=None, status=None,
+            kv_shared=False):
     dev = dev or to_device(torch, case)
     ps = case.partition_size if partition_size is None else partition_size
     out = pa.paged_attn_decode(dev["q"], dev["k"], dev["v"], dev["table"], dev["seqlens"],
                                case.scale, layout=case.layout, partition_size=ps, path=path,
-                               status=status)
+                               status=status, kv_shared=kv_shared)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64)
 
 
-def paths_for(kv_dtype):
-    return ["valu", "mfma"] if kv_dtype != "f32" else ["valu"]
+def paths_for(case):
+    """Every kernel that can run this case: VALU always; for 16-bit K/V the
+    one-workgroup-per-partition MFMA kernel and, for block_size >= 16 and at
+    most 1024 sequences, the persistent streaming MFMA kernel."""
+    if case.kv_dtype == "f32":
+        return ["valu"]
+    out = ["valu", "mfma_grid"]
+    if case.bs >= 16 and case.B <= 1024:
+        out.append("mfma_stream")
+    return out
 
 
 # --- small cases spanning several tiles, ragged tails, edge lengths ---------
@@ -86,7 +95,7 @@ def test_small_cases_match_oracle(torch_cuda, idx):
                             layout=layout, spare=4)
     want = run_oracle(case)
     dev = to_device(torch_cuda, case)
-    for path in paths_for(dt):
+    for path in paths_for(case):
         for ps in (part, 0):
             got = run_gpu(torch_cuda, case, dev, path=path, partition_size=ps)
             assert np.isfinite(got).all(), (path, ps)
@@ -99,8 +108,9 @@ def test_g16_on_matrix_cores(torch_cuda):
     case, _, _ = paged_case(rng, B=2, Hq=32, Hkv=2, D=128, bs=16, kv_dtype="bf16",
                             seqlens=[333, 90])
     want = run_oracle(case)
-    got = run_gpu(torch_cuda, case, path="mfma", partition_size=64)
-    assert np.abs(got - want).max() <= 3e-3
+    for path in ("mfma_grid", "mfma_stream"):
+        got = run_gpu(torch_cuda, case, path=path, partition_size=64)
+        assert np.abs(got - want).max() <= 3e-3, path
 
 
 def test_peaked_softmax_keeps_tolerance(torch_cuda):
@@ -111,7 +121,7 @@ def test_peaked_softmax_keeps_tolerance(torch_cuda):
         case, _, _ = paged_case(rng, B=2, Hq=8, Hkv=2, D=128, bs=16, kv_dtype=dt,
                                 seqlens=[2, 37], scale=4.0 / np.sqrt(128), kv_std=2.0)
         want = run_oracle(case)
-        for path in ("valu", "mfma"):
+        for path in paths_for(case):
             got = run_gpu(torch_cuda, case, path=path, partition_size=32)
             assert np.abs(got - want).max() <= 3e-3, (dt, path)
 
@@ -142,9 +152,8 @@ def sample_pairs(case, n, rng):
     return np.stack([b[:n], h[:n]], axis=1)
 
 
-@pytest.mark.parametrize("k,path", [(1, "valu"), (2, "valu"), (2, "mfma"), (3, "mfma"),
-                                    (3, "valu"), (4, "mfma"), (4, "valu"), (5, "mfma"),
-                                    (5, "valu")])
+@pytest.mark.parametrize("k,path", [(1, "valu")] + [
+    (k, path) for k in (2, 3, 4, 5) for path in ("mfma_stream", "mfma_grid", "valu")])
 def test_config_matches_oracle(torch_cuda, k, path):
     case = config_case(k)
     rng = np.random.default_rng(k)
@@ -157,6 +166,19 @@ def test_config_matches_oracle(torch_cuda, k, path):
     err = np.abs(got - want).max()
     print(f"config {k} {path}: max-abs error {err:.3e}")
     assert err <= TOL[case.kv_dtype]
+
+
+def test_config5_shared_blocks_cacheable_loads(torch_cuda):
+    """The prefix-shared workload with the shared-blocks flag (cacheable K/V
+    loads) and the library's own partition choice."""
+    case = config_case(5)
+    rng = np.random.default_rng(55)
+    pairs = sample_pairs(case, 192, rng)
+    want = run_oracle(case, pairs=pairs)
+    for path in ("mfma_stream", "auto"):
+        got = run_gpu(torch_cuda, case, path=path, partition_size=0, kv_shared=True)
+        assert np.isfinite(got).all()
+        assert np.abs(got[pairs[:, 0], pairs[:, 1]] - want).max() <= 3e-3, path
 
 
 def test_config1_combine_path(torch_cuda):
@@ -176,7 +198,7 @@ def test_invalid_entries_are_skipped_and_reported(torch_cuda):
                             seqlens=[70, 40, 20])
     case.block_table[0, 1] = -1          # unassigned entry inside the attended range
     case.block_table[1, 0] = case.NB     # beyond the pool
-    for path in ("valu", "mfma"):
+    for path in paths_for(case):
         status = torch.zeros(1, dtype=torch.int32, device="cuda")
         got = run_gpu(torch, case, path=path, partition_size=32, status=status)
         assert int(status.item()) & pa.PA_STATUS_BAD_BLOCK
@@ -184,9 +206,10 @@ def test_invalid_entries_are_skipped_and_reported(torch_cuda):
     case.block_table[0, 1] = case.block_table[0, 0]
     case.block_table[1, 0] = case.block_table[1, 1]
     case.seqlens[2] = case.MBS * case.bs + 5   # too long: clamped and reported
-    status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    run_gpu(torch, case, path="mfma", partition_size=32, status=status)
-    assert int(status.item()) & pa.PA_STATUS_BAD_SEQLEN
+    for path in paths_for(case):
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        run_gpu(torch, case, path=path, partition_size=32, status=status)
+        assert int(status.item()) & pa.PA_STATUS_BAD_SEQLEN, path
 
 
 def test_block_relabeling_and_reruns_are_bitwise_identical(torch_cuda):
@@ -200,7 +223,7 @@ def test_block_relabeling_and_reruns_are_bitwise_identical(torch_cuda):
     v2[1 + perm] = case.v_store[1:]
     t2 = np.where(case.block_table >= 0, perm[np.maximum(case.block_table, 0)], -1).astype(np.int32)
     c2 = W.Case(**{**case.__dict__, "k_store": k2, "v_store": v2, "block_table": t2})
-    for path in ("valu", "mfma"):
+    for path in paths_for(case):
         a = run_gpu(torch, case, path=path, partition_size=64)
         b = run_gpu(torch, case, path=path, partition_size=64)
         c = run_gpu(torch, c2, path=path, partition_size=64)
@@ -211,8 +234,42 @@ def test_single_token_returns_v_row(torch_cuda):
     rng = np.random.default_rng(92)
     case, Kc, Vc = paged_case(rng, B=4, Hq=8, Hkv=2, D=256, bs=16, kv_dtype="bf16",
                               seqlens=[1, 1, 1, 1])
-    for path in ("valu", "mfma"):
+    for path in paths_for(case):
         got = run_gpu(torch_cuda, case, path=path)
         for b in range(4):
             for h in range(8):
                 assert np.array_equal(got[b, h], Vc[b][h // 4][0]), path
+
+
+# --- the streaming kernel's work split -----------------------------------------
+
+STREAM_CASES = [
+    # name, B, Hq, Hkv, D, bs, dtype, seqlens, partition
+    ("many_partitions_per_wave", 3, 16, 2, 128, 16, "bf16", [3000, 77, 1500], 32),
+    ("empty_between", 6, 8, 4, 64, 16, "f16", [0, 300, 0, 0, 45, 1], 64),
+    ("d256_short_parts", 2, 12, 2, 256, 32, "bf16", [900, 2000], 64),
+    ("partial_last_chunk", 2, 8, 1, 128, 64, "bf16", [33, 1025], 512),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(STREAM_CASES)), ids=[s[0] for s in STREAM_CASES])
+def test_stream_kernel_work_split(torch_cuda, idx):
+    name, B, Hq, Hkv, D, bs, dt, L, part = STREAM_CASES[idx]
+    rng = np.random.default_rng(700 + idx)
+    case, _, _ = paged_case(rng, B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, kv_dtype=dt, seqlens=L, spare=2)
+    want = run_oracle(case)
+    got = run_gpu(torch_cuda, case, path="mfma_stream", partition_size=part)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= 3e-3
+
+
+def test_stream_kernel_thousand_sequences(torch_cuda):
+    """1000 sequences: the item prefix spans all 16 windows of the scan."""
+    rng = np.random.default_rng(800)
+    L = rng.integers(0, 120, size=1000)
+    case, _, _ = paged_case(rng, B=1000, Hq=4, Hkv=2, D=64, bs=16, kv_dtype="bf16", seqlens=L)
+    pairs = np.stack([np.arange(1000), rng.integers(0, 4, size=1000)], axis=1)
+    want = run_oracle(case, pairs=pairs)
+    for ps in (32, 64):
+        got = run_gpu(torch_cuda, case, path="mfma_stream", partition_size=ps)
+        assert np.abs(got[pairs[:, 0], pairs[:, 1]] - want).max() <= 3e-3, ps
