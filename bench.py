@@ -146,9 +146,13 @@ def measure(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
     for _ in range(warmup):
         wl.call()
     ms = time_steps(torch, wl.call, steps)
+    # the partition kernel alone: one event pair around `steps` back-to-back
+    # launches on the launch stream (average launch duration), plus per-launch
+    # event pairs for the spread
+    part_avg_ms = time_steps(torch, lambda: wl.call("partition"), steps)
     part_ms = time_each(torch, lambda: wl.call("partition"), steps)
     wl.call()  # leave the workspace of a complete call behind for the combine timing
-    comb_ms = time_each(torch, lambda: wl.call("combine"), steps)
+    comb_ms = time_steps(torch, lambda: wl.call("combine"), steps)
     cold_ms = time_each(torch, wl.call, max(5, steps // 4), flush=lambda: flush_buf.add_(1))
     c = wl.case
     t = ms / 1e3
@@ -156,10 +160,10 @@ def measure(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
         "ms_per_step": ms,
         "kv_gbs": wl.kv_bytes / t / 1e9,
         "seq_heads_per_s": c.B * c.Hq / t,
-        "partition_kernel_us": float(part_ms.mean() * 1e3),
+        "partition_kernel_us": float(part_avg_ms * 1e3),
         "partition_kernel_us_p10_p90": [float(np.percentile(part_ms, 10) * 1e3),
                                         float(np.percentile(part_ms, 90) * 1e3)],
-        "combine_kernel_us": float(comb_ms.mean() * 1e3),
+        "combine_kernel_us": float(comb_ms * 1e3),
         "cold_ms_median": float(np.median(cold_ms)),
         "cold_kv_gbs": wl.kv_bytes / (np.median(cold_ms) / 1e3) / 1e9,
         "kv_bytes": wl.kv_bytes,
@@ -207,6 +211,15 @@ def cpu_baseline(wl: Workload, budget_s: float) -> dict:
         if dt > budget_s / 3 or n >= len(pairs_all):
             break
         n = min(len(pairs_all), int(n * max(2.0, budget_s / 3 / max(dt, 1e-3))))
+    if used == len(pairs_all):  # the whole batch fits the budget: best of up to 3 runs
+        for _ in range(2):
+            if t_used * 2 > budget_s:
+                break
+            t0 = time.perf_counter()
+            O.paged_attn_decode(c.q, c.k_pool, c.v_pool, c.block_table, c.seqlens, c.scale,
+                                kv_dtype=c.kv_dtype, block_size=c.bs, num_kv_heads=c.Hkv,
+                                layout=c.layout, pairs=pairs_all, nthreads=threads)
+            t_used = min(t_used, time.perf_counter() - t0)
     tok_sample = int(c.seqlens[pairs_all[:used, 0]].astype(np.int64).sum())
     tok_all = int(c.seqlens.astype(np.int64).sum()) * c.Hq
     t_full = t_used * tok_all / tok_sample
@@ -214,7 +227,7 @@ def cpu_baseline(wl: Workload, budget_s: float) -> dict:
             "kind": "oracle",
             "sample": f"{used} of {c.B * c.Hq} (sequence, query head) pairs of {c.name} "
                       f"({tok_sample} of {tok_all} head-tokens) in {t_used:.2f}s, "
-                      "extrapolated by head-token count",
+                      "extrapolated by head-token count (best of up to 3 runs when the whole batch fits)",
             "seq_heads_per_s": round(c.B * c.Hq / t_full, 3)}
 
 
