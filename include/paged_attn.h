@@ -47,10 +47,12 @@ typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } 
 /* Which partition kernel runs: VALU (vector ALU dot products and reductions) or
  * MFMA (matrix-core micro-GEMMs for the G x d . d x N scores and the P . V
  * product). MFMA needs f16 or bf16 K/V and has two kernels: MFMA_STREAM, a
- * persistent kernel in which each wave streams a contiguous run of partitions
- * (block_size >= 16, batch <= 1024), and MFMA_GRID, one workgroup per
- * partition (any block size and batch). PA_PATH_MFMA picks MFMA_STREAM when it
- * applies, else MFMA_GRID; AUTO picks MFMA for 16-bit K/V and VALU for fp32. */
+ * persistent kernel in which each wave streams an equal share of the batch's
+ * 16-token chunks (block_size >= 16, batch <= 1024, fewer than 2^31 chunks per
+ * KV head: batch * ceil(max_blocks_per_seq * block_size / 16) < 2^31), and
+ * MFMA_GRID, one workgroup per partition (any block size and batch).
+ * PA_PATH_MFMA picks MFMA_STREAM when it applies, else MFMA_GRID; AUTO picks
+ * MFMA for 16-bit K/V and VALU for fp32. */
 typedef enum pa_path {
   PA_PATH_AUTO = 0,
   PA_PATH_VALU = 1,
@@ -76,8 +78,8 @@ typedef enum pa_path {
                               /* [32, 16384], or spanning more than 1024 blocks       */
 #define PA_E_WORKSPACE (-9)   /* workspace NULL or smaller than required             */
 #define PA_E_PATH (-10)       /* path not a pa_path, an MFMA path asked for f32 K/V, */
-                              /* or MFMA_STREAM asked for block_size < 16 or batch   */
-                              /* > 1024                                              */
+                              /* or MFMA_STREAM asked for block_size < 16, batch     */
+                              /* > 1024 or 2^31 chunks or more                       */
 #define PA_E_LAUNCH (-11)     /* the HIP runtime refused a launch                    */
 #define PA_E_TABLE (-12)      /* (check_inputs) an entry read for an attended token  */
                               /* is outside [0, num_blocks)                           */
@@ -156,14 +158,16 @@ int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache,
 /*
  * The two phases of paged_attn_decode, callable separately (same arguments and
  * rules). paged_attn_partition_phase runs the partition kernel: every
- * (sequence, KV head, partition) folds its tokens into a running softmax state;
- * a sequence with one partition gets its normalised output written to out, the
- * others leave their states in the workspace. paged_attn_combine_phase merges
- * those states into out with the max-rescaling combine (page "Paged Attention
- * Kernel Architecture for BI-V100", section 2 level 3 and section 6 phase 2) and
- * reads only cache_seqlens and the workspace. Calling the partition phase and
- * then the combine phase on one stream equals paged_attn_decode. The combine
- * phase is a no-op when paged_attn_workspace_size() is 0.
+ * (sequence, KV head, partition) folds its tokens into a running softmax state
+ * (on the streaming path a partition may be folded in pieces by several waves);
+ * a sequence whose single partition was folded whole gets its normalised output
+ * written to out, the others leave their states in the workspace.
+ * paged_attn_combine_phase merges those states into out with the max-rescaling
+ * combine (page "Paged Attention Kernel Architecture for BI-V100", section 2
+ * level 3 and section 6 phase 2) and reads only cache_seqlens and the
+ * workspace. Calling the partition phase and then the combine phase on one
+ * stream equals paged_attn_decode; the partition phase alone completes out only
+ * when paged_attn_workspace_size() is 0. The combine phase is a no-op then.
  */
 int paged_attn_partition_phase(const pa_desc* desc, const float* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,
@@ -173,9 +177,13 @@ int paged_attn_partition_phase(const pa_desc* desc, const float* q, const void* 
 int paged_attn_combine_phase(const pa_desc* desc, const int32_t* cache_seqlens, float* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace paged_attn_decode needs for this descriptor: the partial
- * (max, sum, output) of every possible partition, sized from
- * max_blocks_per_seq * block_size. 0 when one partition always suffices.
+/* Bytes of workspace paged_attn_decode needs for this descriptor on the
+ * current device: the partial (max, sum, output) of every possible partition,
+ * sized from max_blocks_per_seq * block_size, and on the streaming path
+ * (PA_PATH_MFMA_STREAM) also a link per partition and one continuation state per
+ * wave of the kernel's grid, which depends on the device's compute-unit count.
+ * 0 when one partition always suffices and the path is not the streaming one.
+ * The contents need no initialisation and carry nothing between calls.
  * Returns 0 for an invalid descriptor too; call paged_attn_validate first. */
 size_t paged_attn_workspace_size(const pa_desc* desc);
 

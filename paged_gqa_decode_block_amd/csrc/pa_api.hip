@@ -25,19 +25,18 @@ int64_t max_tokens(const pa_desc* d) { return (int64_t)d->max_blocks_per_seq * d
 
 int pick_path(const pa_desc* d);
 int cu_count();
+int stream_variant();
 
 // Partition size for a descriptor that passed validation of everything else.
-// Without a caller choice: for the streaming kernel, 2048 tokens when there are
-// at least as many (sequence, KV head) streams as waves (each wave then walks
-// whole streams and larger partitions mean fewer partial states), else 512;
-// for the other kernels 512, halved (down to 64) while the busiest possible
-// grid would hold fewer than 1024 work items.
+// Without a caller choice: 4096 tokens for the streaming kernel (its waves
+// split the work by chunks, so the partition size only sets how many partial
+// states are written and merged); for the other kernels 512, halved (down to
+// 64) while the busiest possible grid would hold fewer than 1024 work items.
 int pick_partition(const pa_desc* d) {
   if (d->partition_size > 0) return d->partition_size;
   const int64_t T = max_tokens(d);
   if (pick_path(d) == PA_PATH_MFMA_STREAM) {
-    const int64_t streams = (int64_t)d->batch * d->num_kv_heads;
-    int part = streams >= 8LL * cu_count() ? 2048 : 512;
+    int part = 4096;
     while ((part >> ilog2(d->block_size)) + 2 > pa::kTableCap && part > 32) part >>= 1;
     return part;
   }
@@ -53,8 +52,10 @@ int pick_partition(const pa_desc* d) {
 // PA_PATH_MFMA_STREAM (or an error).
 int pick_path(const pa_desc* d) {
   const int G = d->num_q_heads / d->num_kv_heads;
+  // the streaming kernel counts a batch's 16-token chunks per KV head in 32 bits
   const bool stream_ok =
-      pa::stream_supports(d->kv_dtype, d->head_dim, G, d->block_size, d->batch);
+      pa::stream_supports(d->kv_dtype, d->head_dim, G, d->block_size, d->batch) &&
+      (int64_t)d->batch * ((max_tokens(d) + 15) / 16) < ((int64_t)1 << 31);
   switch (d->path) {
     case PA_PATH_VALU:
       return pa::valu_supports(d->kv_dtype, d->head_dim, G) ? PA_PATH_VALU : PA_E_SHAPE;
@@ -95,6 +96,15 @@ bool stream_nt() {
     v = (e && e[0] == '0') ? 0 : 1;
   }
   return v == 1;
+}
+
+// Grid of the streaming kernel for a descriptor on the current device: it
+// bounds the chunks of work by max_blocks_per_seq * block_size tokens per
+// sequence.
+int stream_waves(const pa_desc* d) {
+  const int64_t chunks_per_stream = (max_tokens(d) + 15) / 16;
+  return pa::stream_grid(d->head_dim, stream_variant(), cu_count(),
+                         (int64_t)d->batch * d->num_kv_heads * chunks_per_stream);
 }
 
 // Compute units of the current device (cached per device).
@@ -143,6 +153,34 @@ int validate(const pa_desc* d) {
   return path < 0 ? path : PA_OK;
 }
 
+// Workspace regions of a valid descriptor, as byte offsets (each 256-byte
+// aligned; off[kWsParts] is the total): partition states m, l, acc for every
+// (sequence, query head, partition), then for the streaming kernel the
+// partition links and one continuation state per wave. Kernels other than the
+// streaming one need nothing when one partition always suffices.
+enum { kWsM, kWsL, kWsAcc, kWsLink, kWsCm, kWsCl, kWsCacc, kWsCmore, kWsParts };
+void workspace_layout(const pa_desc* d, size_t* off) {
+  const int part = pick_partition(d);
+  const int64_t pmax = (max_tokens(d) + part - 1) / part;
+  const bool stream = pick_path(d) == PA_PATH_MFMA_STREAM;
+  size_t sz[kWsParts] = {0};
+  if (stream || pmax > 1) {
+    const size_t rows = (size_t)d->batch * d->num_q_heads * (size_t)pmax;
+    sz[kWsM] = sz[kWsL] = rows * sizeof(float);
+    sz[kWsAcc] = rows * d->head_dim * sizeof(float);
+  }
+  if (stream) {
+    const int G = d->num_q_heads / d->num_kv_heads;
+    const size_t waves = (size_t)stream_waves(d);
+    sz[kWsLink] = (size_t)d->batch * d->num_kv_heads * (size_t)pmax * sizeof(int32_t);
+    sz[kWsCm] = sz[kWsCl] = waves * G * sizeof(float);
+    sz[kWsCacc] = waves * G * d->head_dim * sizeof(float);
+    sz[kWsCmore] = waves * sizeof(int32_t);
+  }
+  off[0] = 0;
+  for (int i = 0; i < kWsParts; ++i) off[i + 1] = off[i] + align256(sz[i]);
+}
+
 }  // namespace
 
 extern "C" {
@@ -163,11 +201,9 @@ int paged_attn_resolved_path(const pa_desc* desc) {
 
 size_t paged_attn_workspace_size(const pa_desc* desc) {
   if (validate(desc) != PA_OK) return 0;
-  const int part = pick_partition(desc);
-  const int64_t pmax = (max_tokens(desc) + part - 1) / part;
-  if (pmax <= 1) return 0;
-  const size_t rows = (size_t)desc->batch * desc->num_q_heads * (size_t)pmax;
-  return 2 * align256(rows * sizeof(float)) + align256(rows * desc->head_dim * sizeof(float));
+  size_t off[kWsParts + 1];
+  workspace_layout(desc, off);
+  return off[kWsParts];
 }
 
 int paged_attn_check_inputs(const pa_desc* desc, const int32_t* table, const int32_t* seqlens) {
@@ -252,12 +288,22 @@ int prepare(const pa_desc* desc, const float* q, const void* k_cache, const void
   p.part = part;
   p.pmax = (int)((max_tokens(desc) + part - 1) / part);
   p.qscale = scale * 1.4426950408889634f;  // log2(e): scores in base-2 units
+  p.cus = cu_count();
   if (need > 0) {
-    const size_t rows = (size_t)p.B * p.Hq * (size_t)p.pmax;
+    size_t off[kWsParts + 1];
+    workspace_layout(desc, off);
     char* ws = (char*)workspace;
-    p.ws_m = (float*)ws;
-    p.ws_l = (float*)(ws + align256(rows * sizeof(float)));
-    p.ws_acc = (float*)(ws + 2 * align256(rows * sizeof(float)));
+    p.ws_m = (float*)(ws + off[kWsM]);
+    p.ws_l = (float*)(ws + off[kWsL]);
+    p.ws_acc = (float*)(ws + off[kWsAcc]);
+    if (pick_path(desc) == PA_PATH_MFMA_STREAM) {
+      p.ws_link = (int32_t*)(ws + off[kWsLink]);
+      p.ws_cm = (float*)(ws + off[kWsCm]);
+      p.ws_cl = (float*)(ws + off[kWsCl]);
+      p.ws_cacc = (float*)(ws + off[kWsCacc]);
+      p.ws_cmore = (int32_t*)(ws + off[kWsCmore]);
+      p.nwaves = stream_waves(desc);
+    }
   }
   return PA_OK;
 }
@@ -266,7 +312,7 @@ int run_partition(const pa_desc* desc, const pa::Params& p, hipStream_t s) {
   hipError_t e;
   switch (pick_path(desc)) {
     case PA_PATH_MFMA_STREAM:
-      e = pa::launch_partition_stream(p, desc->kv_dtype, cu_count(), stream_variant(),
+      e = pa::launch_partition_stream(p, desc->kv_dtype, stream_variant(),
                                       !(desc->flags & PA_FLAG_KV_SHARED) && stream_nt(), s);
       break;
     case PA_PATH_MFMA_GRID: e = pa::launch_partition_mfma(p, desc->kv_dtype, s); break;
@@ -276,7 +322,9 @@ int run_partition(const pa_desc* desc, const pa::Params& p, hipStream_t s) {
 }
 
 int run_combine(const pa::Params& p, hipStream_t s) {
-  if (p.pmax <= 1) return PA_OK;
+  // without links (kernels other than the streaming one) a single partition
+  // was written out already
+  if (p.pmax <= 1 && !p.ws_link) return PA_OK;
   return pa::launch_combine(p, s) == hipSuccess ? PA_OK : PA_E_LAUNCH;
 }
 

@@ -10,6 +10,14 @@
 // partitions at once; only p < n is read. Sequences with one partition were
 // already written by the partition kernel and are skipped here.
 //
+// After the streaming kernel a partition may have been split between waves:
+// its slot then holds the first piece and its link names the wave holding the
+// next piece (a continuation slot, which says whether a further wave holds
+// more). The pieces are folded into the partition's state with the same op
+// before it joins the merge. With that kernel a sequence's single partition is
+// read here too unless its link says it was written out, and an empty sequence
+// gets zeros.
+//
 // Grid (D / 64, H_q, B), 256 threads: thread (stripe s, quad u) owns dims
 // 4u .. 4u+3 of a 64-dim slice (float4 loads) and partitions p = s, s + 16, ....
 // Each thread folds its partitions with the same max-rescaling op, eight
@@ -31,28 +39,90 @@ __global__ void __launch_bounds__(256) combine_kernel(Params p) {
   const int d = blockIdx.x * 64 + 4 * u;
   const int L = clamped_len(p, b, false);
   const int n = (L + p.part - 1) / p.part;
-  if (n <= 1) return;
+  const bool chained = p.ws_link != nullptr;
+  const int hk = h / p.G, g = h - hk * p.G;
+  const int32_t* link = chained ? p.ws_link + ((int64_t)b * p.Hkv + hk) * p.pmax : nullptr;
+  if (chained ? (n == 1 && link[0] == -2) : n <= 1) return;
 
   const int64_t row = ((int64_t)b * p.Hq + h) * p.pmax;
   const float* mrow = p.ws_m + row;
   const float* lrow = p.ws_l + row;
   const float* arow = p.ws_acc + row * p.D + d;
 
+  // (m, l, a) <- (m, l, a) merged with (cm, cl, ca)
+  auto merge = [](float& m, float& l, float4& a, float cm, float cl, float4 ca) {
+    const float M = fmaxf(m, cm);
+    const float mu = M == -INFINITY ? 0.f : M;
+    const float w0 = exp2_fast(m - mu), w1 = exp2_fast(cm - mu);
+    l = w0 * l + w1 * cl;
+    a.x = w0 * a.x + w1 * ca.x;
+    a.y = w0 * a.y + w1 * ca.y;
+    a.z = w0 * a.z + w1 * ca.z;
+    a.w = w0 * a.w + w1 * ca.w;
+    m = M;
+  };
+  // continuation piece of link lk (a wave index + 1); returns the next link
+  auto piece = [&](int lk, float& cm, float& cl, float4& ca) {
+    const int64_t c = (int64_t)(lk - 1) * p.G + g;
+    cm = p.ws_cm[c];
+    cl = p.ws_cl[c];
+    ca = *(const float4*)(p.ws_cacc + c * p.D + d);
+    return p.ws_cmore[lk - 1] ? lk + 1 : 0;
+  };
+
   float Ms = -INFINITY, Ls = 0.f;
   float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int i0 = s; i0 < n; i0 += kStripes * kBatch) {
     float mv[kBatch], lv[kBatch];
     float4 av[kBatch];
+    int lkv[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int i = i0 + k * kStripes;
       mv[k] = -INFINITY;
       lv[k] = 0.f;
       av[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      lkv[k] = -1;
       if (i < n) {
         mv[k] = mrow[i];
         lv[k] = lrow[i];
         av[k] = *(const float4*)(arow + (int64_t)i * p.D);
+        if (chained) lkv[k] = link[i];
+      }
+    }
+    if (chained) {
+      // The first two pieces of every chain in the batch are loaded together
+      // (the second speculatively: continuation slots of consecutive waves are
+      // adjacent); longer chains are walked after.
+      float cm[kBatch], cl[kBatch], cm2[kBatch], cl2[kBatch];
+      float4 ca[kBatch], ca2[kBatch];
+      int nx[kBatch], nx2[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        cm[k] = cm2[k] = -INFINITY;
+        cl[k] = cl2[k] = 0.f;
+        ca[k] = ca2[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        nx[k] = nx2[k] = 0;
+        const int lk = lkv[k];
+        if (lk > 0 && lk <= p.nwaves) {
+          nx[k] = piece(lk, cm[k], cl[k], ca[k]);
+          if (lk + 1 <= p.nwaves) nx2[k] = piece(lk + 1, cm2[k], cl2[k], ca2[k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        merge(mv[k], lv[k], av[k], cm[k], cl[k], ca[k]);
+        if (nx[k] > 0) {  // the second piece belongs to this partition
+          merge(mv[k], lv[k], av[k], cm2[k], cl2[k], ca2[k]);
+          nx[k] = nx2[k];
+        }
+        for (int lk = nx[k]; lk > 0 && lk <= p.nwaves;) {
+          float m1, l1;
+          float4 a1;
+          const int nl = piece(lk, m1, l1, a1);
+          merge(mv[k], lv[k], av[k], m1, l1, a1);
+          lk = nl;
+        }
       }
     }
     float bm = Ms;

@@ -21,6 +21,13 @@ struct Params {
   float* ws_m;              // [B, Hq, pmax]  running max, base-2 units
   float* ws_l;              // [B, Hq, pmax]  sum of 2^(s - m)
   float* ws_acc;            // [B, Hq, pmax, D] unnormalised output
+  // streaming kernel only (NULL otherwise): partition links and the waves'
+  // continuation states (a piece of a partition that starts inside it)
+  int32_t* ws_link;         // [B, Hkv, pmax] -2 written out, -1 complete, else continuing wave + 1
+  float* ws_cm;             // [waves, G]
+  float* ws_cl;             // [waves, G]
+  float* ws_cacc;           // [waves, G, D]
+  int32_t* ws_cmore;        // [waves] 1 when the partition goes on into the next wave
   int32_t* status;          // optional
   int64_t ksb, ksh, kst;    // K strides (elements)
   int64_t vsb, vsh, vst;    // V strides
@@ -29,6 +36,8 @@ struct Params {
   int part;                 // partition size in tokens
   int pmax;                 // ceil(MBS * bs / part)
   float qscale;             // scale * log2(e): scores are kept in base-2 units
+  int cus;                  // compute units of the device (streaming kernel)
+  int nwaves;               // continuation slots in the workspace (streaming kernel)
 };
 
 enum { kStatusBadBlock = 1, kStatusBadSeqlen = 2 };
@@ -37,12 +46,26 @@ enum { kStatusBadBlock = 1, kStatusBadSeqlen = 2 };
 hipError_t launch_partition_valu(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_partition_mfma(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_combine(const Params& p, hipStream_t s);
-// Persistent streaming MFMA kernel on a device with `cus` compute units;
+// Persistent streaming MFMA kernel on a device with p.cus compute units;
 // `variant` picks a ring depth / occupancy pair (0 = default), `nt` the
 // non-temporal cache policy for K/V loads.
-hipError_t launch_partition_stream(const Params& p, int dtype, int cus, int variant, bool nt,
-                                   hipStream_t s);
+hipError_t launch_partition_stream(const Params& p, int dtype, int variant, bool nt, hipStream_t s);
 bool stream_supports(int dtype, int D, int G, int block_size, int batch);
+// Grid of the streaming kernel (one wave per workgroup) for head_dim D, ring
+// variant `variant`, `cus` compute units and at most `chunk_bound` 16-token
+// chunks of work; the workspace holds one continuation slot per wave.
+int stream_grid(int D, int variant, int cus, int64_t chunk_bound);
+
+// Waves of the streaming kernel that take work for n_chunks chunks: the whole
+// grid when each gets at least kStreamMinChunks, else fewer, kept a multiple of
+// the compute-unit count while there is at least one per unit.
+constexpr int kStreamMinChunks = 16;
+__host__ __device__ inline int stream_active_waves(int64_t n_chunks, int grid, int cus) {
+  int64_t w = n_chunks / kStreamMinChunks;
+  if (w >= grid) return grid;
+  if (w >= cus) w = w / cus * cus;
+  return (int)(w < 1 ? 1 : w);
+}
 bool valu_supports(int dtype, int D, int G);
 bool mfma_supports(int dtype, int D, int G);
 

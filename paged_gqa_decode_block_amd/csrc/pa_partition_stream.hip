@@ -1,14 +1,21 @@
 // pa_partition_stream.hip -- persistent streaming partition kernel (MFMA, gfx950).
 //
-// The work items are the (sequence b, KV head, KV partition p) triples of the
-// split-KV decomposition (page "Paged Attention Kernel Architecture for
-// BI-V100", sections 4 and 6), numbered sequence by sequence, KV head by KV
-// head, partition by partition. One wave per SIMD is launched and wave w takes a
-// contiguous run of items, so it mostly walks one (b, KV head) token stream
-// across several partitions. Along that stream it keeps a ring of NBUF 16-token
-// chunks of K and V in flight in registers (as many as the 6-bit vector-memory
-// counter can track), so the memory system always has ~50-60 KB per wave
-// outstanding and no partition starts with an empty pipeline.
+// The split-KV decomposition (page "Paged Attention Kernel Architecture for
+// BI-V100", sections 4 and 6) is counted in 16-token chunks: each (sequence b,
+// KV head) token stream has ceil(L_b / 16) of them, numbered sequence by
+// sequence, KV head by KV head. One or two waves per SIMD are launched (a
+// multiple of the compute-unit count) and the waves in use take equal
+// contiguous shares of the chunks, so every compute unit streams the same number
+// of bytes. A share mostly walks one stream. Along a stream the wave keeps a
+// ring of NBUF 16-token chunks of K and V in flight in registers; the ring's
+// issue is unconditional and its table reads travel in ring order, so the wait
+// before each chunk covers that chunk's loads only.
+//
+// Partial states stay per partition (PART tokens of a stream): a piece of a
+// partition that starts at the partition's first chunk goes to the partition's
+// slot together with a link; a share that begins inside a partition leaves that
+// first piece in the wave's continuation slot, and the link of the partition
+// names the wave. The combine kernel follows the links.
 //
 // Loads are raw buffer loads of full token rows (each 16-byte lane load is part
 // of a contiguous row segment of 128-512 bytes) with the non-temporal hint. The
@@ -29,13 +36,15 @@
 // Q' and P are split into hi + lo 16-bit parts (two MFMAs each) so products keep
 // ~16 mantissa bits. The running output is rescaled lazily: p = 2^(s - m) uses a
 // reference max m that is only raised (and acc, l rescaled) when a score exceeds
-// it by more than 8, so p <= 256 and most chunks skip the rescale. Whenever the stream crosses a partition boundary the
-// partition's state is written (workspace, or normalised output when the
-// sequence has one partition) and reset. Tokens at or past L_b and chunks behind
-// an invalid table entry are never loaded; their scores are -inf.
+// it by more than 8, so p <= 256 and most chunks skip the rescale. At every
+// partition boundary and at the end of a share the piece's state is written
+// (partition slot or continuation slot, or the normalised output when the piece
+// is a whole single-partition sequence) and reset. Tokens at or past L_b and
+// chunks behind an invalid table entry are never loaded; their scores are -inf.
 //
-// Requires block_size >= 16 (a 16-token chunk lies in one block) and at most
-// 1024 sequences (the item prefix is formed in registers).
+// Requires block_size >= 16 (a 16-token chunk lies in one block), at most 1024
+// sequences (the chunk prefix is formed in registers) and fewer than 2^31
+// chunks per KV head in the batch.
 #include <type_traits>
 
 #include "pa_kernels.h"
@@ -178,52 +187,57 @@ partition_stream_kernel(Params p) {
   const int G = p.G, Hkv = p.Hkv, PART = p.part;
   const int CPP = PART >> 4;  // chunks per partition
 
-  // ---- 1. partitions per sequence and this wave's item range ---------------
-  // np(b) = max(1, ceil(L_b / PART)) (an empty sequence still has one item: it
-  // writes zeros). Items of sequence b: Hkv * np(b).
+  // ---- 1. chunk counts and this wave's share ---------------------------------
+  // Work is counted in 16-token chunks: sequence b has nc(b) = ceil(L_b / 16)
+  // chunks per KV head, numbered sequence by sequence, KV head by KV head,
+  // token by token. The waves in use take equal contiguous shares (sizes at
+  // most one chunk apart), and their number is a multiple of the compute-unit
+  // count whenever there is enough work, so every compute unit streams the
+  // same number of bytes until the end. A share may begin or end inside a
+  // partition; the wave then leaves that piece as a continuation state.
   const int nwin = (p.B + 63) >> 6;
-  int npw[kMaxWindows];
+  int ncw[kMaxWindows];
   int tot = 0;
 #pragma unroll
   for (int wi = 0; wi < kMaxWindows; ++wi) {
-    int np = 0;
+    int nc = 0;
     if (wi < nwin) {
       const int b = wi * 64 + lane;
-      if (b < p.B) {
-        const int L = clamped_len(p, b, blockIdx.x == 0);
-        np = L == 0 ? 1 : (L + PART - 1) / PART;
-      }
+      if (b < p.B) nc = (clamped_len(p, b, blockIdx.x == 0) + 15) >> 4;
     }
-    npw[wi] = np;
+    ncw[wi] = nc;
   }
 #pragma unroll
   for (int wi = 0; wi < kMaxWindows; ++wi) {
-    int s = npw[wi];
+    int s = ncw[wi];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
     tot += s;  // uniform
   }
-  const int64_t n_items = (int64_t)tot * Hkv;
-  int64_t i = n_items * blockIdx.x / gridDim.x;
-  const int64_t i_end = n_items * (blockIdx.x + 1) / gridDim.x;
-  if (i >= i_end) return;
+  const int64_t n_chunks = (int64_t)tot * Hkv;
+  const int nw = stream_active_waves(n_chunks, (int)gridDim.x, p.cus);
+  if ((int)blockIdx.x >= nw) return;
+  int64_t g = n_chunks * blockIdx.x / nw;
+  const int64_t g_end = n_chunks * (blockIdx.x + 1) / nw;
+  if (g >= g_end) return;
 
-  // sequence holding item i: P(b) <= i / Hkv < P(b + 1)
-  int b = 0, Pb = 0, npb = 1;
+  // sequence holding chunk g: Hkv * P(b) <= g < Hkv * P(b + 1), P = prefix of nc
+  int b = 0, ncb = 1;
+  int64_t Pb = 0;
   {
-    const int x = (int)(i / Hkv);
+    const int x = (int)(g / Hkv);
     int carry = 0;
     bool found = false;
 #pragma unroll
     for (int wi = 0; wi < kMaxWindows; ++wi) {
       if (!found && wi < nwin) {
-        const int incl = wave_incl_scan(npw[wi], lane) + carry;
-        const uint64_t hit = __ballot(incl > x && npw[wi] > 0);
+        const int incl = wave_incl_scan(ncw[wi], lane) + carry;
+        const uint64_t hit = __ballot(incl > x && ncw[wi] > 0);
         if (hit) {
           const int src = __builtin_ctzll(hit);
           b = wi * 64 + src;
-          npb = __shfl(npw[wi], src);
-          Pb = __shfl(incl, src) - npb;
+          ncb = __shfl(ncw[wi], src);
+          Pb = __shfl(incl, src) - ncb;
           found = true;
         }
         carry = __shfl(incl, 63);
@@ -231,6 +245,12 @@ partition_stream_kernel(Params p) {
     }
   }
   int L = clamped_len(p, b, false);
+  int hk, j;
+  {
+    const int64_t e = g - Pb * Hkv;
+    hk = (int)(e / ncb);
+    j = (int)(e - (int64_t)hk * ncb);
+  }
 
   const int bsm = (1 << p.bs_log2) - 1;
   const int rowL = lane / C::CPR;  // row within a load instruction
@@ -246,42 +266,30 @@ partition_stream_kernel(Params p) {
     voffs[s] = (s * C::RPI + rowL) * vst_bytes + 16 * cc;
   }
 
-  // ---- 2. segments: runs of items with the same (b, KV head) ----------------
-  while (i < i_end) {
-    const int e = (int)(i - (int64_t)Pb * Hkv);
-    const int hk = e / npb;
-    const int pf = e - hk * npb;
-    const int pl = (int)min<int64_t>((int64_t)npb, pf + (i_end - i));
-
-    if (L == 0) {  // empty context: zeros for the group's heads
-      for (int k = lane; k < G * D / 4; k += 64) {
-        const int g = k / (D / 4), c4 = k % (D / 4);
-        *(float4*)(p.out + ((int64_t)b * p.Hq + hk * G + g) * D + 4 * c4) = make_float4(0, 0, 0, 0);
-      }
-    } else {
-      const int T0 = pf * PART;
-      const int T1 = min(L, pl * PART);
-      const int nch = (T1 - T0 + 15) >> 4;
+  // ---- 2. segments: the share's runs of chunks within one (b, KV head) -------
+  int bad_block = 0;
+  while (g < g_end) {
+    const int jA = j;
+    const int nch = (int)min<int64_t>((int64_t)(ncb - j), g_end - g);
+    {
+      const int T0 = 16 * jA;
+      const int T1 = min(L, 16 * (jA + nch));
       const int32_t* trow = p.table + (int64_t)b * p.MBS;
       const char* kbase = (const char*)p.k + (int64_t)hk * p.ksh * (int)sizeof(T);
       const char* vbase = (const char*)p.v + (int64_t)hk * p.vsh * (int)sizeof(T);
 
-      // block id of chunk cw + lane (invalid -> -1, reported)
-      auto load_ids = [&](int cw) {
-        int id = -1;
-        const int c = cw + lane;
-        if (c < nch) {
-          id = trow[(T0 + 16 * c) >> p.bs_log2];
-          if (id < 0 || id >= p.NB) {
-            if (p.status) atomicOr(p.status, kStatusBadBlock);
-            id = -1;
-          }
-        }
-        return id;
+      // Table entries of the segment's blocks, read through a descriptor over
+      // exactly those entries (chunks past the end read 0 and are masked by
+      // cn < nch). Each issue also fetches the entry of the chunk its ring slot
+      // takes next, NBUF chunks later, so the fetch travels in ring order and
+      // its wait never covers loads still in flight for later chunks.
+      const int nblk = (T1 + bsm) >> p.bs_log2;
+      const __amdgpu_buffer_rsrc_t rst = uniform_rsrc((const char*)trow, nblk * 4);
+      auto fetch_id = [&](int cn) -> int {
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(rst, ((T0 + 16 * cn) >> p.bs_log2) * 4, 0, 0);
       };
-      int cw = 0;
-      int idv = load_ids(0);
-      int idn = nch > 64 ? load_ids(64) : -1;
+      int idr[NBUF];
+      static_for<0, NBUF>([&](auto S) { idr[decltype(S)::value] = fetch_id(decltype(S)::value); });
 
       // Q' fragments of head r (zero for padded heads)
       V8 qhi[kQLds ? 1 : KS], qlo[kQLds ? 1 : KS];
@@ -315,13 +323,18 @@ partition_stream_kernel(Params p) {
       // number of attended rows (0 behind an invalid table entry). The buffer
       // descriptors cover exactly those rows: lanes whose row lies beyond them
       // read zeros without a memory access.
-      auto issue = [&](int cn, uint4 (&rk)[LPC], uint4 (&rv)[LPC]) -> int {
-        if (cn >= cw + 64) {  // the issue pointer enters the next window of ids
-          cw += 64;
-          idv = idn;
-          idn = cw + 64 < nch ? load_ids(cw + 64) : -1;
+      // An entry outside [0, NB) inside the attended range is never
+      // dereferenced; it is noted in bad_block and reported once when the
+      // wave ends (no store or atomic sits between the ring's loads).
+      auto issue = [&](int cn, uint4 (&rk)[LPC], uint4 (&rv)[LPC], int& ids) -> int {
+        int id = -1;
+        if (cn < nch) {
+          id = __builtin_amdgcn_readfirstlane(ids);
+          if (id < 0 || id >= p.NB) {
+            bad_block = 1;
+            id = -1;
+          }
         }
-        const int id = __builtin_amdgcn_readlane(idv, cn - cw);
         const int tok0 = T0 + 16 * cn;
         const int rows = id >= 0 ? min(16, T1 - tok0) : 0;
         const int64_t row0 = id >= 0 ? (int64_t)(tok0 & bsm) : 0;
@@ -335,6 +348,7 @@ partition_stream_kernel(Params p) {
           rk[s] = buf_load<POL>(rsk, koffs[s]);
           rv[s] = buf_load<POL>(rsv, voffs[s]);
         }
+        ids = fetch_id(cn + NBUF);
         return rows;
       };
 
@@ -343,12 +357,35 @@ partition_stream_kernel(Params p) {
       for (int k = 0; k < MB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
       float m = -INFINITY, l = 0.f;
 
-      // write the finished partition pp's state and reset
-      auto flush = [&](int pp) {
+      // Write the state of the piece of partition pp = jc / CPP that ends at
+      // chunk jc, and reset. A piece that starts at its partition's first
+      // chunk goes to the partition's slot, with the partition's link: -2 when
+      // it is the sequence's only partition and complete (the output is then
+      // written here, normalised), -1 when complete, else the next wave, whose
+      // share continues it. Only a share's first piece can start inside a
+      // partition; it goes to this wave's continuation slot, flagged when the
+      // partition goes on into the next wave too.
+      auto flush = [&](int jc) {
+        const int pp = jc / CPP;
+        const bool is_main = pp * CPP >= jA;
+        const bool covers_end = jc + 1 == min(ncb, (pp + 1) * CPP);
+        const bool direct = is_main && covers_end && ncb <= CPP;
         const float lt = quad_sum(l);
+        // one store sequence per destination: a select between two argument
+        // pointers would be compiled into a vector load of the selected
+        // argument, which waits for every K/V load in flight
+        auto store = [&](float* ap, float* mp, float* lp) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            *(float4*)(ap + 16 * mb) = make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
+          if (q == 0) {
+            *mp = m;
+            *lp = lt;
+          }
+        };
         if (r < G) {
           const int h = hk * G + r;
-          if (npb == 1) {
+          if (direct) {
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
             float* op = p.out + ((int64_t)b * p.Hq + h) * D + 4 * q;
 #pragma unroll
@@ -356,17 +393,20 @@ partition_stream_kernel(Params p) {
               const f32x4 o = acc[mb] * inv;
               *(float4*)(op + 16 * mb) = make_float4(o[0], o[1], o[2], o[3]);
             }
-          } else {
+          } else if (is_main) {
             const int64_t row = ((int64_t)b * p.Hq + h) * p.pmax + pp;
-            float* ap = p.ws_acc + row * D + 4 * q;
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              *(float4*)(ap + 16 * mb) = make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
-            if (q == 0) {
-              p.ws_m[row] = m;
-              p.ws_l[row] = lt;
-            }
+            store(p.ws_acc + row * D + 4 * q, p.ws_m + row, p.ws_l + row);
+          } else {
+            const int64_t row = (int64_t)blockIdx.x * G + r;
+            store(p.ws_cacc + row * D + 4 * q, p.ws_cm + row, p.ws_cl + row);
           }
+        }
+        if (lane == 0) {
+          if (is_main)
+            p.ws_link[((int64_t)b * Hkv + hk) * p.pmax + pp] =
+                direct ? -2 : covers_end ? -1 : (int)blockIdx.x + 2;  // wave x + 1, plus one
+          else
+            p.ws_cmore[blockIdx.x] = covers_end ? 0 : 1;
         }
 #pragma unroll
         for (int k = 0; k < MB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -442,71 +482,92 @@ partition_stream_kernel(Params p) {
       };
 
       // ---- the ring: slot c % NBUF holds chunk c; chunk c + NBUF - 1 is issued
-      // just before chunk c is consumed
+      // just before chunk c is consumed. The issue is unconditional (a chunk
+      // past the end has an empty descriptor and reads nothing), so every path
+      // through the loop carries the same loads and the wait before each
+      // consume covers only that chunk's loads, not the whole ring.
       uint4 rk[NBUF][LPC], rv[NBUF][LPC];
       int rows[NBUF];
       static_for<0, NBUF - 1>([&](auto S) {
         constexpr int s = decltype(S)::value;
-        rows[s] = s < nch ? issue(s, rk[s], rv[s]) : 0;
+        rows[s] = issue(s, rk[s], rv[s], idr[s]);
       });
+      int to_bound = CPP - jA % CPP;  // chunks until the next partition boundary
       for (int cb = 0; cb < nch; cb += NBUF) {
         static_for<0, NBUF>([&](auto S) {
           constexpr int s = decltype(S)::value;
           constexpr int sn = (s + NBUF - 1) % NBUF;
           const int c = cb + s;
+          rows[sn] = issue(c + NBUF - 1, rk[sn], rv[sn], idr[sn]);
+          // keep the new chunk's loads ahead of this chunk's wait
+          __builtin_amdgcn_sched_barrier(0);
           if (c < nch) {
-            if (c + NBUF - 1 < nch) rows[sn] = issue(c + NBUF - 1, rk[sn], rv[sn]);
             consume(rows[s], rk[s], rv[s]);
-            if ((c + 1) % CPP == 0 || c + 1 == nch) flush(pf + c / CPP);
+            if (--to_bound == 0 || c + 1 == nch) {
+              flush(jA + c);
+              to_bound = CPP;
+            }
           }
         });
       }
     }
 
-    // advance to the next segment
-    i += pl - pf;
-    if (pl == npb && hk + 1 == Hkv && i < i_end) {
-      Pb += npb;
-      ++b;
-      L = clamped_len(p, b, false);
-      npb = L == 0 ? 1 : (L + PART - 1) / PART;
+    // advance to the next (b, KV head) with chunks
+    g += nch;
+    j = jA + nch;
+    if (j == ncb && g < g_end) {
+      j = 0;
+      if (++hk == Hkv) {
+        hk = 0;
+        do {  // ends: chunks remain, so a non-empty sequence follows
+          ++b;
+          L = clamped_len(p, b, false);
+          ncb = (L + 15) >> 4;
+        } while (ncb == 0);
+      }
     }
   }
+  if (__ballot(bad_block) && lane == 0 && p.status) atomicOr(p.status, kStatusBadBlock);
 }
 
-template <typename T, int D, int NBUF, int OCC, int POL>
-hipError_t launch_t(const Params& p, int cus, hipStream_t s) {
-  const int64_t items = (int64_t)p.B * p.Hkv * p.pmax;
-  const int64_t slots = 4LL * OCC * cus;  // one wave per SIMD slot
-  const int waves = (int)(items < slots ? items : slots);
+// Ring depth / occupancy variants per head_dim (variant 0 is the default).
+// {NBUF, OCC} for head_dim 64, 128, 256.
+constexpr int kVariants[3][3][2] = {
+    {{6, 2}, {3, 2}, {3, 1}},   // 0
+    {{12, 1}, {6, 1}, {2, 1}},  // 1
+    {{4, 4}, {2, 3}, {4, 1}},   // 2
+};
+constexpr int dim_index(int D) { return D == 64 ? 0 : D == 128 ? 1 : 2; }
+
+template <typename T, int D, int V, int POL>
+hipError_t launch_t(const Params& p, hipStream_t s) {
+  constexpr int NBUF = kVariants[V][dim_index(D)][0], OCC = kVariants[V][dim_index(D)][1];
+  const int64_t bound = (int64_t)p.B * p.Hkv * (((int64_t)p.MBS << p.bs_log2) + 15) / 16;
+  const int waves = stream_grid(D, V, p.cus, bound);
   hipLaunchKernelGGL((partition_stream_kernel<T, D, NBUF, OCC, POL>), dim3(waves), dim3(64), 0, s,
                      p);
   return hipGetLastError();
 }
 
-// Ring depth / occupancy variants per head_dim (variant 0 is the default).
 template <typename T, int POL>
-hipError_t launch_v(const Params& p, int cus, int variant, hipStream_t s) {
+hipError_t launch_v(const Params& p, int variant, hipStream_t s) {
+#define PA_STREAM_CASE(DD)                                          \
+  case DD:                                                          \
+    if (variant == 1) return launch_t<T, DD, 1, POL>(p, s);         \
+    if (variant == 2) return launch_t<T, DD, 2, POL>(p, s);         \
+    return launch_t<T, DD, 0, POL>(p, s);
   switch (p.D) {
-    case 64:
-      if (variant == 1) return launch_t<T, 64, 12, 1, POL>(p, cus, s);
-      if (variant == 2) return launch_t<T, 64, 4, 4, POL>(p, cus, s);
-      return launch_t<T, 64, 6, 2, POL>(p, cus, s);
-    case 128:
-      if (variant == 1) return launch_t<T, 128, 6, 1, POL>(p, cus, s);
-      if (variant == 2) return launch_t<T, 128, 2, 3, POL>(p, cus, s);
-      return launch_t<T, 128, 3, 2, POL>(p, cus, s);
-    case 256:
-      if (variant == 1) return launch_t<T, 256, 2, 1, POL>(p, cus, s);
-      if (variant == 2) return launch_t<T, 256, 4, 1, POL>(p, cus, s);
-      return launch_t<T, 256, 3, 1, POL>(p, cus, s);
+    PA_STREAM_CASE(64)
+    PA_STREAM_CASE(128)
+    PA_STREAM_CASE(256)
   }
+#undef PA_STREAM_CASE
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t launch_d(const Params& p, int cus, int variant, bool nt, hipStream_t s) {
-  return nt ? launch_v<T, 2>(p, cus, variant, s) : launch_v<T, 0>(p, cus, variant, s);
+hipError_t launch_d(const Params& p, int variant, bool nt, hipStream_t s) {
+  return nt ? launch_v<T, 2>(p, variant, s) : launch_v<T, 0>(p, variant, s);
 }
 
 }  // namespace
@@ -515,10 +576,15 @@ bool stream_supports(int dtype, int D, int G, int block_size, int batch) {
   return mfma_supports(dtype, D, G) && block_size >= 16 && batch <= kMaxWindows * 64;
 }
 
-hipError_t launch_partition_stream(const Params& p, int dtype, int cus, int variant, bool nt,
-                                   hipStream_t s) {
-  if (dtype == 1) return launch_d<_Float16>(p, cus, variant, nt, s);
-  if (dtype == 2) return launch_d<__bf16>(p, cus, variant, nt, s);
+int stream_grid(int D, int variant, int cus, int64_t chunk_bound) {
+  const int v = variant >= 0 && variant <= 2 ? variant : 0;
+  const int occ = kVariants[v][dim_index(D)][1];
+  return stream_active_waves(chunk_bound, 4 * occ * cus, cus);
+}
+
+hipError_t launch_partition_stream(const Params& p, int dtype, int variant, bool nt, hipStream_t s) {
+  if (dtype == 1) return launch_d<_Float16>(p, variant, nt, s);
+  if (dtype == 2) return launch_d<__bf16>(p, variant, nt, s);
   return hipErrorInvalidValue;
 }
 

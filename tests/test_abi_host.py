@@ -99,27 +99,59 @@ def test_descriptor_errors(kw, code):
     assert pa.strerror(code) not in ("", "unknown status")
 
 
+def _al(x):
+    return (x + 255) // 256 * 256
+
+
+def _stream_waves(d, cus=256, occ=2, min_chunks=16):
+    """Grid of the streaming kernel for head_dim 128 (two waves per SIMD): one
+    wave per SIMD slot, fewer when the chunk bound gives each wave less than 16
+    chunks, kept a multiple of the compute units while one per unit remains.
+    (Without a GPU the library assumes 256 compute units.)"""
+    bound = d.batch * d.num_kv_heads * ((d.max_blocks_per_seq * d.block_size + 15) // 16)
+    grid = 4 * occ * cus
+    w = bound // min_chunks
+    if w >= grid:
+        return grid
+    if w >= cus:
+        w = w // cus * cus
+    return max(w, 1)
+
+
 def test_partition_size_choice_and_workspace():
-    d = _desc(partition_size=512)
+    # kernels with one workgroup per partition: nothing when one partition suffices
+    d = _desc(partition_size=512, path="mfma_grid")
     assert pa.partition_size(d) == 512
-    # pmax = ceil(16*16 / 512) = 1: no partial states needed
-    assert pa.workspace_size(d) == 0
-    d = _desc(partition_size=64)
+    assert pa.workspace_size(d) == 0        # pmax = ceil(16*16 / 512) = 1
+    d = _desc(partition_size=64, path="mfma_grid")
     pmax = 256 // 64
     rows = 2 * 8 * pmax
-    al = lambda x: (x + 255) // 256 * 256
-    assert pa.workspace_size(d) == 2 * al(rows * 4) + al(rows * 128 * 4)
-    # automatic choice: halves from 512 while the grid would be small
-    auto = pa.partition_size(_desc(batch=1, max_blocks_per_seq=6250, num_blocks=6250))
+    assert pa.workspace_size(d) == 2 * _al(rows * 4) + _al(rows * 128 * 4)
+    # the streaming kernel: partition states, links, one continuation state per wave
+    for part, mbs, batch in ((512, 16, 2), (64, 16, 2), (512, 2048, 64)):
+        d = _desc(partition_size=part, max_blocks_per_seq=mbs, batch=batch)
+        assert pa.PATH_NAME[pa.resolved_path(d)] == "mfma_stream"
+        pmax = -(-mbs * 16 // part)
+        rows = batch * 8 * pmax
+        W = _stream_waves(d)
+        want = (2 * _al(rows * 4) + _al(rows * 128 * 4) + _al(batch * 2 * pmax * 4)
+                + 2 * _al(W * 4 * 4) + _al(W * 4 * 128 * 4) + _al(W * 4))
+        assert pa.workspace_size(d) == want, (part, mbs, batch)
+    # automatic choice: 4096 for the streaming kernel; for the others 512,
+    # halved while the grid would be small
+    assert pa.partition_size(_desc(batch=1, max_blocks_per_seq=6250, num_blocks=6250)) == 4096
+    auto = pa.partition_size(_desc(batch=1, max_blocks_per_seq=6250, num_blocks=6250, path="mfma_grid"))
     assert auto in (64, 128, 256, 512)
-    big = pa.partition_size(_desc(batch=64, num_kv_heads=8, num_q_heads=64,
+    big = pa.partition_size(_desc(batch=64, num_kv_heads=8, num_q_heads=64, path="mfma_grid",
                                   max_blocks_per_seq=2048, num_blocks=50000))
     assert big == 512
     # monotone in batch and in max_blocks_per_seq
-    sizes = [pa.workspace_size(_desc(batch=b, partition_size=32)) for b in (1, 2, 4, 8)]
-    assert sizes == sorted(sizes) and sizes[0] > 0
-    sizes = [pa.workspace_size(_desc(max_blocks_per_seq=m, partition_size=32)) for m in (4, 8, 16, 32)]
-    assert sizes == sorted(sizes)
+    for path in ("mfma_grid", "auto"):
+        sizes = [pa.workspace_size(_desc(batch=b, partition_size=32, path=path)) for b in (1, 2, 4, 8)]
+        assert sizes == sorted(sizes) and sizes[0] > 0
+        sizes = [pa.workspace_size(_desc(max_blocks_per_seq=m, partition_size=32, path=path))
+                 for m in (4, 8, 16, 32)]
+        assert sizes == sorted(sizes)
 
 
 def test_check_inputs_on_host_copies():

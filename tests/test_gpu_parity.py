@@ -249,6 +249,12 @@ STREAM_CASES = [
     ("empty_between", 6, 8, 4, 64, 16, "f16", [0, 300, 0, 0, 45, 1], 64),
     ("d256_short_parts", 2, 12, 2, 256, 32, "bf16", [900, 2000], 64),
     ("partial_last_chunk", 2, 8, 1, 128, 64, "bf16", [33, 1025], 512),
+    # one partition per sequence, each split over ~16 waves (500 chunks, 31 waves)
+    ("single_partition_many_waves", 2, 8, 1, 128, 16, "bf16", [4000, 3990], 4096),
+    # nothing to attend: zeros from the combine
+    ("all_empty", 3, 8, 2, 128, 16, "bf16", [0, 0, 0], 64),
+    # 4800 chunks: 300 waves' worth, rounded down to a multiple of the compute units
+    ("waves_rounded_to_cus", 1, 8, 2, 128, 16, "bf16", [38400], 512),
 ]
 
 
@@ -273,3 +279,34 @@ def test_stream_kernel_thousand_sequences(torch_cuda):
     for ps in (32, 64):
         got = run_gpu(torch_cuda, case, path="mfma_stream", partition_size=ps)
         assert np.abs(got[pairs[:, 0], pairs[:, 1]] - want).max() <= 3e-3, ps
+
+
+def test_stream_kernel_continuation_chains(torch_cuda):
+    """The 100K-token workload with 4096- and 8192-token partitions: a wave's
+    share (about 24 chunks) is much shorter than a partition (256 or 512
+    chunks), so each partition is pieced together from ten or more waves'
+    continuation states."""
+    case = config_case(3)
+    want = run_oracle(case)
+    for ps in (4096, 8192):
+        got = run_gpu(torch_cuda, case, path="mfma_stream", partition_size=ps)
+        assert np.isfinite(got).all()
+        assert np.abs(got - want).max() <= 3e-3, ps
+
+
+def test_partition_then_combine_phase_equals_decode(torch_cuda):
+    """The two phases called one after the other give the one-call result bit
+    for bit (same workspace, same stream)."""
+    torch = torch_cuda
+    rng = np.random.default_rng(93)
+    case, _, _ = paged_case(rng, B=3, Hq=16, Hkv=2, D=128, bs=16, kv_dtype="bf16",
+                            seqlens=[3000, 77, 1500])
+    dev = to_device(torch, case)
+    args = (dev["q"], dev["k"], dev["v"], dev["table"], dev["seqlens"], case.scale)
+    for path in ("mfma_stream", "mfma_grid"):
+        full = pa.paged_attn_decode(*args, partition_size=64, path=path)
+        out = torch.zeros_like(full)
+        pa.paged_attn_decode(*args, out, partition_size=64, path=path, phase="partition")
+        pa.paged_attn_decode(*args, out, partition_size=64, path=path, phase="combine")
+        torch.cuda.synchronize()
+        assert torch.equal(out, full), path
