@@ -76,12 +76,12 @@ int pick_path(const pa_desc* d) {
 }
 
 // Ring depth / occupancy variant of the streaming kernel: PAGEDATTN_STREAM_VARIANT
-// (0, 1, 2; read once) for tuning sweeps, 0 otherwise.
+// (0 to 3; read once) for tuning sweeps, 0 otherwise.
 int stream_variant() {
   static int v = -1;
   if (v < 0) {
     const char* e = getenv("PAGEDATTN_STREAM_VARIANT");
-    v = (e && e[0] >= '0' && e[0] <= '2') ? e[0] - '0' : 0;
+    v = (e && e[0] >= '0' && e[0] <= '3') ? e[0] - '0' : 0;
   }
   return v;
 }

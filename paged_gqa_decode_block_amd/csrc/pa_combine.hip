@@ -18,21 +18,22 @@
 // read here too unless its link says it was written out, and an empty sequence
 // gets zeros.
 //
-// Grid (D / 64, H_q, B), 256 threads: thread (stripe s, quad u) owns dims
-// 4u .. 4u+3 of a 64-dim slice (float4 loads) and partitions p = s, s + 16, ....
-// Each thread folds its partitions with the same max-rescaling op, eight
+// Grid (D / 64, H_q, B), 16 x S threads: thread (stripe s, quad u) owns dims
+// 4u .. 4u+3 of a 64-dim slice (float4 loads) and partitions p = s, s + S, ....
+// Each thread folds its partitions with the same max-rescaling op, a batch of
 // partitions' loads in flight per round, so no pass over all maxima has to
-// finish first; the 16 stripes' states then meet in LDS.
+// finish first; the S stripes' states then meet in LDS. S is 16, or 64 (32
+// beyond 256) when there are more than 64 partitions, so one round usually
+// covers them all.
 #include "pa_kernels.h"
 
 namespace pa {
 namespace {
 
-constexpr int kStripes = 16;
-
-// kBatch: partitions per thread per round (1, 4 or 8, from the partition count).
-template <int kBatch>
-__global__ void __launch_bounds__(256) combine_kernel(Params p) {
+// kStripes: partition stripes (16, 32 or 64); kBatch: partitions per thread per
+// round (1, 4 or 8); both chosen from the partition count.
+template <int kStripes, int kBatch>
+__global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int tid = threadIdx.x;
   const int u = tid & 15, s = tid >> 4;
@@ -181,12 +182,14 @@ __global__ void __launch_bounds__(256) combine_kernel(Params p) {
 
 hipError_t launch_combine(const Params& p, hipStream_t s) {
   dim3 grid(p.D / 64, p.Hq, p.B);
-  if (p.pmax <= kStripes)
-    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, s, p);
-  else if (p.pmax <= 4 * kStripes)
-    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, s, p);
+  if (p.pmax <= 16)
+    hipLaunchKernelGGL((combine_kernel<16, 1>), grid, dim3(256), 0, s, p);
+  else if (p.pmax <= 64)
+    hipLaunchKernelGGL((combine_kernel<16, 4>), grid, dim3(256), 0, s, p);
+  else if (p.pmax <= 256)
+    hipLaunchKernelGGL((combine_kernel<64, 4>), grid, dim3(1024), 0, s, p);
+  else  // 512 threads: a batch of 8 needs more than the 128 registers of 1024-thread blocks
+    hipLaunchKernelGGL((combine_kernel<32, 8>), grid, dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

@@ -167,7 +167,7 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 // NBUF: ring slots (chunks in flight + 1), (NBUF - 1) * 2 * LPC <= 63 so the
 // vector-memory counter can track them all. OCC: waves per SIMD the register
 // allocation is held to. POL: cache policy of the K/V loads.
-template <typename T, int D, int NBUF, int OCC, int POL>
+template <typename T, int D, int NBUF, int OCC, int POL, bool QL>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 partition_stream_kernel(Params p) {
   typedef Mx<T> M;
@@ -177,7 +177,7 @@ partition_stream_kernel(Params p) {
   constexpr int LPC = C::LPC, KS = C::KS, MB = C::MB;
   static_assert((NBUF - 1) * 2 * LPC <= 63, "ring deeper than the vector-memory counter");
 
-  constexpr bool kQLds = D == 256;  // Q' fragments in LDS for d = 256, registers otherwise
+  constexpr bool kQLds = QL;  // Q' fragments in LDS (else in registers)
   __shared__ __attribute__((aligned(16))) uint16_t s_k[16 * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[16 * D];
   __shared__ __attribute__((aligned(16))) V8 s_q[kQLds ? 2 : 1][kQLds ? KS : 1][64];
@@ -530,22 +530,25 @@ partition_stream_kernel(Params p) {
   if (__ballot(bad_block) && lane == 0 && p.status) atomicOr(p.status, kStatusBadBlock);
 }
 
-// Ring depth / occupancy variants per head_dim (variant 0 is the default).
-// {NBUF, OCC} for head_dim 64, 128, 256.
-constexpr int kVariants[3][3][2] = {
-    {{6, 2}, {3, 2}, {3, 1}},   // 0
-    {{12, 1}, {6, 1}, {2, 1}},  // 1
-    {{4, 4}, {2, 3}, {4, 1}},   // 2
+// Ring depth / occupancy / Q' placement variants per head_dim (variant 0 is
+// the default): {NBUF, OCC, Q' in LDS} for head_dim 64, 128, 256.
+constexpr int kNumVariants = 4;
+constexpr int kVariants[kNumVariants][3][3] = {
+    {{6, 2, 0}, {3, 2, 0}, {3, 1, 1}},   // 0
+    {{12, 1, 0}, {6, 1, 0}, {2, 1, 1}},  // 1
+    {{4, 4, 0}, {2, 3, 0}, {4, 1, 1}},   // 2
+    {{8, 2, 1}, {4, 2, 1}, {3, 1, 1}},   // 3 (d = 256 at two waves per SIMD would spill)
 };
 constexpr int dim_index(int D) { return D == 64 ? 0 : D == 128 ? 1 : 2; }
 
 template <typename T, int D, int V, int POL>
 hipError_t launch_t(const Params& p, hipStream_t s) {
   constexpr int NBUF = kVariants[V][dim_index(D)][0], OCC = kVariants[V][dim_index(D)][1];
+  constexpr bool QL = kVariants[V][dim_index(D)][2] != 0;
   const int64_t bound = (int64_t)p.B * p.Hkv * (((int64_t)p.MBS << p.bs_log2) + 15) / 16;
   const int waves = stream_grid(D, V, p.cus, bound);
-  hipLaunchKernelGGL((partition_stream_kernel<T, D, NBUF, OCC, POL>), dim3(waves), dim3(64), 0, s,
-                     p);
+  hipLaunchKernelGGL((partition_stream_kernel<T, D, NBUF, OCC, POL, QL>), dim3(waves), dim3(64), 0,
+                     s, p);
   return hipGetLastError();
 }
 
@@ -555,6 +558,7 @@ hipError_t launch_v(const Params& p, int variant, hipStream_t s) {
   case DD:                                                          \
     if (variant == 1) return launch_t<T, DD, 1, POL>(p, s);         \
     if (variant == 2) return launch_t<T, DD, 2, POL>(p, s);         \
+    if (variant == 3) return launch_t<T, DD, 3, POL>(p, s);         \
     return launch_t<T, DD, 0, POL>(p, s);
   switch (p.D) {
     PA_STREAM_CASE(64)
@@ -577,7 +581,7 @@ bool stream_supports(int dtype, int D, int G, int block_size, int batch) {
 }
 
 int stream_grid(int D, int variant, int cus, int64_t chunk_bound) {
-  const int v = variant >= 0 && variant <= 2 ? variant : 0;
+  const int v = variant >= 0 && variant < kNumVariants ? variant : 0;
   const int occ = kVariants[v][dim_index(D)][1];
   return stream_active_waves(chunk_bound, 4 * occ * cus, cus);
 }
