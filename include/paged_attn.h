@@ -156,6 +156,37 @@ int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache,
                       size_t workspace_bytes, int32_t* status, void* stream);
 
 /*
+ * The decode step with the new token (page "Paged attention", decoding path:
+ * the kernel appends the step's keys and values to the paged cache in place):
+ * for every sequence b and KV head, writes k_new[b, h_kv, :] and
+ * v_new[b, h_kv, :] at token t = cache_seqlens[b], i.e. block
+ * block_table[b][t / block_size], offset t % block_size, then does what
+ * paged_attn_decode does over the cache_seqlens[b] + 1 tokens. cache_seqlens is
+ * read, not changed (the caller advances it), and block_table must already map
+ * the new token's block.
+ *
+ *   k_new, v_new   [B, H_kv, d], contiguous, the cache's element type, 16-byte
+ *                  aligned, device memory owned by the caller
+ *   k_cache,
+ *   v_cache        written at the new token's slot only
+ *   other arguments as for paged_attn_decode
+ *
+ * Three kernels are enqueued on `stream` (append, partition, combine); nothing
+ * is allocated and no memset is issued, so the call can be captured in a HIP
+ * graph and replayed with the tensors' contents updated in place between
+ * replays. A new token beyond max_blocks_per_seq * block_size, or whose table
+ * entry is outside [0, NB), is not written; the status word gets
+ * PA_STATUS_BAD_SEQLEN or PA_STATUS_BAD_BLOCK (and the attention clamps or skips
+ * that token). Returns the codes of paged_attn_decode, and PA_E_NULL / PA_E_ALIGN
+ * for k_new or v_new.
+ */
+int paged_attn_decode_append(const pa_desc* desc, const float* q, const void* k_new,
+                             const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* block_table, const int32_t* cache_seqlens, float scale,
+                             float* out, void* workspace, size_t workspace_bytes, int32_t* status,
+                             void* stream);
+
+/*
  * The two phases of paged_attn_decode, callable separately (same arguments and
  * rules). paged_attn_partition_phase runs the partition kernel: every
  * (sequence, KV head, partition) folds its tokens into a running softmax state

@@ -11,7 +11,8 @@ from __future__ import annotations
 
 from ._lib import (  # noqa: F401
     EXPORTED, LIB_PATH, PA_DTYPE, PA_FLAG_KV_SHARED, PA_PATH, PA_STATUS_BAD_BLOCK, PA_STATUS_BAD_SEQLEN, PATH_NAME,
-    PaDesc, PagedAttnError, check_inputs, decode_raw, load_library, make_desc, partition_size,
+    PaDesc, PagedAttnError, check_inputs, decode_append_raw, decode_raw, load_library, make_desc,
+    partition_size,
     resolved_path, strerror, validate, workspace_size,
 )
 
@@ -106,4 +107,46 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, ou
         status.data_ptr() if status is not None else 0, int(stream), phase)
     if rc != 0:
         raise PagedAttnError(rc, "paged_attn_decode: ")
+    return out
+
+
+def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, scale,
+                             out=None, *, layout="HND", partition_size=0, path="auto",
+                             workspace=None, status=None, stream=None, kv_shared=False):
+    """The decode step with the new token: writes ``k_new``/``v_new`` ([B, H_kv, d],
+    the cache's dtype) at token ``cache_seqlens[b]`` of each sequence's paged cache,
+    then attends ``cache_seqlens[b] + 1`` tokens. ``cache_seqlens`` is not changed.
+    No allocation happens when ``out`` and ``workspace`` are given (or the cached
+    workspace already exists), so the call can be captured in a CUDA/HIP graph."""
+    import torch
+
+    if not q.is_cuda:
+        raise ValueError("paged_attn_decode_append runs on the GPU; q is on the CPU")
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1] if layout == "HND" else k_cache.shape[2]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dtype != k_cache.dtype or tuple(t.shape) != (B, Hkv, D) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H_kv, d] tensor of the cache's dtype")
+    for name, t, dt in (("q", q, torch.float32), ("block_table", block_table, torch.int32),
+                        ("cache_seqlens", cache_seqlens, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    desc = desc_for(q, k_cache, v_cache, block_table, layout=layout,
+                    partition_size=partition_size, path=path, kv_shared=kv_shared)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = workspace_for(desc, q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = decode_append_raw(
+        desc, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), block_table.data_ptr(), cache_seqlens.data_ptr(), float(scale),
+        out.data_ptr(), workspace.data_ptr() if workspace is not None else 0,
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        status.data_ptr() if status is not None else 0, int(stream))
+    if rc != 0:
+        raise PagedAttnError(rc, "paged_attn_decode_append: ")
     return out

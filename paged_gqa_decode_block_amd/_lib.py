@@ -28,7 +28,8 @@ PA_STATUS_BAD_BLOCK = 1
 PA_STATUS_BAD_SEQLEN = 2
 
 EXPORTED = (
-    "paged_attn_decode", "paged_attn_partition_phase", "paged_attn_combine_phase",
+    "paged_attn_decode", "paged_attn_decode_append", "paged_attn_partition_phase",
+    "paged_attn_combine_phase",
     "paged_attn_workspace_size", "paged_attn_validate", "paged_attn_partition_size", "paged_attn_resolved_path", "paged_attn_check_inputs",
     "paged_attn_strerror", "paged_attn_abi_version",
 )
@@ -82,6 +83,9 @@ def load_library(path: str = LIB_PATH):
     dp = ctypes.POINTER(PaDesc)
     lib.paged_attn_decode.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp, vp]
     lib.paged_attn_decode.restype = i32
+    lib.paged_attn_decode_append.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
+                                             sz, vp, vp]
+    lib.paged_attn_decode_append.restype = i32
     lib.paged_attn_partition_phase.argtypes = lib.paged_attn_decode.argtypes
     lib.paged_attn_partition_phase.restype = i32
     lib.paged_attn_combine_phase.argtypes = [dp, vp, vp, vp, sz, vp]
@@ -127,6 +131,15 @@ def validate(desc: PaDesc) -> int:
 
 def workspace_size(desc: PaDesc) -> int:
     return int(load_library().paged_attn_workspace_size(ctypes.byref(desc)))
+
+
+def decode_append_raw(desc: PaDesc, q_ptr: int, knew_ptr: int, vnew_ptr: int, k_ptr: int, v_ptr: int,
+                      table_ptr: int, seqlens_ptr: int, scale: float, out_ptr: int, ws_ptr: int,
+                      ws_bytes: int, status_ptr: int, stream: int) -> int:
+    """Direct call of paged_attn_decode_append with integer device addresses."""
+    return int(load_library().paged_attn_decode_append(
+        ctypes.byref(desc), q_ptr, knew_ptr, vnew_ptr, k_ptr, v_ptr, table_ptr, seqlens_ptr,
+        ctypes.c_float(scale), out_ptr, ws_ptr, ws_bytes, status_ptr, stream))
 
 
 def partition_size(desc: PaDesc) -> int:

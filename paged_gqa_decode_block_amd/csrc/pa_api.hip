@@ -345,6 +345,26 @@ int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache, 
   return run_combine(p, (hipStream_t)stream);
 }
 
+int paged_attn_decode_append(const pa_desc* desc, const float* q, const void* k_new,
+                             const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* block_table, const int32_t* cache_seqlens, float scale,
+                             float* out, void* workspace, size_t workspace_bytes, int32_t* status,
+                             void* stream) {
+  pa::Params p;
+  int rc = prepare(desc, q, k_cache, v_cache, block_table, cache_seqlens, scale, out, workspace,
+                   workspace_bytes, status, true, p);
+  if (rc != PA_OK || p.B == 0) return rc;
+  if (!k_new || !v_new) return PA_E_NULL;
+  if (((uintptr_t)k_new | (uintptr_t)v_new) & 15) return PA_E_ALIGN;
+  p.len_add = 1;  // the new token is attended too
+  const hipStream_t s = (hipStream_t)stream;
+  if (pa::launch_append(p, k_new, v_new, elem_bytes(desc->kv_dtype), s) != hipSuccess)
+    return PA_E_LAUNCH;
+  rc = run_partition(desc, p, s);
+  if (rc != PA_OK) return rc;
+  return run_combine(p, s);
+}
+
 int paged_attn_partition_phase(const pa_desc* desc, const float* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,
                                const int32_t* cache_seqlens, float scale, float* out,

@@ -37,6 +37,7 @@ struct Params {
   int pmax;                 // ceil(MBS * bs / part)
   float qscale;             // scale * log2(e): scores are kept in base-2 units
   int cus;                  // compute units of the device (streaming kernel)
+  int len_add;              // tokens attended = cache_seqlens[b] + len_add (1 after an append)
   int nwaves;               // continuation slots in the workspace (streaming kernel)
 };
 
@@ -46,6 +47,10 @@ enum { kStatusBadBlock = 1, kStatusBadSeqlen = 2 };
 hipError_t launch_partition_valu(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_partition_mfma(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_combine(const Params& p, hipStream_t s);
+// Write each sequence's new K and V rows ([B, H_kv, d], the cache's element
+// type) at token cache_seqlens[b] of its paged cache.
+hipError_t launch_append(const Params& p, const void* k_new, const void* v_new, int elem_bytes,
+                         hipStream_t s);
 // Persistent streaming MFMA kernel on a device with p.cus compute units;
 // `variant` picks a ring depth / occupancy pair (0 = default), `nt` the
 // non-temporal cache policy for K/V loads.
@@ -77,7 +82,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 // Cache length of sequence b, clamped to [0, MBS * bs] (a bad value is reported).
 __device__ __forceinline__ int clamped_len(const Params& p, int b, bool report) {
-  int L = p.seqlens[b];
+  int L = p.seqlens[b] + p.len_add;
   const int lmax = p.MBS << p.bs_log2;
   if (L < 0 || L > lmax) {
     if (report && p.status) atomicOr(p.status, kStatusBadSeqlen);

@@ -196,3 +196,16 @@ def test_flags_field():
     d = _desc()
     d.reserved = 1
     assert pa.validate(d) == -2
+
+
+def test_decode_append_argument_errors():
+    d = _desc()
+    good = 1 << 20  # never dereferenced: every call below fails before any launch
+    args = dict(q_ptr=good, knew_ptr=good, vnew_ptr=good, k_ptr=good, v_ptr=good, table_ptr=good,
+                seqlens_ptr=good, scale=1.0, out_ptr=good, ws_ptr=good,
+                ws_bytes=pa.workspace_size(d), status_ptr=0, stream=0)
+    assert pa.decode_append_raw(_desc(head_dim=100), **args) == -3
+    assert pa.decode_append_raw(d, **{**args, "knew_ptr": 0}) == -1
+    assert pa.decode_append_raw(d, **{**args, "vnew_ptr": 0}) == -1
+    assert pa.decode_append_raw(d, **{**args, "vnew_ptr": good + 8}) == -7
+    assert pa.decode_append_raw(_desc(batch=0), **{**args, "knew_ptr": 0}) == 0  # nothing to do

@@ -310,3 +310,128 @@ def test_partition_then_combine_phase_equals_decode(torch_cuda):
         pa.paged_attn_decode(*args, out, partition_size=64, path=path, phase="combine")
         torch.cuda.synchronize()
         assert torch.equal(out, full), path
+
+
+# --- the decode step with the new token (append in place), and graph replay -----
+
+def _append_case(rng, *, kv_dtype="bf16", layout="HND", L0=(100, 31, 200), steps=4, B=3, Hq=8,
+                 Hkv=2, D=128, bs=16):
+    """A paged case whose tables already map `steps` more tokens per sequence; the
+    slots of those future tokens hold NaN until an append writes them."""
+    final = [int(x) + steps for x in L0]
+    case, _, _ = paged_case(rng, B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, kv_dtype=kv_dtype, seqlens=final,
+                            layout=layout)
+    nan = np.float32(np.nan) if kv_dtype == "f32" else np.uint16(0x7FC0 if kv_dtype == "bf16" else 0x7E00)
+    for b in range(B):
+        for t in range(L0[b], final[b]):
+            _slot(case, b, t)[0][...] = nan
+            _slot(case, b, t)[1][...] = nan
+    return W.Case(**{**case.__dict__, "seqlens": np.asarray(L0, dtype=np.int32)})
+
+
+def _slot(case, b, t):
+    """Views of token t of sequence b in the host K and V stores ([H_kv, d])."""
+    blk = 1 + case.block_table[b, t // case.bs]
+    off = t % case.bs
+    if case.layout == "HND":
+        return case.k_store[blk, :, off, :], case.v_store[blk, :, off, :]
+    return case.k_store[blk, off, :, :], case.v_store[blk, off, :, :]
+
+
+def _new_token(torch, rng, case):
+    """Step inputs: q (float32) and k_new / v_new in the cache's storage type, on
+    host and device."""
+    q = rng.standard_normal((case.B, case.Hq, case.D)).astype(np.float32)
+    kn = W.to_storage(rng.standard_normal((case.B, case.Hkv, case.D)).astype(np.float32), case.kv_dtype)
+    vn = W.to_storage(rng.standard_normal((case.B, case.Hkv, case.D)).astype(np.float32), case.kv_dtype)
+
+    def dev(a):
+        if case.kv_dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+        return t.view(torch.bfloat16 if case.kv_dtype == "bf16" else torch.float16).to("cuda")
+
+    return q, kn, vn, torch.from_numpy(q).to("cuda"), dev(kn), dev(vn)
+
+
+def _append_host(case, q, kn, vn):
+    """The host-side step: write the new token, return the case to attend (L + 1)."""
+    for b in range(case.B):
+        ks, vs = _slot(case, b, int(case.seqlens[b]))
+        ks[...] = kn[b]
+        vs[...] = vn[b]
+    return W.Case(**{**case.__dict__, "q": q, "seqlens": case.seqlens + 1})
+
+
+@pytest.mark.parametrize("kv_dtype,layout", [("bf16", "HND"), ("f16", "NHD"), ("f32", "HND")])
+def test_decode_append_matches_oracle(torch_cuda, kv_dtype, layout):
+    """Two decode steps, each appending the new token in place and attending it:
+    every kernel path against the oracle on the updated cache, and the cache slot
+    holds exactly the appended rows (NaN poison in the future slots would show a
+    read before the write)."""
+    torch = torch_cuda
+    for path in paths_for(_append_case(np.random.default_rng(0), kv_dtype=kv_dtype, layout=layout)):
+        rng = np.random.default_rng(95)
+        case = _append_case(rng, kv_dtype=kv_dtype, layout=layout)
+        dev = to_device(torch, case)
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for step in range(2):
+            q, kn, vn, qd, knd, vnd = _new_token(torch, rng, case)
+            ref = _append_host(case, q, kn, vn)
+            want = run_oracle(ref)
+            got = pa.paged_attn_decode_append(qd, knd, vnd, dev["k"], dev["v"], dev["table"],
+                                              dev["seqlens"], case.scale, layout=layout,
+                                              partition_size=64, path=path, status=status)
+            torch.cuda.synchronize()
+            got = got.cpu().numpy().astype(np.float64)
+            assert np.isfinite(got).all(), (path, step)
+            assert np.abs(got - want).max() <= TOL[kv_dtype], (path, step)
+            pool_k = dev["k"].cpu().numpy() if kv_dtype == "f32" else dev["k"].cpu().view(torch.int16).numpy().view(np.uint16)
+            for b in range(case.B):
+                t = int(case.seqlens[b])
+                blk, off = case.block_table[b, t // case.bs], t % case.bs
+                row = pool_k[blk, :, off, :] if layout == "HND" else pool_k[blk, off, :, :]
+                assert np.array_equal(row.view(np.uint8), np.ascontiguousarray(kn[b]).view(np.uint8))
+            dev["seqlens"] += 1
+            case = W.Case(**{**ref.__dict__, "seqlens": ref.seqlens})
+        assert int(status.item()) == 0, path
+
+
+def test_decode_append_graph_replay(torch_cuda):
+    """The append + decode step captured once in a HIP graph and replayed for four
+    decode steps: inputs are updated in place between replays (new q and K/V rows
+    copied in, cache lengths advanced by eager work), and every replay matches the
+    oracle on the cache as it then stands."""
+    torch = torch_cuda
+    rng = np.random.default_rng(96)
+    case = _append_case(rng, steps=4)
+    dev = to_device(torch, case)
+    q_s = torch.zeros(case.B, case.Hq, case.D, dtype=torch.float32, device="cuda")
+    kn_s = torch.zeros(case.B, case.Hkv, case.D, dtype=torch.bfloat16, device="cuda")
+    vn_s = torch.zeros_like(kn_s)
+    out_s = torch.zeros_like(q_s)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    args = (dev["k"], dev["v"], dev["table"], dev["seqlens"], case.scale)
+    # a plain decode first: creates the cached workspace outside the capture
+    pa.paged_attn_decode(q_s, *args, out_s, partition_size=64)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.paged_attn_decode_append(q_s, kn_s, vn_s, *args, out_s, partition_size=64, status=status)
+    torch.cuda.synchronize()
+    for step in range(4):
+        q, kn, vn, qd, knd, vnd = _new_token(torch, rng, case)
+        q_s.copy_(qd)
+        kn_s.copy_(knd)
+        vn_s.copy_(vnd)
+        ref = _append_host(case, q, kn, vn)
+        want = run_oracle(ref)
+        g.replay()
+        torch.cuda.synchronize()
+        got = out_s.cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all(), step
+        assert np.abs(got - want).max() <= 3e-3, step
+        dev["seqlens"] += 1   # eager work between replays
+        torch.cuda.synchronize()
+        case = W.Case(**{**ref.__dict__, "seqlens": ref.seqlens})
+    assert int(status.item()) == 0
