@@ -171,6 +171,48 @@ def measure(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
     }
 
 
+def measure_append_graph(wl: Workload, steps: int) -> dict:
+    """The decode step with the new token (paged_attn_decode_append: append kernel,
+    partition, combine), captured once in a HIP graph and replayed. Each replay
+    appends every sequence's last cached token over itself (cache lengths minus
+    one, K/V rows gathered from the cache) and attends the same L tokens, so the
+    KV bytes and the output equal the plain step's."""
+    import paged_gqa_decode_block_amd as pa
+
+    torch = wl.torch
+    c = wl.case
+    L = wl.seqlens.long()
+    Lm1 = (wl.seqlens - 1).clamp(min=0).contiguous()
+    t = (L - 1).clamp(min=0)
+    blk = wl.table.long().gather(1, (t // c.bs).unsqueeze(1)).squeeze(1).clamp(min=0)
+    off = t % c.bs
+    if c.layout == "HND":
+        kn, vn = wl.k_pool[blk, :, off, :], wl.v_pool[blk, :, off, :]
+    else:
+        kn, vn = wl.k_pool[blk, off, :, :], wl.v_pool[blk, off, :, :]
+    kn, vn = kn.contiguous(), vn.contiguous()
+    out = torch.empty_like(wl.q)
+
+    def step():
+        pa.paged_attn_decode_append(wl.q, kn, vn, wl.k_pool, wl.v_pool, wl.table, Lm1, c.scale, out,
+                                    layout=c.layout, partition_size=wl.part, path=wl.path,
+                                    workspace=wl.ws, kv_shared=wl.kv_shared)
+
+    step()
+    wl.call()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, wl.out))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        g.replay()
+    ms = time_steps(torch, g.replay, steps)
+    return {"append_graph_step_us": float(ms * 1e3),
+            "append_graph_kv_gbs": wl.kv_bytes / (ms / 1e3) / 1e9,
+            "append_output_equals_decode": same}
+
+
 def roofline(wl: Workload, r: dict) -> dict:
     achieved = wl.kv_bytes / (r["partition_kernel_us"] / 1e6) / 1e9
     out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -278,6 +320,9 @@ def main():
 
     flush_buf = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > 256 MB MALL
     r = measure(wl, a.steps, a.warmup, flush_buf)
+    r.update(measure_append_graph(wl, a.steps))
+    log(f"[bench] {wl.case.name}: append + decode step as a graph replay "
+        f"{r['append_graph_step_us']:.1f} us (output equals the plain step: {r['append_output_equals_decode']})")
     log(f"[bench] {wl.case.name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['kv_gbs']:.0f} GB/s")
     rl = roofline(wl, r)
     also = {}
