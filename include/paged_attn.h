@@ -84,6 +84,8 @@ typedef enum pa_path {
 #define PA_E_TABLE (-12)      /* (check_inputs) an entry read for an attended token  */
                               /* is outside [0, num_blocks)                           */
 #define PA_E_SEQLEN (-13)     /* (check_inputs) a cache length < 0 or > MBS * bs     */
+#define PA_E_NOMEM (-14)      /* (block manager) not enough free blocks              */
+#define PA_E_SEQ (-15)        /* (block manager) unknown sequence, index or length   */
 
 /* pa_desc.flags bits. */
 #define PA_FLAG_KV_SHARED 1  /* physical blocks may be listed by several sequences   */

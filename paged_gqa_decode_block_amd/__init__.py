@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     resolved_path, strerror, validate, workspace_size,
 )
 
+from .block_manager import BlockManager, copy_blocks  # noqa: E402,F401
+
 _TORCH_DTYPE_NAME = {"torch.float32": "f32", "torch.float16": "f16", "torch.bfloat16": "bf16"}
 _ws_cache: dict = {}
 

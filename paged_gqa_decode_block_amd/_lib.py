@@ -32,6 +32,11 @@ EXPORTED = (
     "paged_attn_combine_phase",
     "paged_attn_workspace_size", "paged_attn_validate", "paged_attn_partition_size", "paged_attn_resolved_path", "paged_attn_check_inputs",
     "paged_attn_strerror", "paged_attn_abi_version",
+    # include/paged_block_manager.h
+    "paged_attn_bm_create", "paged_attn_bm_destroy", "paged_attn_bm_allocate_blocks",
+    "paged_attn_bm_free_sequence", "paged_attn_bm_share_prefix", "paged_attn_bm_cow_block",
+    "paged_attn_bm_append_slot", "paged_attn_bm_num_free", "paged_attn_bm_ref_count",
+    "paged_attn_bm_sequence_blocks", "paged_attn_bm_block_table", "paged_attn_copy_blocks",
 )
 
 
@@ -104,6 +109,26 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_strerror.restype = ctypes.c_char_p
     lib.paged_attn_abi_version.argtypes = []
     lib.paged_attn_abi_version.restype = i32
+    i64, ip = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
+    lib.paged_attn_bm_create.argtypes = [i32, i32]
+    lib.paged_attn_bm_create.restype = vp
+    lib.paged_attn_bm_destroy.argtypes = [vp]
+    lib.paged_attn_bm_destroy.restype = None
+    lib.paged_attn_bm_allocate_blocks.argtypes = [vp, i64, i32]
+    lib.paged_attn_bm_free_sequence.argtypes = [vp, i64]
+    lib.paged_attn_bm_share_prefix.argtypes = [vp, i64, i64, i32]
+    lib.paged_attn_bm_cow_block.argtypes = [vp, i64, i32, ip, ip]
+    lib.paged_attn_bm_append_slot.argtypes = [vp, i64, i32, ip, ip]
+    lib.paged_attn_bm_num_free.argtypes = [vp]
+    lib.paged_attn_bm_ref_count.argtypes = [vp, i32]
+    lib.paged_attn_bm_sequence_blocks.argtypes = [vp, i64, ip, i32]
+    lib.paged_attn_bm_block_table.argtypes = [vp, ctypes.POINTER(ctypes.c_int64), i32, i32, ip]
+    lib.paged_attn_copy_blocks.argtypes = [dp, vp, vp, vp, i32, vp, vp]
+    for name in ("paged_attn_bm_allocate_blocks", "paged_attn_bm_free_sequence",
+                 "paged_attn_bm_share_prefix", "paged_attn_bm_cow_block", "paged_attn_bm_append_slot",
+                 "paged_attn_bm_num_free", "paged_attn_bm_ref_count", "paged_attn_bm_sequence_blocks",
+                 "paged_attn_bm_block_table", "paged_attn_copy_blocks"):
+        getattr(lib, name).restype = i32
     _lib = lib
     return lib
 

@@ -238,6 +238,8 @@ const char* paged_attn_strerror(int status) {
     case PA_E_LAUNCH: return "the HIP runtime refused a kernel launch";
     case PA_E_TABLE: return "a block_table entry for an attended token is outside [0, num_blocks)";
     case PA_E_SEQLEN: return "a cache length is negative or beyond max_blocks_per_seq * block_size";
+    case PA_E_NOMEM: return "not enough free blocks in the block manager";
+    case PA_E_SEQ: return "unknown sequence, or a block index or length outside it";
   }
   return "unknown status";
 }

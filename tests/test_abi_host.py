@@ -17,9 +17,14 @@ HEADER = os.path.join(ROOT, "include", "paged_attn.h")
 
 
 def _header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(paged_attn_\w+)\s*\(", text)))
+    """Every function declared in include/*.h."""
+    names = set()
+    for h in sorted(os.listdir(os.path.dirname(HEADER))):
+        if h.endswith(".h"):
+            text = open(os.path.join(os.path.dirname(HEADER), h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(paged_attn_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_loads_and_exports_every_declared_symbol():

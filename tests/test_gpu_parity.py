@@ -435,3 +435,53 @@ def test_decode_append_graph_replay(torch_cuda):
         torch.cuda.synchronize()
         case = W.Case(**{**ref.__dict__, "seqlens": ref.seqlens})
     assert int(status.item()) == 0
+
+
+# --- the block manager's copy-on-write on the device ---------------------------
+
+def test_copy_on_write_with_block_manager(torch_cuda):
+    """Two sequences share three blocks (the last one partly filled) through the
+    block manager and both append a different token at position 40. The first
+    appender gets a fresh copy of the shared block (paged_attn_copy_blocks on the
+    device), the second then owns the original; each sequence attends its own
+    new token, against the oracle."""
+    torch = torch_cuda
+    rng = np.random.default_rng(97)
+    Hq, Hkv, D, bs, L, NB = 8, 2, 128, 16, 40, 8
+    bm = pa.BlockManager(NB, bs)
+    bm.allocate_blocks(0, 3)
+    bm.share_prefix(0, 1, 3)
+    k_store = np.full((NB + 1, Hkv, bs, D), 0x7FC0, dtype=np.uint16)   # bf16 NaN
+    v_store = k_store.copy()
+    kc = W.to_storage(rng.standard_normal((Hkv, L, D)).astype(np.float32), "bf16")
+    vc = W.to_storage(rng.standard_normal((Hkv, L, D)).astype(np.float32), "bf16")
+    for j, blk in enumerate(bm.sequence_blocks(0)):
+        lo, hi = j * bs, min(L, (j + 1) * bs)
+        k_store[1 + blk, :, : hi - lo, :] = kc[:, lo:hi, :]
+        v_store[1 + blk, :, : hi - lo, :] = vc[:, lo:hi, :]
+    kd = torch.from_numpy(k_store.view(np.int16)).view(torch.bfloat16).to("cuda")[1:]
+    vd = torch.from_numpy(v_store.view(np.int16)).view(torch.bfloat16).to("cuda")[1:]
+    pairs = [r for r in (bm.append_slot(0, L), bm.append_slot(1, L)) if r is not None]
+    assert len(pairs) == 1 and bm.sequence_blocks(1)[2] == pairs[0][0]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pa.copy_blocks(kd, vd, torch.tensor(pairs, dtype=torch.int32, device="cuda"), status=status)
+    for src, dst in pairs:  # the host mirror of the copy
+        k_store[1 + dst] = k_store[1 + src]
+        v_store[1 + dst] = v_store[1 + src]
+    table = bm.block_table([0, 1], 3)
+    case = W.Case(name="cow", kv_dtype="bf16", B=2, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, MBS=3,
+                  seqlens=np.array([L, L], dtype=np.int32), block_table=table,
+                  q=np.zeros((2, Hq, D), dtype=np.float32), k_store=k_store, v_store=v_store,
+                  scale=1.0 / np.sqrt(D))
+    q, kn, vn, qd, knd, vnd = _new_token(torch, rng, case)
+    ref = _append_host(case, q, kn, vn)
+    want = run_oracle(ref)
+    for path in ("mfma_stream", "mfma_grid", "valu"):
+        out = pa.paged_attn_decode_append(qd, knd, vnd, kd, vd, torch.from_numpy(table).to("cuda"),
+                                          torch.from_numpy(case.seqlens).to("cuda"), case.scale,
+                                          partition_size=32, path=path, status=status)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.abs(got - want).max() <= 3e-3, path
+    assert int(status.item()) == 0
+    assert np.abs(want[0] - want[1]).max() > 1e-3  # the two new tokens differ
