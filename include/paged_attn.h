@@ -92,6 +92,9 @@ typedef enum pa_path {
                              /* (prefix sharing): keep K/V loads cacheable so shared */
                              /* blocks are reused from cache; without it K/V are     */
                              /* streamed with non-temporal loads                     */
+#define PA_FLAG_QO_BF16 2    /* q and out are bf16 instead of fp32 (accumulation,     */
+                             /* partial states and the combine stay fp32; out is      */
+                             /* rounded to nearest even once, at the end)             */
 
 /* Bits the kernels OR into the optional device status word. */
 #define PA_STATUS_BAD_BLOCK 1   /* an attended token's table entry was outside [0, NB) */
@@ -131,7 +134,8 @@ typedef struct pa_desc {
  * the default stream). Returns once two kernels are enqueued; it never
  * synchronises the device.
  *
- *   q              float32 [B, H_q, d], contiguous, 16-byte aligned
+ *   q              float32 [B, H_q, d] (bf16 with PA_FLAG_QO_BF16), contiguous,
+ *                  16-byte aligned
  *   k_cache,
  *   v_cache        pools as described at pa_desc, 16-byte aligned
  *   block_table    int32 [B, max_blocks_per_seq], row-major. Only the entries
@@ -139,8 +143,8 @@ typedef struct pa_desc {
  *                  entry and must not appear in that range.
  *   cache_seqlens  int32 [B], L_b in [0, max_blocks_per_seq * block_size]
  *   scale          multiplies q . k before the softmax (usually 1/sqrt(d))
- *   out            float32 [B, H_q, d], contiguous, 16-byte aligned; L_b = 0
- *                  gives zeros
+ *   out            float32 [B, H_q, d] (bf16 with PA_FLAG_QO_BF16), contiguous,
+ *                  16-byte aligned; L_b = 0 gives zeros
  *   workspace      device memory of at least paged_attn_workspace_size(desc)
  *                  bytes (may be NULL when that size is 0), 256-byte aligned
  *   status         optional device int32; the kernels OR PA_STATUS_* bits into
@@ -152,9 +156,9 @@ typedef struct pa_desc {
  * synchronisation); use paged_attn_check_inputs on host copies to vet them.
  * Calls that share a workspace must be ordered on one stream.
  */
-int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache,
+int paged_attn_decode(const pa_desc* desc, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_table,
-                      const int32_t* cache_seqlens, float scale, float* out, void* workspace,
+                      const int32_t* cache_seqlens, float scale, void* out, void* workspace,
                       size_t workspace_bytes, int32_t* status, void* stream);
 
 /*
@@ -182,10 +186,10 @@ int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache,
  * that token). Returns the codes of paged_attn_decode, and PA_E_NULL / PA_E_ALIGN
  * for k_new or v_new.
  */
-int paged_attn_decode_append(const pa_desc* desc, const float* q, const void* k_new,
+int paged_attn_decode_append(const pa_desc* desc, const void* q, const void* k_new,
                              const void* v_new, void* k_cache, void* v_cache,
                              const int32_t* block_table, const int32_t* cache_seqlens, float scale,
-                             float* out, void* workspace, size_t workspace_bytes, int32_t* status,
+                             void* out, void* workspace, size_t workspace_bytes, int32_t* status,
                              void* stream);
 
 /*
@@ -202,12 +206,12 @@ int paged_attn_decode_append(const pa_desc* desc, const float* q, const void* k_
  * stream equals paged_attn_decode; the partition phase alone completes out only
  * when paged_attn_workspace_size() is 0. The combine phase is a no-op then.
  */
-int paged_attn_partition_phase(const pa_desc* desc, const float* q, const void* k_cache,
+int paged_attn_partition_phase(const pa_desc* desc, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,
-                               const int32_t* cache_seqlens, float scale, float* out,
+                               const int32_t* cache_seqlens, float scale, void* out,
                                void* workspace, size_t workspace_bytes, int32_t* status,
                                void* stream);
-int paged_attn_combine_phase(const pa_desc* desc, const int32_t* cache_seqlens, float* out,
+int paged_attn_combine_phase(const pa_desc* desc, const int32_t* cache_seqlens, void* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace paged_attn_decode needs for this descriptor on the

@@ -10,7 +10,8 @@ call. Build the library with ``python -m paged_gqa_decode_block_amd.build``.
 from __future__ import annotations
 
 from ._lib import (  # noqa: F401
-    EXPORTED, LIB_PATH, PA_DTYPE, PA_FLAG_KV_SHARED, PA_PATH, PA_STATUS_BAD_BLOCK, PA_STATUS_BAD_SEQLEN, PATH_NAME,
+    EXPORTED, LIB_PATH, PA_DTYPE, PA_FLAG_KV_SHARED, PA_FLAG_QO_BF16, PA_PATH, PA_STATUS_BAD_BLOCK,
+    PA_STATUS_BAD_SEQLEN, PATH_NAME,
     PaDesc, PagedAttnError, check_inputs, decode_append_raw, decode_raw, load_library, make_desc,
     partition_size,
     resolved_path, strerror, validate, workspace_size,
@@ -52,7 +53,21 @@ def desc_for(q, k_cache, v_cache, block_table, *, layout="HND", partition_size=0
     return make_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
                      num_blocks=NB, max_blocks_per_seq=block_table.shape[1],
                      kv_dtype=_kv_dtype(k_cache), k_strides=ks, v_strides=vs,
-                     partition_size=partition_size, path=path, kv_shared=kv_shared)
+                     partition_size=partition_size, path=path, kv_shared=kv_shared,
+                     qo_bf16=str(q.dtype) == "torch.bfloat16")
+
+
+def _check_q_tables(torch, q, block_table, cache_seqlens):
+    if q.dtype not in (torch.float32, torch.bfloat16) or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float32 or bfloat16 tensor")
+    for name, t in (("block_table", block_table), ("cache_seqlens", cache_seqlens)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+
+
+def _check_out(q, out):
+    if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape and dtype")
 
 
 def workspace_for(desc: PaDesc, device):
@@ -73,9 +88,10 @@ def workspace_for(desc: PaDesc, device):
 def paged_attn_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, out=None, *,
                       layout="HND", partition_size=0, path="auto", workspace=None, status=None,
                       stream=None, phase="both", kv_shared=False):
-    """Single-query paged GQA attention; returns ``out`` (float32 [B, H_q, d]).
+    """Single-query paged GQA attention; returns ``out`` ([B, H_q, d], q's dtype).
 
-    q float32 [B, H_q, d]; block_table int32 [B, MBS]; cache_seqlens int32 [B];
+    q float32 or bfloat16 [B, H_q, d] (out has the same dtype; accumulation is
+    fp32 either way); block_table int32 [B, MBS]; cache_seqlens int32 [B];
     all on one GPU. Enqueued on ``stream`` (default: torch's current stream).
     ``status`` is an optional int32 device tensor the kernels OR error bits into.
     ``phase`` "partition" or "combine" runs one of the two kernels alone (the
@@ -87,14 +103,12 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, ou
 
     if not q.is_cuda:
         raise ValueError("paged_attn_decode runs on the GPU; q is on the CPU")
-    for name, t, dt in (("q", q, torch.float32), ("block_table", block_table, torch.int32),
-                        ("cache_seqlens", cache_seqlens, torch.int32)):
-        if t.dtype != dt or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    _check_q_tables(torch, q, block_table, cache_seqlens)
     desc = desc_for(q, k_cache, v_cache, block_table, layout=layout,
                     partition_size=partition_size, path=path, kv_shared=kv_shared)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(q, out)
     if workspace is None:
         workspace = workspace_for(desc, q.device)
     if stream is None:
@@ -129,14 +143,12 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cac
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         if t.dtype != k_cache.dtype or tuple(t.shape) != (B, Hkv, D) or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [B, H_kv, d] tensor of the cache's dtype")
-    for name, t, dt in (("q", q, torch.float32), ("block_table", block_table, torch.int32),
-                        ("cache_seqlens", cache_seqlens, torch.int32)):
-        if t.dtype != dt or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    _check_q_tables(torch, q, block_table, cache_seqlens)
     desc = desc_for(q, k_cache, v_cache, block_table, layout=layout,
                     partition_size=partition_size, path=path, kv_shared=kv_shared)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(q, out)
     if workspace is None:
         workspace = workspace_for(desc, q.device)
     if stream is None:

@@ -141,7 +141,7 @@ int validate(const pa_desc* d) {
     if (st[i] <= 0 || (st[i] * eb) % 16) return PA_E_STRIDE;
   if (d->k_stride_token < d->head_dim || d->v_stride_token < d->head_dim) return PA_E_STRIDE;
   if (d->path < PA_PATH_AUTO || d->path > PA_PATH_MFMA_STREAM) return PA_E_PATH;
-  if ((d->flags & ~PA_FLAG_KV_SHARED) || d->reserved) return PA_E_SHAPE;
+  if ((d->flags & ~(PA_FLAG_KV_SHARED | PA_FLAG_QO_BF16)) || d->reserved) return PA_E_SHAPE;
   if (d->partition_size != 0) {
     const int ps = d->partition_size;
     if (ps < 32 || ps > 16384 || ps % 32) return PA_E_PARTITION;
@@ -250,8 +250,8 @@ namespace {
 
 // Shared argument checks and parameter set-up of the decode entry points.
 // Returns PA_OK and fills p, or an error code.
-int prepare(const pa_desc* desc, const float* q, const void* k_cache, const void* v_cache,
-            const int32_t* block_table, const int32_t* cache_seqlens, float scale, float* out,
+int prepare(const pa_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+            const int32_t* block_table, const int32_t* cache_seqlens, float scale, void* out,
             void* workspace, size_t workspace_bytes, int32_t* status, bool need_inputs,
             pa::Params& p) {
   int rc = validate(desc);
@@ -291,6 +291,7 @@ int prepare(const pa_desc* desc, const float* q, const void* k_cache, const void
   p.pmax = (int)((max_tokens(desc) + part - 1) / part);
   p.qscale = scale * 1.4426950408889634f;  // log2(e): scores in base-2 units
   p.cus = cu_count();
+  p.qo_bf16 = (desc->flags & PA_FLAG_QO_BF16) ? 1 : 0;
   if (need > 0) {
     size_t off[kWsParts + 1];
     workspace_layout(desc, off);
@@ -334,9 +335,9 @@ int run_combine(const pa::Params& p, hipStream_t s) {
 
 extern "C" {
 
-int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache, const void* v_cache,
+int paged_attn_decode(const pa_desc* desc, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_table, const int32_t* cache_seqlens, float scale,
-                      float* out, void* workspace, size_t workspace_bytes, int32_t* status,
+                      void* out, void* workspace, size_t workspace_bytes, int32_t* status,
                       void* stream) {
   pa::Params p;
   int rc = prepare(desc, q, k_cache, v_cache, block_table, cache_seqlens, scale, out, workspace,
@@ -347,10 +348,10 @@ int paged_attn_decode(const pa_desc* desc, const float* q, const void* k_cache, 
   return run_combine(p, (hipStream_t)stream);
 }
 
-int paged_attn_decode_append(const pa_desc* desc, const float* q, const void* k_new,
+int paged_attn_decode_append(const pa_desc* desc, const void* q, const void* k_new,
                              const void* v_new, void* k_cache, void* v_cache,
                              const int32_t* block_table, const int32_t* cache_seqlens, float scale,
-                             float* out, void* workspace, size_t workspace_bytes, int32_t* status,
+                             void* out, void* workspace, size_t workspace_bytes, int32_t* status,
                              void* stream) {
   pa::Params p;
   int rc = prepare(desc, q, k_cache, v_cache, block_table, cache_seqlens, scale, out, workspace,
@@ -367,9 +368,9 @@ int paged_attn_decode_append(const pa_desc* desc, const float* q, const void* k_
   return run_combine(p, s);
 }
 
-int paged_attn_partition_phase(const pa_desc* desc, const float* q, const void* k_cache,
+int paged_attn_partition_phase(const pa_desc* desc, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,
-                               const int32_t* cache_seqlens, float scale, float* out,
+                               const int32_t* cache_seqlens, float scale, void* out,
                                void* workspace, size_t workspace_bytes, int32_t* status,
                                void* stream) {
   pa::Params p;
@@ -379,7 +380,7 @@ int paged_attn_partition_phase(const pa_desc* desc, const float* q, const void* 
   return run_partition(desc, p, (hipStream_t)stream);
 }
 
-int paged_attn_combine_phase(const pa_desc* desc, const int32_t* cache_seqlens, float* out,
+int paged_attn_combine_phase(const pa_desc* desc, const int32_t* cache_seqlens, void* out,
                              void* workspace, size_t workspace_bytes, void* stream) {
   pa::Params p;
   const int rc = prepare(desc, nullptr, nullptr, nullptr, nullptr, cache_seqlens, 1.f, out,

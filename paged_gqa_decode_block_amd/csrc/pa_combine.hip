@@ -173,8 +173,8 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
       num.w += w * s_a[k][tid].w;
     }
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    *(float4*)(p.out + ((int64_t)b * p.Hq + h) * p.D + d) =
-        make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+    store_out4(p, ((int64_t)b * p.Hq + h) * p.D + d, num.x * inv, num.y * inv, num.z * inv,
+               num.w * inv);
   }
 }
 

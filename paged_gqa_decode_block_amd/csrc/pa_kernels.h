@@ -12,12 +12,12 @@ namespace pa {
 constexpr int kTableCap = 1024;
 
 struct Params {
-  const float* q;           // [B, Hq, D]
+  const void* q;            // [B, Hq, D] fp32, or bf16 when qo_bf16
   const void* k;            // pool, element strides below
   const void* v;
   const int32_t* table;     // [B, MBS]
   const int32_t* seqlens;   // [B]
-  float* out;               // [B, Hq, D]
+  void* out;                // [B, Hq, D] fp32, or bf16 when qo_bf16
   float* ws_m;              // [B, Hq, pmax]  running max, base-2 units
   float* ws_l;              // [B, Hq, pmax]  sum of 2^(s - m)
   float* ws_acc;            // [B, Hq, pmax, D] unnormalised output
@@ -38,6 +38,7 @@ struct Params {
   float qscale;             // scale * log2(e): scores are kept in base-2 units
   int cus;                  // compute units of the device (streaming kernel)
   int len_add;              // tokens attended = cache_seqlens[b] + len_add (1 after an append)
+  int qo_bf16;              // q and out are bf16 (else fp32)
   int nwaves;               // continuation slots in the workspace (streaming kernel)
 };
 
@@ -89,6 +90,39 @@ __device__ __forceinline__ int clamped_len(const Params& p, int b, bool report) 
     L = L < 0 ? 0 : lmax;
   }
   return L;
+}
+
+// q and out in fp32 or bf16 (p.qo_bf16, uniform). bf16 -> fp32 is exact;
+// fp32 -> bf16 rounds to nearest even and keeps NaN a NaN.
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+// q elements idx .. idx + 3 (idx a multiple of 4) as floats.
+__device__ __forceinline__ float4 load_q4(const Params& p, int64_t idx) {
+  if (p.qo_bf16) {
+    const uint2 u = *(const uint2*)((const uint16_t*)p.q + idx);
+    return make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16),
+                       bf16_to_f32(u.y & 0xffffu), bf16_to_f32(u.y >> 16));
+  }
+  return *(const float4*)((const float*)p.q + idx);
+}
+// out elements idx .. idx + 3 (idx a multiple of 4), and a single element.
+__device__ __forceinline__ void store_out4(const Params& p, int64_t idx, float a, float b, float c,
+                                           float d) {
+  if (p.qo_bf16)
+    *(uint2*)((uint16_t*)p.out + idx) =
+        make_uint2(f32_to_bf16(a) | (f32_to_bf16(b) << 16), f32_to_bf16(c) | (f32_to_bf16(d) << 16));
+  else
+    *(float4*)((float*)p.out + idx) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store_out1(const Params& p, int64_t idx, float v) {
+  if (p.qo_bf16)
+    ((uint16_t*)p.out)[idx] = (uint16_t)f32_to_bf16(v);
+  else
+    ((float*)p.out)[idx] = v;
 }
 
 // Stage the physical ids of blocks [j0, j1] of sequence b in LDS; an id outside

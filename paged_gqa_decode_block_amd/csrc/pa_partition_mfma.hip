@@ -106,7 +106,7 @@ partition_mfma_kernel(Params p) {
     if (part == 0) {  // empty context: zeros
       for (int i = lane; i < G * D / 4; i += 64) {
         const int g = i / (D / 4), c4 = i % (D / 4);
-        *(float4*)(p.out + ((int64_t)b * p.Hq + hk * G + g) * D + 4 * c4) = make_float4(0, 0, 0, 0);
+        store_out4(p, ((int64_t)b * p.Hq + hk * G + g) * D + 4 * c4, 0.f, 0.f, 0.f, 0.f);
       }
     }
     return;
@@ -125,11 +125,11 @@ partition_mfma_kernel(Params p) {
   V8 qreg[kQInLds ? 1 : 2][kQInLds ? 1 : KS];
   {
     const bool hv = r < G;
-    const float* qp = p.q + ((int64_t)b * p.Hq + hk * G + (hv ? r : 0)) * D + 8 * q;
+    const int64_t qrow = ((int64_t)b * p.Hq + hk * G + (hv ? r : 0)) * D + 8 * q;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      float4 a = hv ? *(const float4*)(qp + 32 * ks) : make_float4(0, 0, 0, 0);
-      float4 c = hv ? *(const float4*)(qp + 32 * ks + 4) : make_float4(0, 0, 0, 0);
+      float4 a = hv ? load_q4(p, qrow + 32 * ks) : make_float4(0, 0, 0, 0);
+      float4 c = hv ? load_q4(p, qrow + 32 * ks + 4) : make_float4(0, 0, 0, 0);
       const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
       V8 hi, lo;
 #pragma unroll
@@ -303,11 +303,11 @@ partition_mfma_kernel(Params p) {
   const int h = hk * G + r;
   if (npart == 1) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* op = p.out + ((int64_t)b * p.Hq + h) * D + 4 * q;
+    const int64_t orow = ((int64_t)b * p.Hq + h) * D + 4 * q;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const f32x4 o = acc[mb] * inv;
-      *(float4*)(op + 16 * mb) = make_float4(o[0], o[1], o[2], o[3]);
+      store_out4(p, orow + 16 * mb, o[0], o[1], o[2], o[3]);
     }
   } else {
     const int64_t row = ((int64_t)b * p.Hq + h) * p.pmax + part;

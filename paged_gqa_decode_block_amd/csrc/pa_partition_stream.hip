@@ -295,11 +295,11 @@ partition_stream_kernel(Params p) {
       V8 qhi[kQLds ? 1 : KS], qlo[kQLds ? 1 : KS];
       {
         const bool hv = r < G;
-        const float* qp = p.q + ((int64_t)b * p.Hq + hk * G + (hv ? r : 0)) * D + 8 * q;
+        const int64_t qrow = ((int64_t)b * p.Hq + hk * G + (hv ? r : 0)) * D + 8 * q;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const float4 a = hv ? *(const float4*)(qp + 32 * ks) : make_float4(0, 0, 0, 0);
-          const float4 c = hv ? *(const float4*)(qp + 32 * ks + 4) : make_float4(0, 0, 0, 0);
+          const float4 a = hv ? load_q4(p, qrow + 32 * ks) : make_float4(0, 0, 0, 0);
+          const float4 c = hv ? load_q4(p, qrow + 32 * ks + 4) : make_float4(0, 0, 0, 0);
           const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
           V8 hi, lo;
 #pragma unroll
@@ -387,11 +387,11 @@ partition_stream_kernel(Params p) {
           const int h = hk * G + r;
           if (direct) {
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
-            float* op = p.out + ((int64_t)b * p.Hq + h) * D + 4 * q;
+            const int64_t orow = ((int64_t)b * p.Hq + h) * D + 4 * q;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
               const f32x4 o = acc[mb] * inv;
-              *(float4*)(op + 16 * mb) = make_float4(o[0], o[1], o[2], o[3]);
+              store_out4(p, orow + 16 * mb, o[0], o[1], o[2], o[3]);
             }
           } else if (is_main) {
             const int64_t row = ((int64_t)b * p.Hq + h) * p.pmax + pp;

@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(256) partition_valu_kernel(Params p) {
   if (L == 0) {
     if (part == 0) {
       for (int i = tid; i < G * D; i += 256)
-        p.out[((int64_t)b * p.Hq + hk * G + i / D) * D + i % D] = 0.f;
+        store_out1(p, ((int64_t)b * p.Hq + hk * G + i / D) * D + i % D, 0.f);
     }
     return;
   }
@@ -112,10 +112,10 @@ __global__ void __launch_bounds__(256) partition_valu_kernel(Params p) {
   float qv[G][E];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float* qp = p.q + ((int64_t)b * p.Hq + hk * G + g) * D + cl * E;
+    const int64_t qrow = ((int64_t)b * p.Hq + hk * G + g) * D + cl * E;
 #pragma unroll
     for (int e = 0; e < E; e += 4) {
-      const float4 x = *(const float4*)(qp + e);
+      const float4 x = load_q4(p, qrow + e);
       qv[g][e] = x.x * p.qscale;
       qv[g][e + 1] = x.y * p.qscale;
       qv[g][e + 2] = x.z * p.qscale;
@@ -230,7 +230,7 @@ __global__ void __launch_bounds__(256) partition_valu_kernel(Params p) {
     }
     const int h = hk * G + g;
     if (npart == 1) {
-      p.out[((int64_t)b * p.Hq + h) * D + d] = ls > 0.f ? as / ls : 0.f;
+      store_out1(p, ((int64_t)b * p.Hq + h) * D + d, ls > 0.f ? as / ls : 0.f);
     } else {
       const int64_t rw = ((int64_t)b * p.Hq + h) * p.pmax + part;
       p.ws_acc[rw * D + d] = as;

@@ -195,6 +195,8 @@ def test_decode_argument_errors_return_before_device_work():
 
 def test_flags_field():
     assert pa.validate(_desc(kv_shared=True)) == 0
+    assert pa.validate(_desc(qo_bf16=True)) == 0
+    assert pa.validate(_desc(kv_shared=True, qo_bf16=True)) == 0
     d = _desc()
     d.flags = 4  # unknown bit
     assert pa.validate(d) == -2

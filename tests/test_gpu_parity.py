@@ -485,3 +485,32 @@ def test_copy_on_write_with_block_manager(torch_cuda):
         assert np.abs(got - want).max() <= 3e-3, path
     assert int(status.item()) == 0
     assert np.abs(want[0] - want[1]).max() > 1e-3  # the two new tokens differ
+
+
+# --- bf16 q and out ---------------------------------------------------------------
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f16", "f32"])
+def test_bf16_q_and_out(torch_cuda, kv_dtype):
+    """q given in bf16 and out written in bf16 (PA_FLAG_QO_BF16): with q values
+    that bf16 holds exactly, the bf16 output is the fp32 path's output rounded
+    to nearest even (torch's conversion), bit for bit, on every kernel path;
+    against the oracle it is within the K/V tolerance plus half a bf16 ulp."""
+    torch = torch_cuda
+    rng = np.random.default_rng(98)
+    q = W.from_storage(W.to_storage(rng.standard_normal((3, 16, 128)).astype(np.float32), "bf16"),
+                       "bf16").astype(np.float32)
+    case, _, _ = paged_case(rng, B=3, Hq=16, Hkv=2, D=128, bs=16, kv_dtype=kv_dtype,
+                            seqlens=[700, 1, 33], q=q)
+    want = run_oracle(case)
+    dev = to_device(torch, case)
+    q16 = dev["q"].to(torch.bfloat16)
+    args = (dev["k"], dev["v"], dev["table"], dev["seqlens"], case.scale)
+    for path in paths_for(case):
+        for ps in (32, 0):
+            o32 = pa.paged_attn_decode(dev["q"], *args, partition_size=ps, path=path)
+            o16 = pa.paged_attn_decode(q16, *args, partition_size=ps, path=path)
+            torch.cuda.synchronize()
+            assert o16.dtype == torch.bfloat16
+            assert torch.equal(o16, o32.to(torch.bfloat16)), (path, ps)
+            got = o16.float().cpu().numpy().astype(np.float64)
+            assert (np.abs(got - want) <= TOL[kv_dtype] + np.abs(want) * 2.0 ** -8).all(), (path, ps)
