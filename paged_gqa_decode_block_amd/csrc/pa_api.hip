@@ -26,6 +26,7 @@ int64_t max_tokens(const pa_desc* d) { return (int64_t)d->max_blocks_per_seq * d
 int pick_path(const pa_desc* d);
 int cu_count();
 int stream_variant();
+int stream_variant_for(const pa_desc* d);
 
 // Partition size for a descriptor that passed validation of everything else.
 // Without a caller choice: 4096 tokens for the streaming kernel (its waves
@@ -86,6 +87,9 @@ int stream_variant() {
   return v;
 }
 
+// The variant a call runs: bf16 q/out is built for the default variant only.
+int stream_variant_for(const pa_desc* d) { return (d->flags & PA_FLAG_QO_BF16) ? 0 : stream_variant(); }
+
 // Non-temporal K/V loads in the streaming kernel (unless the descriptor says
 // blocks are shared): PAGEDATTN_STREAM_NT=0 turns them off for tuning sweeps
 // (read once), on otherwise.
@@ -103,7 +107,7 @@ bool stream_nt() {
 // sequence.
 int stream_waves(const pa_desc* d) {
   const int64_t chunks_per_stream = (max_tokens(d) + 15) / 16;
-  return pa::stream_grid(d->head_dim, stream_variant(), cu_count(),
+  return pa::stream_grid(d->head_dim, stream_variant_for(d), cu_count(),
                          (int64_t)d->batch * d->num_kv_heads * chunks_per_stream);
 }
 
@@ -315,7 +319,7 @@ int run_partition(const pa_desc* desc, const pa::Params& p, hipStream_t s) {
   hipError_t e;
   switch (pick_path(desc)) {
     case PA_PATH_MFMA_STREAM:
-      e = pa::launch_partition_stream(p, desc->kv_dtype, stream_variant(),
+      e = pa::launch_partition_stream(p, desc->kv_dtype, stream_variant_for(desc),
                                       !(desc->flags & PA_FLAG_KV_SHARED) && stream_nt(), s);
       break;
     case PA_PATH_MFMA_GRID: e = pa::launch_partition_mfma(p, desc->kv_dtype, s); break;

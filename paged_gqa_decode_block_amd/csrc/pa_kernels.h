@@ -100,9 +100,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
-// q elements idx .. idx + 3 (idx a multiple of 4) as floats.
+// q elements idx .. idx + 3 (idx a multiple of 4) as floats; QO: 0 fp32,
+// 1 bf16, -1 read p.qo_bf16 at run time. Kernels whose register budget is tight
+// take the dtype as a template argument: a run-time branch at the output store
+// made the register allocator spill the streaming kernel's ring.
+template <int QO = -1>
 __device__ __forceinline__ float4 load_q4(const Params& p, int64_t idx) {
-  if (p.qo_bf16) {
+  if (QO == 1 || (QO < 0 && p.qo_bf16)) {
     const uint2 u = *(const uint2*)((const uint16_t*)p.q + idx);
     return make_float4(bf16_to_f32(u.x & 0xffffu), bf16_to_f32(u.x >> 16),
                        bf16_to_f32(u.y & 0xffffu), bf16_to_f32(u.y >> 16));
@@ -110,9 +114,10 @@ __device__ __forceinline__ float4 load_q4(const Params& p, int64_t idx) {
   return *(const float4*)((const float*)p.q + idx);
 }
 // out elements idx .. idx + 3 (idx a multiple of 4), and a single element.
+template <int QO = -1>
 __device__ __forceinline__ void store_out4(const Params& p, int64_t idx, float a, float b, float c,
                                            float d) {
-  if (p.qo_bf16)
+  if (QO == 1 || (QO < 0 && p.qo_bf16))
     *(uint2*)((uint16_t*)p.out + idx) =
         make_uint2(f32_to_bf16(a) | (f32_to_bf16(b) << 16), f32_to_bf16(c) | (f32_to_bf16(d) << 16));
   else

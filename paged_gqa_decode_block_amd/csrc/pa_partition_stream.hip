@@ -167,7 +167,7 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 // NBUF: ring slots (chunks in flight + 1), (NBUF - 1) * 2 * LPC <= 63 so the
 // vector-memory counter can track them all. OCC: waves per SIMD the register
 // allocation is held to. POL: cache policy of the K/V loads.
-template <typename T, int D, int NBUF, int OCC, int POL, bool QL>
+template <typename T, int D, int NBUF, int OCC, int POL, bool QL, int QO>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 partition_stream_kernel(Params p) {
   typedef Mx<T> M;
@@ -298,8 +298,8 @@ partition_stream_kernel(Params p) {
         const int64_t qrow = ((int64_t)b * p.Hq + hk * G + (hv ? r : 0)) * D + 8 * q;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const float4 a = hv ? load_q4(p, qrow + 32 * ks) : make_float4(0, 0, 0, 0);
-          const float4 c = hv ? load_q4(p, qrow + 32 * ks + 4) : make_float4(0, 0, 0, 0);
+          const float4 a = hv ? load_q4<QO>(p, qrow + 32 * ks) : make_float4(0, 0, 0, 0);
+          const float4 c = hv ? load_q4<QO>(p, qrow + 32 * ks + 4) : make_float4(0, 0, 0, 0);
           const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
           V8 hi, lo;
 #pragma unroll
@@ -391,7 +391,7 @@ partition_stream_kernel(Params p) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
               const f32x4 o = acc[mb] * inv;
-              store_out4(p, orow + 16 * mb, o[0], o[1], o[2], o[3]);
+              store_out4<QO>(p, orow + 16 * mb, o[0], o[1], o[2], o[3]);
             }
           } else if (is_main) {
             const int64_t row = ((int64_t)b * p.Hq + h) * p.pmax + pp;
@@ -541,25 +541,27 @@ constexpr int kVariants[kNumVariants][3][3] = {
 };
 constexpr int dim_index(int D) { return D == 64 ? 0 : D == 128 ? 1 : 2; }
 
-template <typename T, int D, int V, int POL>
+template <typename T, int D, int V, int POL, int QO>
 hipError_t launch_t(const Params& p, hipStream_t s) {
   constexpr int NBUF = kVariants[V][dim_index(D)][0], OCC = kVariants[V][dim_index(D)][1];
   constexpr bool QL = kVariants[V][dim_index(D)][2] != 0;
   const int64_t bound = (int64_t)p.B * p.Hkv * (((int64_t)p.MBS << p.bs_log2) + 15) / 16;
   const int waves = stream_grid(D, V, p.cus, bound);
-  hipLaunchKernelGGL((partition_stream_kernel<T, D, NBUF, OCC, POL, QL>), dim3(waves), dim3(64), 0,
-                     s, p);
+  hipLaunchKernelGGL((partition_stream_kernel<T, D, NBUF, OCC, POL, QL, QO>), dim3(waves), dim3(64),
+                     0, s, p);
   return hipGetLastError();
 }
 
+// fp32 q/out: every variant; bf16 q/out: the default variant only
 template <typename T, int POL>
 hipError_t launch_v(const Params& p, int variant, hipStream_t s) {
 #define PA_STREAM_CASE(DD)                                          \
   case DD:                                                          \
-    if (variant == 1) return launch_t<T, DD, 1, POL>(p, s);         \
-    if (variant == 2) return launch_t<T, DD, 2, POL>(p, s);         \
-    if (variant == 3) return launch_t<T, DD, 3, POL>(p, s);         \
-    return launch_t<T, DD, 0, POL>(p, s);
+    if (p.qo_bf16) return launch_t<T, DD, 0, POL, 1>(p, s);         \
+    if (variant == 1) return launch_t<T, DD, 1, POL, 0>(p, s);      \
+    if (variant == 2) return launch_t<T, DD, 2, POL, 0>(p, s);      \
+    if (variant == 3) return launch_t<T, DD, 3, POL, 0>(p, s);      \
+    return launch_t<T, DD, 0, POL, 0>(p, s);
   switch (p.D) {
     PA_STREAM_CASE(64)
     PA_STREAM_CASE(128)
