@@ -53,10 +53,10 @@ int pick_partition(const pa_desc* d) {
 // PA_PATH_MFMA_STREAM (or an error).
 int pick_path(const pa_desc* d) {
   const int G = d->num_q_heads / d->num_kv_heads;
-  // the streaming kernel counts a batch's 16-token chunks per KV head in 32 bits
+  // the streaming kernel counts a batch's 16-token chunks (all KV heads) in 32 bits
   const bool stream_ok =
       pa::stream_supports(d->kv_dtype, d->head_dim, G, d->block_size, d->batch) &&
-      (int64_t)d->batch * ((max_tokens(d) + 15) / 16) < ((int64_t)1 << 31);
+      (int64_t)d->batch * d->num_kv_heads * ((max_tokens(d) + 15) / 16) < ((int64_t)1 << 31);
   switch (d->path) {
     case PA_PATH_VALU:
       return pa::valu_supports(d->kv_dtype, d->head_dim, G) ? PA_PATH_VALU : PA_E_SHAPE;

@@ -72,6 +72,13 @@ __host__ __device__ inline int stream_active_waves(int64_t n_chunks, int grid, i
   if (w >= cus) w = w / cus * cus;
   return (int)(w < 1 ? 1 : w);
 }
+// The same in 32 bits (the kernel's chunk count is below 2^31).
+__host__ __device__ inline int stream_active_waves32(int n_chunks, int grid, int cus) {
+  int w = n_chunks / kStreamMinChunks;
+  if (w >= grid) return grid;
+  if (w >= cus) w = w / cus * cus;
+  return w < 1 ? 1 : w;
+}
 bool valu_supports(int dtype, int D, int G);
 bool mfma_supports(int dtype, int D, int G);
 

@@ -195,37 +195,59 @@ partition_stream_kernel(Params p) {
   // count whenever there is enough work, so every compute unit streams the
   // same number of bytes until the end. A share may begin or end inside a
   // partition; the wave then leaves that piece as a continuation state.
+  // All windows' lengths are loaded before any is checked, so the loads travel
+  // together; wave 0 reports an out-of-range length once.
   const int nwin = (p.B + 63) >> 6;
-  int ncw[kMaxWindows];
+  int ncw[kMaxWindows], lw[kMaxWindows];
   int tot = 0;
 #pragma unroll
   for (int wi = 0; wi < kMaxWindows; ++wi) {
-    int nc = 0;
-    if (wi < nwin) {
-      const int b = wi * 64 + lane;
-      if (b < p.B) nc = (clamped_len(p, b, blockIdx.x == 0) + 15) >> 4;
-    }
-    ncw[wi] = nc;
+    const int b = wi * 64 + lane;
+    lw[wi] = (wi < nwin && b < p.B) ? p.seqlens[b] : 0;
   }
+  {
+    const int lmax = p.MBS << p.bs_log2;
+    bool bad_len = false;
 #pragma unroll
-  for (int wi = 0; wi < kMaxWindows; ++wi) {
-    int s = ncw[wi];
+    for (int wi = 0; wi < kMaxWindows; ++wi) {
+      const int b = wi * 64 + lane;
+      int Lb = lw[wi] + p.len_add;
+      if (wi < nwin && b < p.B && (Lb < 0 || Lb > lmax)) {
+        bad_len = true;
+        Lb = Lb < 0 ? 0 : lmax;
+      }
+      lw[wi] = (wi < nwin && b < p.B) ? Lb : 0;
+      ncw[wi] = (lw[wi] + 15) >> 4;
+    }
+    if (blockIdx.x == 0 && __ballot(bad_len) && lane == 0 && p.status)
+      atomicOr(p.status, kStatusBadSeqlen);
+  }
+  {
+    // lane-local sum over the windows, then one wave reduction
+    int s = 0;
+#pragma unroll
+    for (int wi = 0; wi < kMaxWindows; ++wi) s += ncw[wi];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    tot += s;  // uniform
+    tot = s;  // uniform
   }
-  const int64_t n_chunks = (int64_t)tot * Hkv;
-  const int nw = stream_active_waves(n_chunks, (int)gridDim.x, p.cus);
+  // 32-bit chunk arithmetic: the host admits only batches with fewer than
+  // 2^31 chunks. Wave x takes base + (x < extra) chunks starting at
+  // x * base + min(x, extra).
+  const int n_chunks = tot * Hkv;
+  const int nw = stream_active_waves32(n_chunks, (int)gridDim.x, p.cus);
   if ((int)blockIdx.x >= nw) return;
-  int64_t g = n_chunks * blockIdx.x / nw;
-  const int64_t g_end = n_chunks * (blockIdx.x + 1) / nw;
+  const int sh_base = n_chunks / nw, sh_extra = n_chunks - sh_base * nw;
+  const int wx = (int)blockIdx.x;
+  int g = wx * sh_base + min(wx, sh_extra);
+  const int g_end = g + sh_base + (wx < sh_extra ? 1 : 0);
   if (g >= g_end) return;
 
   // sequence holding chunk g: Hkv * P(b) <= g < Hkv * P(b + 1), P = prefix of nc
-  int b = 0, ncb = 1;
-  int64_t Pb = 0;
+  int b = 0, ncb = 1, L = 0;
+  int Pb = 0;
   {
-    const int x = (int)(g / Hkv);
+    const int x = g / Hkv;
     int carry = 0;
     bool found = false;
 #pragma unroll
@@ -237,6 +259,7 @@ partition_stream_kernel(Params p) {
           const int src = __builtin_ctzll(hit);
           b = wi * 64 + src;
           ncb = __shfl(ncw[wi], src);
+          L = __shfl(lw[wi], src);
           Pb = __shfl(incl, src) - ncb;
           found = true;
         }
@@ -244,12 +267,11 @@ partition_stream_kernel(Params p) {
       }
     }
   }
-  int L = clamped_len(p, b, false);
   int hk, j;
   {
-    const int64_t e = g - Pb * Hkv;
-    hk = (int)(e / ncb);
-    j = (int)(e - (int64_t)hk * ncb);
+    const int e = g - Pb * Hkv;
+    hk = e / ncb;
+    j = e - hk * ncb;
   }
 
   const int bsm = (1 << p.bs_log2) - 1;
@@ -270,7 +292,7 @@ partition_stream_kernel(Params p) {
   int bad_block = 0;
   while (g < g_end) {
     const int jA = j;
-    const int nch = (int)min<int64_t>((int64_t)(ncb - j), g_end - g);
+    const int nch = min(ncb - j, g_end - g);
     {
       const int T0 = 16 * jA;
       const int T1 = min(L, 16 * (jA + nch));
@@ -290,17 +312,34 @@ partition_stream_kernel(Params p) {
       };
       int idr[NBUF];
       static_for<0, NBUF>([&](auto S) { idr[decltype(S)::value] = fetch_id(decltype(S)::value); });
+      // table entries before Q in the load queue: the ring's first issue waits
+      // for the entries only
+      __builtin_amdgcn_sched_barrier(0);
 
-      // Q' fragments of head r (zero for padded heads)
-      V8 qhi[kQLds ? 1 : KS], qlo[kQLds ? 1 : KS];
+      // Q of head r (zero for padded heads): the loads are issued here, but
+      // turned into Q' fragments only after the ring's first K/V loads are
+      // issued, so the wave's first HBM requests do not wait for Q.
+      float4 qa[KS], qb[KS];
       {
         const bool hv = r < G;
         const int64_t qrow = ((int64_t)b * p.Hq + hk * G + (hv ? r : 0)) * D + 8 * q;
+        // every lane loads (padded heads read head 0's row, a valid address)
+        // and make_q zeroes padded heads: no branch around the loads
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const float4 a = hv ? load_q4<QO>(p, qrow + 32 * ks) : make_float4(0, 0, 0, 0);
-          const float4 c = hv ? load_q4<QO>(p, qrow + 32 * ks + 4) : make_float4(0, 0, 0, 0);
-          const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+          qa[ks] = load_q4<QO>(p, qrow + 32 * ks);
+          qb[ks] = load_q4<QO>(p, qrow + 32 * ks + 4);
+        }
+      }
+      V8 qhi[kQLds ? 1 : KS], qlo[kQLds ? 1 : KS];
+      auto make_q = [&]() {
+        const bool hv = r < G;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          float x[8] = {qa[ks].x, qa[ks].y, qa[ks].z, qa[ks].w,
+                        qb[ks].x, qb[ks].y, qb[ks].z, qb[ks].w};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x[k] = hv ? x[k] : 0.f;
           V8 hi, lo;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
@@ -317,7 +356,7 @@ partition_stream_kernel(Params p) {
             qlo[ks] = lo;
           }
         }
-      }
+      };
 
       // issue the loads of chunk cn into one ring slot; returns the chunk's
       // number of attended rows (0 behind an invalid table entry). The buffer
@@ -327,13 +366,15 @@ partition_stream_kernel(Params p) {
       // dereferenced; it is noted in bad_block and reported once when the
       // wave ends (no store or atomic sits between the ring's loads).
       auto issue = [&](int cn, uint4 (&rk)[LPC], uint4 (&rv)[LPC], int& ids) -> int {
-        int id = -1;
-        if (cn < nch) {
-          id = __builtin_amdgcn_readfirstlane(ids);
-          if (id < 0 || id >= p.NB) {
-            bad_block = 1;
-            id = -1;
-          }
+        // the entry is read whatever cn is: a read inside the cn < nch branch
+        // lets the compiler move the entry's load next to it and wait for it
+        // (and everything issued before) right there
+        int id = __builtin_amdgcn_readfirstlane(ids);
+        if (cn >= nch) {
+          id = -1;
+        } else if (id < 0 || id >= p.NB) {
+          bad_block = 1;
+          id = -1;
         }
         const int tok0 = T0 + 16 * cn;
         const int rows = id >= 0 ? min(16, T1 - tok0) : 0;
@@ -492,6 +533,7 @@ partition_stream_kernel(Params p) {
         constexpr int s = decltype(S)::value;
         rows[s] = issue(s, rk[s], rv[s], idr[s]);
       });
+      make_q();
       int to_bound = CPP - jA % CPP;  // chunks until the next partition boundary
       for (int cb = 0; cb < nch; cb += NBUF) {
         static_for<0, NBUF>([&](auto S) {
