@@ -94,14 +94,11 @@ static int64_t slot_of(const problem* p, int b, int t, int* off) {
   return phys;
 }
 
-/* One (b, h) pair: out[0..D) in fp64. s is caller scratch of MBS*bs doubles. */
-static int one_head(const problem* p, int b, int h, double* s, double* out) {
-  int L = p->seqlens[b];
-  int G = p->Hq / p->Hkv;
-  int hk = h / G;
-  const float* qv = p->q + ((int64_t)b * p->Hq + h) * p->D;
+/* Softmax of scale * q . K[t] over tokens t in [0, L) of sequence b, KV head
+ * hk, applied to V: out[0..D) in fp64 (zeros when L = 0). s is caller scratch
+ * of at least L doubles. Two passes: all scores first, then the weights. */
+static int attend(const problem* p, const float* qv, int b, int hk, int L, double* s, double* out) {
   for (int i = 0; i < p->D; i++) out[i] = 0.0;
-  if (L < 0 || (int64_t)L > (int64_t)p->MBS * p->bs) return OR_ESEQLEN;
   if (L == 0) return OR_OK;
   /* pass 1: scores */
   double M = -INFINITY;
@@ -125,6 +122,19 @@ static int one_head(const problem* p, int b, int h, double* s, double* out) {
   }
   for (int i = 0; i < p->D; i++) out[i] /= Z;
   return OR_OK;
+}
+
+/* One (b, h) pair of the decode: the query is row b of q, the keys are the
+ * L_b cached tokens. */
+static int one_head(const problem* p, int b, int h, double* s, double* out) {
+  int L = p->seqlens[b];
+  int G = p->Hq / p->Hkv;
+  const float* qv = p->q + ((int64_t)b * p->Hq + h) * p->D;
+  if (L < 0 || (int64_t)L > (int64_t)p->MBS * p->bs) {
+    for (int i = 0; i < p->D; i++) out[i] = 0.0;
+    return OR_ESEQLEN;
+  }
+  return attend(p, qv, b, h / G, L, s, out);
 }
 
 typedef struct {
@@ -209,6 +219,56 @@ int oracle_paged_attn_pairs(int B, int Hq, int Hkv, int D, int bs, int NB, int M
   for (int t = 1; t <= started; t++) pthread_join(th[t], NULL);
   free(th);
   return j.status;
+}
+
+/* Paged prefill (varlen queries), one (row, h) pair at a time. Query rows
+ * cu_q[b] .. cu_q[b+1]-1 belong to sequence b (q_len_b of them) and the keys are
+ * its L_b = seqlens_k[b] cached tokens, the new ones included. Row i of the
+ * sequence sits at position L_b - q_len_b + i: causal, it attends tokens
+ * [0, L_b - q_len_b + i] (none when that is negative), else all L_b. */
+int oracle_paged_prefill_pairs(int B, int Hq, int Hkv, int D, int bs, int NB, int MBS, int dtype,
+                               const float* q, const void* k, const void* v,
+                               const int64_t* kstrides, const int64_t* vstrides,
+                               const int32_t* table, const int32_t* cu_q, const int32_t* seqlens_k,
+                               int causal, double scale, const int32_t* pairs, int npairs,
+                               double* out) {
+  int rc = check_shape(B, Hq, Hkv, D, bs, NB, MBS, dtype);
+  if (rc != OR_OK) return rc;
+  if (cu_q[0] != 0) return OR_EARG;
+  for (int b = 0; b < B; b++) {
+    if (cu_q[b + 1] < cu_q[b]) return OR_EARG;
+    if (seqlens_k[b] < 0 || (int64_t)seqlens_k[b] > (int64_t)MBS * bs) return OR_ESEQLEN;
+  }
+  const int total_q = cu_q[B];
+  problem p = {B, Hq, Hkv, D, bs, NB, MBS, dtype, q, k, v,
+               {kstrides[0], kstrides[1], kstrides[2]}, {vstrides[0], vstrides[1], vstrides[2]},
+               table, seqlens_k, scale};
+  double* s = (double*)malloc(sizeof(double) * ((size_t)MBS * bs + 1));
+  if (!s) return OR_ENOMEM;
+  const int G = Hq / Hkv;
+  for (int k2 = 0; k2 < npairs; k2++) {
+    const int row = pairs[2 * k2], h = pairs[2 * k2 + 1];
+    if (row < 0 || row >= total_q || h < 0 || h >= Hq) {
+      free(s);
+      return OR_EARG;
+    }
+    int b = 0;
+    while (cu_q[b + 1] <= row) b++; /* the sequence holding the row */
+    const int qlen = cu_q[b + 1] - cu_q[b], L = seqlens_k[b];
+    int kend = L;
+    if (causal) {
+      kend = L - qlen + (row - cu_q[b]) + 1;
+      if (kend < 0) kend = 0;
+      if (kend > L) kend = L;
+    }
+    rc = attend(&p, q + ((int64_t)row * Hq + h) * D, b, h / G, kend, s, out + (int64_t)k2 * D);
+    if (rc != OR_OK) {
+      free(s);
+      return rc;
+    }
+  }
+  free(s);
+  return OR_OK;
 }
 
 /* Where token t of sequence b lives: writes the table entry and the offset.

@@ -9,7 +9,9 @@ The oracle computes, for each sequence b and query head h, the full softmax of
 token t from block ``block_table[b, t // bs]`` at offset ``t % bs`` and reading KV
 head ``h // (H_q / H_kv)`` (page "Paged Attention Kernel Architecture for
 BI-V100", sections 1, 3 and 4; decode-path example of the paged-attention docs
-page). See ``oracle.c`` for the arithmetic.
+page). ``paged_attn_prefill`` is the varlen (many queries per sequence, causal)
+form over the same paged pool (varlen path of that docs page). See
+``oracle.c`` for the arithmetic.
 """
 from __future__ import annotations
 
@@ -52,6 +54,9 @@ def _load():
     lib.oracle_paged_attn_pairs.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, p,
                                             ctypes.c_double, p, i, p, i]
     lib.oracle_paged_attn_pairs.restype = i
+    lib.oracle_paged_prefill_pairs.argtypes = [i, i, i, i, i, i, i, i, p, p, p, p, p, p, p, p, i,
+                                               ctypes.c_double, p, i, p]
+    lib.oracle_paged_prefill_pairs.restype = i
     lib.oracle_token_slot.argtypes = [p, i, i, i, i, i, p, p]
     lib.oracle_token_slot.restype = i
     lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
@@ -116,6 +121,49 @@ def paged_attn_decode(q, k_pool, v_pool, block_table, seqlens, scale, *, kv_dtyp
     if rc != 0:
         raise OracleError(f"oracle: {ERRORS.get(rc, rc)}")
     return out.reshape(B, Hq, D) if full else out
+
+
+def paged_attn_prefill(q, k_pool, v_pool, block_table, cu_seqlens_q, seqlens_k, scale, *, causal,
+                       kv_dtype, block_size, num_kv_heads, layout="HND", pairs=None):
+    """fp64 outputs of the paged varlen prefill.
+
+    ``q`` is ``[total_q, H_q, D]``; rows ``cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1``
+    are sequence b's queries (the varlen indexing of the paged-attention docs
+    page, varlen path), its keys the ``seqlens_k[b]`` tokens its table maps
+    (the new ones included). With ``causal`` row i of a sequence with q_len
+    queries and L keys attends tokens ``[0, L - q_len + i]`` (none when that is
+    negative, giving zeros), else all L. Returns ``[total_q, H_q, D]`` float64,
+    or ``[len(pairs), D]`` for an ``[n, 2]`` array of (row, h).
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    total_q, Hq, D = q.shape
+    table = np.ascontiguousarray(block_table, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    sk = np.ascontiguousarray(seqlens_k, dtype=np.int32)
+    B, MBS = table.shape
+    assert cu.shape == (B + 1,) and sk.shape == (B,) and int(cu[-1]) == total_q
+    NB = k_pool.shape[0]
+    want = np.float32 if kv_dtype == "f32" else np.uint16
+    assert k_pool.dtype == want and v_pool.dtype == want
+    ks = np.array(pool_strides(layout, num_kv_heads, block_size, D), dtype=np.int64)
+    for arr in (k_pool, v_pool):
+        st = tuple(s // arr.itemsize for s in arr.strides)
+        assert st[-1] == 1 and st[0] == ks[0], "pool must be a dense array"
+    full = pairs is None
+    if full:
+        rr, hh = np.meshgrid(np.arange(total_q), np.arange(Hq), indexing="ij")
+        pairs = np.stack([rr.ravel(), hh.ravel()], axis=1)
+    pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    out = np.zeros((pairs.shape[0], D), dtype=np.float64)
+    rc = lib.oracle_paged_prefill_pairs(
+        B, Hq, num_kv_heads, D, block_size, NB, MBS, _DTYPE_CODE[kv_dtype],
+        q.ctypes.data, k_pool.ctypes.data, v_pool.ctypes.data, ks.ctypes.data, ks.ctypes.data,
+        table.ctypes.data, cu.ctypes.data, sk.ctypes.data, int(bool(causal)),
+        float(np.float32(scale)), pairs.ctypes.data, pairs.shape[0], out.ctypes.data)
+    if rc != 0:
+        raise OracleError(f"oracle: {ERRORS.get(rc, rc)}")
+    return out.reshape(total_q, Hq, D) if full else out
 
 
 def token_slot(block_table, block_size, num_blocks, b, t):
