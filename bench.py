@@ -213,6 +213,61 @@ def measure_append_graph(wl: Workload, steps: int) -> dict:
             "append_output_equals_decode": same}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+
+
+def measure_prefill(k: int, torch, steps: int, warmup: int) -> dict:
+    """The paged varlen prefill (causal) on prefill workload k: one call per
+    step, inputs resident on the GPU. Useful flops count 2 multiply-adds per
+    attended (query row, head, key, dim) for Q.K and the same for P.V; the
+    kernel's matrix-core work is four times that (Q and P in hi + lo parts)."""
+    import paged_gqa_decode_block_amd as pa
+    from paged_gqa_decode_block_amd import workload as W
+
+    t = time.time()
+    c, cu, q = W.make_prefill(k)
+    log(f"[bench] generated prefill workload {k} ({c.name}) in {time.time() - t:.1f}s")
+
+    def pool(store):
+        return torch.from_numpy(np.ascontiguousarray(store).view(np.int16)).view(
+            torch.bfloat16).to("cuda")[1:]
+
+    qd = torch.from_numpy(q).to("cuda")
+    kp, vp = pool(c.k_store), pool(c.v_store)
+    table = torch.from_numpy(c.block_table).to("cuda")
+    cud = torch.from_numpy(cu).to("cuda")
+    sk = torch.from_numpy(c.seqlens).to("cuda")
+    out = torch.empty_like(qd)
+    qlens = np.diff(cu).astype(np.int64)
+    max_q = int(qlens.max())
+    L = c.seqlens.astype(np.int64)
+    keys = int((qlens * (L - qlens) + qlens * (qlens + 1) // 2).sum())   # attended (row, key) pairs
+    flops = 4.0 * c.Hq * c.D * keys
+    kv_bytes = int(L.sum()) * c.Hkv * c.D * 2 * 2
+
+    def call():
+        pa.paged_attn_prefill(qd, kp, vp, table, cud, sk, c.scale, out, max_seqlen_q=max_q,
+                              causal=True)
+
+    for _ in range(warmup):
+        call()
+    ms = time_steps(torch, call, steps)
+    tf = flops / (ms / 1e3) / 1e12
+    log(f"[bench] {c.name}: prefill {ms * 1e3:.1f} us/step, {tf:.1f} useful TFLOP/s")
+    r = {"workload": c.name, "batch": c.B, "num_q_heads": c.Hq, "num_kv_heads": c.Hkv,
+         "head_dim": c.D, "block_size": c.bs, "kv_dtype": c.kv_dtype, "causal": True,
+         "total_q_rows": int(cu[-1]), "total_cached_tokens": int(L.sum()), "seed": 2000 + k,
+         "us_per_step": round(ms * 1e3, 2), "useful_tflops": round(tf, 2),
+         "kv_bytes": kv_bytes,
+         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                      "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "traffic": None, "kernel": "prefill_kernel",
+                      "algorithmic_flops_per_launch": flops}}
+    del qd, kp, vp, out
+    torch.cuda.empty_cache()
+    return r
+
+
 def roofline(wl: Workload, r: dict) -> dict:
     achieved = wl.kv_bytes / (r["partition_kernel_us"] / 1e6) / 1e9
     out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -283,7 +338,9 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "mfma_grid", "mfma_stream"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile", choices=["partition", "both", "copy"], default=None)
+    ap.add_argument("--profile", choices=["partition", "both", "copy", "prefill"], default=None)
+    ap.add_argument("--prefill", type=str, default="1,2",
+                    help="comma-separated prefill workloads to time ('' for none)")
     a = ap.parse_args()
 
     if a.gpus != 1:
@@ -305,6 +362,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"[bench] copied {n} bytes x {a.steps}")
+        return
+
+    if a.profile == "prefill":
+        measure_prefill(1, torch, a.steps, a.warmup)
         return
 
     wl = Workload(a.config, torch, a.path)
@@ -338,6 +399,10 @@ def main():
                               "roofline": roofline(w2, r2)}
         del w2
         torch.cuda.empty_cache()
+    prefill = {}
+    for k in [int(x) for x in a.prefill.split(",") if x.strip()]:
+        r3 = measure_prefill(k, torch, max(5, a.steps // 5), 3)
+        prefill[r3["workload"]] = r3
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")
@@ -362,6 +427,7 @@ def main():
         "roofline": rl,
         "cpu_baseline": cpu,
         "also": also,
+        "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
 

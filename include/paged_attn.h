@@ -214,6 +214,39 @@ int paged_attn_partition_phase(const pa_desc* desc, const void* q, const void* k
 int paged_attn_combine_phase(const pa_desc* desc, const int32_t* cache_seqlens, void* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Paged varlen prefill (the varlen path of the paged-attention docs page, over
+ * the same paged pool as the decode): sequence b owns query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and attends the seqlens_k[b]
+ * tokens its block_table row maps, the new tokens included (written to the
+ * cache beforehand). With causal != 0 row i of a sequence with q_len rows and
+ * L keys attends tokens [0, L - q_len + i] (bottom-right aligned; a row with
+ * none gets zeros), else all L tokens.
+ *
+ *   desc           batch = number of sequences; heads, head_dim, block_size,
+ *                  pool and strides as for the decode. kv_dtype must be f16 or
+ *                  bf16 (else PA_E_PATH), block_size >= 16 (else PA_E_SHAPE).
+ *                  partition_size and path are ignored; PA_FLAG_QO_BF16 makes q
+ *                  and out bf16.
+ *   q              float32 [total_q, H_q, d] (total_q = cu_seqlens_q[batch]),
+ *                  contiguous, 16-byte aligned
+ *   cu_seqlens_q   int32 [batch + 1], cu_seqlens_q[0] = 0, non-decreasing
+ *   seqlens_k      int32 [batch], L_b in [0, max_blocks_per_seq * block_size]
+ *   max_seqlen_q   an upper bound of every q_len (sizes the grid); a longer
+ *                  sequence has its rows past it unwritten and sets
+ *                  PA_STATUS_BAD_SEQLEN
+ *   out            float32 [total_q, H_q, d], contiguous, 16-byte aligned
+ *   status         as for the decode (PA_STATUS_BAD_BLOCK, PA_STATUS_BAD_SEQLEN)
+ *
+ * One pass, no workspace; asynchronous on `stream`, no allocation (graph-
+ * capturable). Returns PA_OK or a PA_E_* code (nothing launched then).
+ */
+int paged_attn_prefill(const pa_desc* desc, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_table,
+                       const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                       int32_t max_seqlen_q, int32_t causal, float scale, void* out,
+                       int32_t* status, void* stream);
+
 /* Bytes of workspace paged_attn_decode needs for this descriptor on the
  * current device: the partial (max, sum, output) of every possible partition,
  * sized from max_blocks_per_seq * block_size, and on the streaming path

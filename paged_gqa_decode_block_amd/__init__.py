@@ -13,7 +13,7 @@ from ._lib import (  # noqa: F401
     EXPORTED, LIB_PATH, PA_DTYPE, PA_FLAG_KV_SHARED, PA_FLAG_QO_BF16, PA_PATH, PA_STATUS_BAD_BLOCK,
     PA_STATUS_BAD_SEQLEN, PATH_NAME,
     PaDesc, PagedAttnError, check_inputs, decode_append_raw, decode_raw, load_library, make_desc,
-    partition_size,
+    partition_size, prefill_raw,
     resolved_path, strerror, validate, workspace_size,
 )
 
@@ -163,4 +163,54 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cac
         status.data_ptr() if status is not None else 0, int(stream))
     if rc != 0:
         raise PagedAttnError(rc, "paged_attn_decode_append: ")
+    return out
+
+
+def paged_attn_prefill(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, out=None,
+                       *, max_seqlen_q=None, causal=True, layout="HND", status=None, stream=None):
+    """Paged varlen prefill; returns ``out`` ([total_q, H_q, d], q's dtype).
+
+    Sequence b owns query rows ``cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1`` of the
+    packed ``q`` ([total_q, H_q, d], float32 or bfloat16) and attends the
+    ``seqlens_k[b]`` tokens its ``block_table`` row maps (the new ones included).
+    With ``causal`` row i of a sequence with q_len rows and L keys attends tokens
+    ``[0, L - q_len + i]`` (zeros when none), else all L. ``max_seqlen_q`` must
+    bound every q_len; when None it is read from ``cu_seqlens_q`` (a device
+    synchronisation, so pass it for graph capture). K/V must be float16 or
+    bfloat16.
+    """
+    import torch
+
+    if not q.is_cuda:
+        raise ValueError("paged_attn_prefill runs on the GPU; q is on the CPU")
+    if q.dim() != 3:
+        raise ValueError("q must be [total_q, H_q, d]")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("seqlens_k", seqlens_k),
+                    ("block_table", block_table)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    if q.dtype not in (torch.float32, torch.bfloat16) or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float32 or bfloat16 tensor")
+    B = block_table.shape[0]
+    if tuple(cu_seqlens_q.shape) != (B + 1,) or tuple(seqlens_k.shape) != (B,):
+        raise ValueError("cu_seqlens_q must be [B + 1] and seqlens_k [B] for a [B, MBS] block_table")
+    if max_seqlen_q is None:
+        max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if B > 0 else 0
+    # the descriptor's batch is the number of sequences (q's first axis is rows)
+    desc = desc_for(q, k_cache, v_cache, block_table, layout=layout)
+    desc.batch = B
+    if out is None:
+        out = torch.empty_like(q)
+    if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape and dtype")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = prefill_raw(desc, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                     block_table.data_ptr(), cu_seqlens_q.data_ptr(), seqlens_k.data_ptr(),
+                     int(max_seqlen_q), bool(causal), float(scale), out.data_ptr(),
+                     status.data_ptr() if status is not None else 0, int(stream))
+    if rc != 0:
+        raise PagedAttnError(rc, "paged_attn_prefill: ")
     return out

@@ -30,7 +30,7 @@ PA_STATUS_BAD_SEQLEN = 2
 
 EXPORTED = (
     "paged_attn_decode", "paged_attn_decode_append", "paged_attn_partition_phase",
-    "paged_attn_combine_phase",
+    "paged_attn_combine_phase", "paged_attn_prefill",
     "paged_attn_workspace_size", "paged_attn_validate", "paged_attn_partition_size", "paged_attn_resolved_path", "paged_attn_check_inputs",
     "paged_attn_strerror", "paged_attn_abi_version",
     # include/paged_block_manager.h
@@ -96,6 +96,9 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_partition_phase.restype = i32
     lib.paged_attn_combine_phase.argtypes = [dp, vp, vp, vp, sz, vp]
     lib.paged_attn_combine_phase.restype = i32
+    lib.paged_attn_prefill.argtypes = [dp, vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp,
+                                       vp]
+    lib.paged_attn_prefill.restype = i32
     lib.paged_attn_workspace_size.argtypes = [dp]
     lib.paged_attn_workspace_size.restype = sz
     lib.paged_attn_validate.argtypes = [dp]
@@ -183,6 +186,16 @@ def check_inputs(desc: PaDesc, block_table_host, seqlens_host) -> int:
     t = np.ascontiguousarray(block_table_host, dtype=np.int32)
     s = np.ascontiguousarray(seqlens_host, dtype=np.int32)
     return load_library().paged_attn_check_inputs(ctypes.byref(desc), t.ctypes.data, s.ctypes.data)
+
+
+def prefill_raw(desc: PaDesc, q_ptr: int, k_ptr: int, v_ptr: int, table_ptr: int, cu_q_ptr: int,
+                seqlens_k_ptr: int, max_seqlen_q: int, causal: bool, scale: float, out_ptr: int,
+                status_ptr: int, stream: int) -> int:
+    """Direct call of paged_attn_prefill with integer device addresses."""
+    return int(load_library().paged_attn_prefill(
+        ctypes.byref(desc), q_ptr or None, k_ptr or None, v_ptr or None, table_ptr or None,
+        cu_q_ptr or None, seqlens_k_ptr or None, int(max_seqlen_q), int(bool(causal)),
+        ctypes.c_float(scale), out_ptr or None, status_ptr or None, stream or None))
 
 
 def decode_raw(desc: PaDesc, q_ptr: int, k_ptr: int, v_ptr: int, table_ptr: int, seqlens_ptr: int,

@@ -257,7 +257,7 @@ namespace {
 int prepare(const pa_desc* desc, const void* q, const void* k_cache, const void* v_cache,
             const int32_t* block_table, const int32_t* cache_seqlens, float scale, void* out,
             void* workspace, size_t workspace_bytes, int32_t* status, bool need_inputs,
-            pa::Params& p) {
+            pa::Params& p, bool need_ws = true) {
   int rc = validate(desc);
   if (rc != PA_OK) return rc;
   memset(&p, 0, sizeof p);
@@ -266,7 +266,7 @@ int prepare(const pa_desc* desc, const void* q, const void* k_cache, const void*
   if (!cache_seqlens || !out) return PA_E_NULL;
   if (need_inputs && (!q || !k_cache || !v_cache || !block_table)) return PA_E_NULL;
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15) return PA_E_ALIGN;
-  const size_t need = paged_attn_workspace_size(desc);
+  const size_t need = need_ws ? paged_attn_workspace_size(desc) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)))
     return PA_E_WORKSPACE;
 
@@ -382,6 +382,24 @@ int paged_attn_partition_phase(const pa_desc* desc, const void* q, const void* k
                          workspace, workspace_bytes, status, true, p);
   if (rc != PA_OK || p.B == 0) return rc;
   return run_partition(desc, p, (hipStream_t)stream);
+}
+
+int paged_attn_prefill(const pa_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* cu_seqlens_q,
+                       const int32_t* seqlens_k, int32_t max_seqlen_q, int32_t causal, float scale,
+                       void* out, int32_t* status, void* stream) {
+  pa::Params p;
+  const int rc = prepare(desc, q, k_cache, v_cache, block_table, seqlens_k, scale, out, nullptr, 0,
+                         status, true, p, false);
+  if (rc != PA_OK || p.B == 0) return rc;
+  if (!cu_seqlens_q) return PA_E_NULL;
+  if (desc->kv_dtype == PA_DTYPE_F32) return PA_E_PATH;
+  if (desc->block_size < 16 || max_seqlen_q < 0) return PA_E_SHAPE;
+  if (max_seqlen_q == 0) return PA_OK;
+  return pa::launch_prefill(p, desc->kv_dtype, cu_seqlens_q, max_seqlen_q, causal != 0,
+                            (hipStream_t)stream) == hipSuccess
+             ? PA_OK
+             : PA_E_LAUNCH;
 }
 
 int paged_attn_combine_phase(const pa_desc* desc, const int32_t* cache_seqlens, void* out,

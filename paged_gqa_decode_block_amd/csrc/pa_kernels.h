@@ -48,6 +48,11 @@ enum { kStatusBadBlock = 1, kStatusBadSeqlen = 2 };
 hipError_t launch_partition_valu(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_partition_mfma(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_combine(const Params& p, hipStream_t s);
+// Paged varlen prefill: query rows cu_q[b] .. cu_q[b+1]-1 of sequence b (at
+// most max_q of them), keys its p.seqlens[b] cached tokens, causal or not;
+// 16-bit K/V only.
+hipError_t launch_prefill(const Params& p, int dtype, const int32_t* cu_q, int max_q, int causal,
+                          hipStream_t s);
 // Write each sequence's new K and V rows ([B, H_kv, d], the cache's element
 // type) at token cache_seqlens[b] of its paged cache.
 hipError_t launch_append(const Params& p, const void* k_new, const void* v_new, int elem_bytes,

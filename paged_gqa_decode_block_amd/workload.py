@@ -371,3 +371,42 @@ def make_config(k: int, seed: int | None = None, layout: str = "HND",
     if k == 5:
         return _config5(seed, layout, tables_only)
     raise ValueError(f"configs are numbered 1..5, got {k}")
+
+
+# Chunked-prefill workloads over the same kind of paged pool: each sequence's
+# cache already holds the new chunk (its last q_len tokens), and the chunk's
+# queries are packed in rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (the varlen
+# indexing of the paged-attention docs page).
+PREFILL_NAMES = {
+    1: "p1_qwen36_chunked_prefill_bf16",
+    2: "p2_large_gqa_chunked_prefill_bf16",
+}
+
+
+def make_prefill(k: int, seed: int | None = None, layout: str = "HND"):
+    """(case, cu_seqlens_q, q) for prefill workload k, seeded with 2000 + k:
+
+    1. the 100K-token decode shape's heads (H_q 24, H_kv 4, d 256, bf16, blocks
+       of 16): 4 sequences of 8192 cached tokens whose last 512 are the chunk;
+    2. the 64-sequence decode shape's heads (H_q 64, H_kv 8, d 128, bf16, blocks
+       of 16): 16 sequences with lengths uniform in [1024, 8192], chunks of 256.
+
+    ``q`` is float32 [total_q, H_q, d] ~ N(0, 1), drawn after the pool.
+    """
+    if seed is None:
+        seed = 2000 + k
+    if k == 1:
+        case = build_case(PREFILL_NAMES[1], B=4, Hq=24, Hkv=4, D=256, bs=16, kv_dtype="bf16",
+                          seqlens=[8192] * 4, layout=layout, seed=seed)
+        qlens = np.full(4, 512, dtype=np.int32)
+    elif k == 2:
+        case = build_case(PREFILL_NAMES[2], B=16, Hq=64, Hkv=8, D=128, bs=16, kv_dtype="bf16",
+                          seqlen_sampler=lambda r: r.integers(1024, 8193, size=16), layout=layout,
+                          seed=seed)
+        qlens = np.minimum(256, case.seqlens).astype(np.int32)
+    else:
+        raise ValueError(f"prefill workloads are numbered 1..2, got {k}")
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    rng = np.random.default_rng(seed + 500)
+    q = rng.standard_normal((int(cu[-1]), case.Hq, case.D), dtype=np.float32)
+    return case, cu, q

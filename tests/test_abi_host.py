@@ -216,3 +216,23 @@ def test_decode_append_argument_errors():
     assert pa.decode_append_raw(d, **{**args, "vnew_ptr": 0}) == -1
     assert pa.decode_append_raw(d, **{**args, "vnew_ptr": good + 8}) == -7
     assert pa.decode_append_raw(_desc(batch=0), **{**args, "knew_ptr": 0}) == 0  # nothing to do
+
+
+def test_prefill_argument_errors():
+    """Every call below fails (or has nothing to do) before any launch."""
+    d = _desc()
+    good = 1 << 20
+    args = dict(q_ptr=good, k_ptr=good, v_ptr=good, table_ptr=good, cu_q_ptr=good,
+                seqlens_k_ptr=good, max_seqlen_q=16, causal=True, scale=1.0, out_ptr=good,
+                status_ptr=0, stream=0)
+    assert pa.prefill_raw(_desc(head_dim=100), **args) == -3              # bad descriptor
+    assert pa.prefill_raw(d, **{**args, "cu_q_ptr": 0}) == -1            # no cu_seqlens_q
+    assert pa.prefill_raw(d, **{**args, "seqlens_k_ptr": 0}) == -1       # no key lengths
+    assert pa.prefill_raw(d, **{**args, "q_ptr": good + 4}) == -7        # misaligned
+    assert pa.prefill_raw(_desc(kv_dtype="f32", k_strides=(4096, 2048, 128)), **args) == -10
+    assert pa.prefill_raw(_desc(block_size=8, k_strides=(2048, 1024, 128)), **args) == -2
+    assert pa.prefill_raw(d, **{**args, "max_seqlen_q": -1}) == -2
+    assert pa.prefill_raw(d, **{**args, "max_seqlen_q": 0}) == 0          # no rows
+    assert pa.prefill_raw(_desc(batch=0), **{**args, "cu_q_ptr": 0}) == 0  # no sequences
+    # no workspace is involved, whatever the decode would need
+    assert pa.workspace_size(d) > 0

@@ -1,0 +1,156 @@
+"""GPU parity of the paged varlen prefill (paged_attn_prefill) against the
+fp64 oracle, element by element: head sizes 64/128/256, fp16 and bf16 K/V,
+HND and NHD pools, causal and full attention, sequences whose query count is
+below, equal to and above their key count, empty sequences and rows with no
+key to attend (zeros), several 16-row tiles with a ragged last one, bf16 q and
+out, and the status report for a max_seqlen_q below a sequence's row count."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import paged_gqa_decode_block_amd as pa
+from oracle import oracle as O
+from util_cases import paged_case
+
+pytestmark = pytest.mark.gpu
+TOL = {"f16": 3e-3, "bf16": 3e-3}
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pa.load_library()
+    return torch
+
+
+def _pool(torch, case, store):
+    t = torch.from_numpy(np.ascontiguousarray(store).view(np.int16))
+    return t.view(torch.bfloat16 if case.kv_dtype == "bf16" else torch.float16).to("cuda")[1:]
+
+
+def _make(rng, *, Hq, Hkv, D, bs, kv_dtype, klens, qlens, layout="HND"):
+    klens = np.asarray(klens, dtype=np.int32)
+    qlens = np.asarray(qlens, dtype=np.int32)
+    case, _, _ = paged_case(rng, B=len(klens), Hq=Hq, Hkv=Hkv, D=D, bs=bs, kv_dtype=kv_dtype,
+                            seqlens=klens, layout=layout)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = rng.standard_normal((int(cu[-1]), Hq, D)).astype(np.float32)
+    return case, cu, q
+
+
+def _oracle(case, cu, q, causal):
+    return O.paged_attn_prefill(q, case.k_pool, case.v_pool, case.block_table, cu, case.seqlens,
+                                case.scale, causal=causal, kv_dtype=case.kv_dtype,
+                                block_size=case.bs, num_kv_heads=case.Hkv, layout=case.layout)
+
+
+def _gpu(torch, case, cu, q, causal, *, max_q=None, status=None, bf16=False):
+    qd = torch.from_numpy(q).to("cuda")
+    if bf16:
+        qd = qd.to(torch.bfloat16)
+    out = pa.paged_attn_prefill(qd, _pool(torch, case, case.k_store), _pool(torch, case, case.v_store),
+                                torch.from_numpy(case.block_table).to("cuda"),
+                                torch.from_numpy(cu).to("cuda"),
+                                torch.from_numpy(case.seqlens).to("cuda"), case.scale,
+                                max_seqlen_q=max_q, causal=causal, layout=case.layout, status=status)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+CASES = [
+    # name, Hq, Hkv, D, bs, dtype, layout, key lengths, query lengths
+    ("d128_g8_mixed", 16, 2, 128, 16, "bf16", "HND", [300, 40, 77, 1], [37, 40, 90, 1]),
+    ("d64_g7_f16", 14, 2, 64, 16, "f16", "HND", [513, 16, 0, 100], [16, 17, 5, 0]),
+    ("d256_g6", 12, 2, 256, 16, "bf16", "HND", [700, 33], [65, 33]),
+    ("d128_nhd_bs32", 8, 1, 128, 32, "bf16", "NHD", [250, 64], [31, 64]),
+    ("d128_g1", 4, 4, 128, 64, "f16", "HND", [129, 200], [129, 3]),
+]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("idx", range(len(CASES)), ids=[c[0] for c in CASES])
+def test_prefill_matches_oracle(torch_cuda, idx, causal):
+    name, Hq, Hkv, D, bs, dt, layout, kl, ql = CASES[idx]
+    rng = np.random.default_rng(1200 + idx)
+    case, cu, q = _make(rng, Hq=Hq, Hkv=Hkv, D=D, bs=bs, kv_dtype=dt, klens=kl, qlens=ql,
+                        layout=layout)
+    want = _oracle(case, cu, q, causal)
+    status = torch_cuda.zeros(1, dtype=torch_cuda.int32, device="cuda")
+    got = _gpu(torch_cuda, case, cu, q, causal, status=status)
+    assert int(status.item()) == 0
+    assert np.isfinite(got).all()
+    err = np.abs(got - want).max()
+    assert err <= TOL[dt], (name, causal, err)
+    # rows that attend nothing are exact zeros
+    for b in range(len(kl)):
+        for i in range(ql[b]):
+            if causal and kl[b] - ql[b] + i + 1 <= 0 or kl[b] == 0:
+                assert np.all(got[cu[b] + i] == 0.0)
+
+
+def test_prefill_last_row_is_the_decode(torch_cuda):
+    """The last causal row of every sequence sees all its keys: it equals the
+    decode kernel's output for that query (both within the tolerance of the
+    oracle, and close to each other)."""
+    torch = torch_cuda
+    rng = np.random.default_rng(1300)
+    kl, ql = [1000, 64, 513], [48, 64, 1]
+    case, cu, q = _make(rng, Hq=16, Hkv=2, D=128, bs=16, kv_dtype="bf16", klens=kl, qlens=ql)
+    got = _gpu(torch, case, cu, q, True)
+    last = cu[1:] - 1
+    qd = torch.from_numpy(np.ascontiguousarray(q[last])).to("cuda")
+    dec = pa.paged_attn_decode(qd, _pool(torch, case, case.k_store), _pool(torch, case, case.v_store),
+                               torch.from_numpy(case.block_table).to("cuda"),
+                               torch.from_numpy(case.seqlens).to("cuda"), case.scale)
+    torch.cuda.synchronize()
+    dec = dec.cpu().numpy().astype(np.float64)
+    assert np.abs(got[last] - dec).max() <= 3e-3
+
+
+def test_prefill_bf16_q_and_out(torch_cuda):
+    rng = np.random.default_rng(1301)
+    case, cu, q = _make(rng, Hq=8, Hkv=2, D=128, bs=16, kv_dtype="bf16", klens=[200, 50],
+                        qlens=[40, 50])
+    q = q.astype(np.float32)
+    want = _oracle(case, cu, q.astype(np.float32), True)
+    got = _gpu(torch_cuda, case, cu, q, True, bf16=True)
+    # bf16 q rounding and the bf16 output: the K/V tolerance plus bf16 steps
+    assert (np.abs(got - want) <= 1e-2 + np.abs(want) * 2.0 ** -7).all()
+
+
+def test_prefill_reports_rows_beyond_max_seqlen_q(torch_cuda):
+    torch = torch_cuda
+    rng = np.random.default_rng(1302)
+    case, cu, q = _make(rng, Hq=4, Hkv=2, D=64, bs=16, kv_dtype="bf16", klens=[100, 100],
+                        qlens=[40, 10])
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = _gpu(torch, case, cu, q, True, max_q=16, status=status)   # sequence 0 has 40 rows
+    assert int(status.item()) & pa.PA_STATUS_BAD_SEQLEN
+    want = _oracle(case, cu, q, True)
+    assert np.abs(got[:16] - want[:16]).max() <= 3e-3                # the rows that fit
+    assert np.abs(got[40:] - want[40:]).max() <= 3e-3                # sequence 1 complete
+
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_prefill_workloads_sampled(torch_cuda, k):
+    """The bench's chunked-prefill workloads at full size, in the bench's launch
+    configuration: sampled (row, head) outputs against the oracle, covering the
+    first and last row of every sequence."""
+    from paged_gqa_decode_block_amd import workload as W
+
+    torch = torch_cuda
+    c, cu, q = W.make_prefill(k)
+    rng = np.random.default_rng(1400 + k)
+    rows = np.concatenate([cu[:-1], cu[1:] - 1, rng.integers(0, int(cu[-1]), 16)])
+    pairs = np.stack([rows, rng.integers(0, c.Hq, rows.size)], axis=1).astype(np.int32)
+    want = O.paged_attn_prefill(q, c.k_pool, c.v_pool, c.block_table, cu, c.seqlens, c.scale,
+                                causal=True, kv_dtype=c.kv_dtype, block_size=c.bs,
+                                num_kv_heads=c.Hkv, layout=c.layout, pairs=pairs)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = _gpu(torch, c, cu, q, True, max_q=int(np.diff(cu).max()), status=status)
+    assert int(status.item()) == 0
+    assert np.abs(got[pairs[:, 0], pairs[:, 1]] - want).max() <= 3e-3
