@@ -7,20 +7,23 @@
 // tokens [0, L_b - q_len_b + i]; a query with no token to attend gets zeros.
 // Otherwise every query attends all L_b tokens.
 //
-// One wave per (tile of 16 query rows of one sequence, query head). The 16
-// rows are the 16 columns of the score and output tiles, so the chunk loop is
-// the decode kernel's with positions in place of heads:
+// One workgroup of four waves per (tile of 16 query rows of one sequence, KV
+// head, group of up to 8 of its query heads). The 256 threads load each
+// 16-token chunk of K and V once (d/64 16-byte pieces each, raw buffer loads
+// through descriptors cut to the chunk's attended rows, an invalid table entry
+// never dereferenced) into a ring of chunks in registers, and stage it into
+// one of two LDS tiles; after one barrier per chunk every wave computes its
+// query heads (head w, w + 4 of the group) against the tile:
 //
 //   scores  S^T[token, row] = K[token, :] . Q'[row, :]       16x16x32 MFMAs
-//   update  running max m, sum l, output per row (base 2, lazily rescaled)
+//   update  running max m, sum l, output per row and head (base 2, lazily
+//           rescaled)
 //   output  O^T[dim, row] += V^T[dim, token] . P^T[token, row]  16x16x16
 //
-// with Q' and P split into hi + lo 16-bit parts. The wave walks the tokens up
-// to the tile's last row's key end in 16-token chunks through a ring of NBUF
-// chunks in registers (raw buffer loads, descriptors cut to the attended rows
-// of the chunk, an invalid table entry never dereferenced), each chunk staged
-// in LDS; a token is masked per column, so rows of the tile end at their own
-// causal bound. No partial state leaves the wave: the tile is normalised and
+// with the tile's 16 rows as the MFMA columns and Q' and P in hi + lo 16-bit
+// parts. The workgroup walks the tokens up to the tile's last row's key end; a
+// token is masked per column, so each row ends at its own causal bound. No
+// partial state leaves the workgroup: each head's tile is normalised and
 // written at the end.
 //
 // Requires 16-bit K/V and block_size >= 16.
@@ -29,74 +32,84 @@
 namespace pa {
 namespace {
 
-template <typename T, int D, int NBUF, int OCC, bool QL, int QO>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
-prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal) {
+constexpr int kPrefillThreads = 256;  // four waves
+constexpr int kHeadsPerGroup = 8;     // query heads per workgroup (two per wave)
+
+template <typename T, int D, int NBUF, int OCC, int QO>
+__global__ void __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) {
   typedef Mx<T> M;
   typedef typename M::v8 V8;
   typedef typename M::v4 V4;
-  typedef Cfg<D> C;
-  constexpr int LPC = C::LPC, KS = C::KS, MB = C::MB;
-  static_assert((NBUF - 1) * 2 * LPC <= 63, "ring deeper than the vector-memory counter");
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[16 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[16 * D];
-  __shared__ __attribute__((aligned(16))) V8 s_q[QL ? 2 : 1][QL ? KS : 1][64];
+  constexpr int KS = D / 32, MB = D / 16;
+  constexpr int PPT = D / 64;  // 16-byte pieces of a chunk per thread (4 D of them)
+  constexpr int HPW = kHeadsPerGroup / 4;
+  static_assert((NBUF - 1) * PPT <= 60, "ring deeper than the vector-memory counter");
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][16 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][16 * D];
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
   const int r = lane & 15, q = lane >> 4;
-  const int b = blockIdx.z, h = blockIdx.y, p0 = 16 * (int)blockIdx.x;
+  const int b = blockIdx.z;
+  const int hk = (int)blockIdx.y / nhg, g0 = ((int)blockIdx.y % nhg) * kHeadsPerGroup;
+  const int hcount = min(kHeadsPerGroup, p.G - g0);
+  const int p0 = 16 * (int)blockIdx.x;
   const int r0 = cu_q[b];
   const int ql = cu_q[b + 1] - r0;
   // rows beyond the grid would be left unwritten: report
-  if (blockIdx.x == 0 && h == 0 && lane == 0 && p.status && (ql < 0 || ql > 16 * (int)gridDim.x))
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0 && p.status &&
+      (ql < 0 || ql > 16 * (int)gridDim.x))
     atomicOr(p.status, kStatusBadSeqlen);
-  if (p0 >= ql) return;
-  const int L = clamped_len(p, b, blockIdx.x == 0 && h == 0 && lane == 0);
-  const int hk = h / p.G;
+  if (p0 >= ql) return;  // the whole workgroup
+  const int L = clamped_len(p, b, blockIdx.x == 0 && blockIdx.y == 0 && tid == 0);
 
   // column r: query position p0 + r of the sequence; its keys are [0, kend_r)
   const bool col_ok = p0 + r < ql;
-  const int kend_r =
-      !col_ok ? 0 : causal ? min(L, max(0, L - ql + p0 + r + 1)) : L;
+  const int kend_r = !col_ok ? 0 : causal ? min(L, max(0, L - ql + p0 + r + 1)) : L;
   const int plast = min(p0 + 15, ql - 1);
   const int kend = causal ? min(L, max(0, L - ql + plast + 1)) : L;  // the tile's
   const int nch = (kend + 15) >> 4;
 
-  // Q' fragments of row p0 + r (zero for rows past the sequence)
-  const int64_t qrow = ((int64_t)(r0 + (col_ok ? p0 + r : 0)) * p.Hq + h) * D + 8 * q;
-  V8 qhi[QL ? 1 : KS], qlo[QL ? 1 : KS];
+  // this wave's query heads: g0 + w + 4 j of the KV head's group
+  bool hon[HPW];
+  V8 qhi[HPW][KS], qlo[HPW][KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const float4 a = load_q4<QO>(p, qrow + 32 * ks);
-    const float4 c = load_q4<QO>(p, qrow + 32 * ks + 4);
-    const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-    V8 hi, lo;
+  for (int j = 0; j < HPW; ++j) {
+    hon[j] = w + 4 * j < hcount;
+    const int h = hk * p.G + g0 + (hon[j] ? w + 4 * j : 0);
+    const int64_t qrow = ((int64_t)(r0 + (col_ok ? p0 + r : 0)) * p.Hq + h) * D + 8 * q;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float y = col_ok ? x[k] * p.qscale : 0.f;
-      const T hh = (T)y;
-      hi[k] = hh;
-      lo[k] = (T)(y - (float)hh);
-    }
-    if constexpr (QL) {
-      s_q[0][ks][lane] = hi;
-      s_q[1][ks][lane] = lo;
-    } else {
-      qhi[ks] = hi;
-      qlo[ks] = lo;
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4 a = load_q4<QO>(p, qrow + 32 * ks);
+      const float4 c = load_q4<QO>(p, qrow + 32 * ks + 4);
+      const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float y = col_ok ? x[k] * p.qscale : 0.f;
+        const T hh = (T)y;
+        qhi[j][ks][k] = hh;
+        qlo[j][ks][k] = (T)(y - (float)hh);
+      }
     }
   }
 
+  // the pieces this thread loads: piece i = tid + 256 k of the chunk's 4 D
+  // (K pieces first): row, 16-byte column and whether it is V
   const int bsm = (1 << p.bs_log2) - 1;
-  const int rowL = lane / C::CPR;
-  const int cc = lane % C::CPR;
-  const int tj = r >> 2, tk = r & 3;
   const int kst_bytes = (int)(p.kst * (int)sizeof(T)), vst_bytes = (int)(p.vst * (int)sizeof(T));
-  int koffs[LPC], voffs[LPC];
+  int poff[PPT], plds[PPT];
+  bool pisv[PPT];
 #pragma unroll
-  for (int s = 0; s < LPC; ++s) {
-    koffs[s] = (s * C::RPI + rowL) * kst_bytes + 16 * cc;
-    voffs[s] = (s * C::RPI + rowL) * vst_bytes + 16 * cc;
+  for (int k = 0; k < PPT; ++k) {
+    const int i = tid + kPrefillThreads * k;
+    // a wave's 64 pieces are consecutive and 2 D is a multiple of 64, so K or V
+    // is the same across the wave: made visibly uniform for the descriptor choice
+    pisv[k] = __builtin_amdgcn_readfirstlane(i >= 2 * D ? 1 : 0) != 0;
+    const int jj = pisv[k] ? i - 2 * D : i;
+    const int row = jj / (D / 8), cc = jj % (D / 8);
+    poff[k] = row * (pisv[k] ? vst_bytes : kst_bytes) + 16 * cc;
+    plds[k] = row * D + 8 * (cc ^ (pisv[k] ? vswz(row) : (row & 7)));
   }
 
   const int32_t* trow = p.table + (int64_t)b * p.MBS;
@@ -111,10 +124,9 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal) {
   static_for<0, NBUF>([&](auto S) { idr[decltype(S)::value] = fetch_id(decltype(S)::value); });
 
   int bad_block = 0;
-  // (both lambdas are forced inline: called out of line, their ring arguments
+  // (the lambdas are forced inline: called out of line, their ring arguments
   // would live in scratch memory)
-  auto issue = [&](int cn, uint4 (&rk)[LPC], uint4 (&rv)[LPC], int& ids)
-      __attribute__((always_inline)) -> int {
+  auto issue = [&](int cn, uint4 (&pc)[PPT], int& ids) __attribute__((always_inline)) {
     int id = __builtin_amdgcn_readfirstlane(ids);
     if (cn >= nch) {
       id = -1;
@@ -131,59 +143,52 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal) {
     const __amdgpu_buffer_rsrc_t rsv =
         uniform_rsrc(vbase + (idc * p.vsb + row0 * p.vst) * (int)sizeof(T), rows * vst_bytes);
 #pragma unroll
-    for (int s = 0; s < LPC; ++s) {
-      rk[s] = buf_load<2>(rsk, koffs[s]);
-      rv[s] = buf_load<2>(rsv, voffs[s]);
+    for (int k = 0; k < PPT; ++k) {
+      pc[k] = buf_load<2>(pisv[k] ? rsv : rsk, poff[k]);  // a scalar select
     }
     ids = fetch_id(cn + NBUF);
-    return rows;
   };
 
-  f32x4 acc[MB];
+  f32x4 acc[HPW][MB];
+  float m[HPW], l[HPW];
 #pragma unroll
-  for (int k = 0; k < MB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j < HPW; ++j) {
+#pragma unroll
+    for (int k = 0; k < MB; ++k) acc[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+  }
+  const int tj = r >> 2, tk = r & 3;
 
-  auto consume = [&](int cn, const uint4 (&rk)[LPC], const uint4 (&rv)[LPC])
-      __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < LPC; ++s) {
-      const int R = s * C::RPI + rowL;
-      *(uint4*)(s_k + R * D + 8 * (cc ^ (R & 7))) = rk[s];
-      *(uint4*)(s_v + R * D + 8 * (cc ^ vswz(R))) = rv[s];
-    }
-    // scores: lane (q, r) gets tokens 4q..4q+3 of the chunk for row r
+  // fold chunk cn (staged in LDS tile `buf`) into head slot j
+  auto consume = [&](int cn, int buf, int j) __attribute__((always_inline)) {
+    const uint16_t* sk = s_k[buf];
+    const uint16_t* sv_ = s_v[buf];
     f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const V8 a = *(const V8*)(s_k + r * D + 8 * ((4 * ks + q) ^ (r & 7)));
-      if constexpr (QL) {
-        st = M::mma32(a, s_q[0][ks][lane], st);
-        st = M::mma32(a, s_q[1][ks][lane], st);
-      } else {
-        st = M::mma32(a, qhi[ks], st);
-        st = M::mma32(a, qlo[ks], st);
-      }
+      const V8 a = *(const V8*)(sk + r * D + 8 * ((4 * ks + q) ^ (r & 7)));
+      st = M::mma32(a, qhi[j][ks], st);
+      st = M::mma32(a, qlo[j][ks], st);
     }
-    // the row's own key bound (causal) also covers the chunk's attended rows
     float sv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) sv[k] = (16 * cn + 4 * q + k < kend_r) ? st[k] : -INFINITY;
     const float mt = quad_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
-    const bool raise = mt > m + 8.f;
+    const bool raise = mt > m[j] + 8.f;
     if (__ballot(raise)) {
-      const float mn = raise ? mt : m;
-      const float alpha = exp2_fast(m - (mn == -INFINITY ? 0.f : mn));
-      l *= alpha;
+      const float mn = raise ? mt : m[j];
+      const float alpha = exp2_fast(m[j] - (mn == -INFINITY ? 0.f : mn));
+      l[j] *= alpha;
 #pragma unroll
-      for (int k = 0; k < MB; ++k) acc[k] *= alpha;
-      m = mn;
+      for (int k = 0; k < MB; ++k) acc[j][k] *= alpha;
+      m[j] = mn;
     }
-    const float mu = m == -INFINITY ? 0.f : m;
+    const float mu = m[j] == -INFINITY ? 0.f : m[j];
     float pv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) pv[k] = exp2_fast(sv[k] - mu);
-    l += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+    l[j] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
     typename M::e4 ph, pl2;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -194,57 +199,74 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal) {
     const V4 phi = M::pack(ph), plo = M::pack(pl2);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int pc = 2 * (mb ^ tj) + ((tk >> 1) ^ (q & 1));
+      const int pcol = 2 * (mb ^ tj) + ((tk >> 1) ^ (q & 1));
       const s16x4 a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(s_v + (4 * q + tj) * D + 8 * pc + 4 * (tk & 1)));
+          (lds_s16x4*)(sv_ + (4 * q + tj) * D + 8 * pcol + 4 * (tk & 1)));
       const V4 av = __builtin_bit_cast(V4, a4);
-      acc[mb] = M::mma16(av, phi, acc[mb]);
-      acc[mb] = M::mma16(av, plo, acc[mb]);
+      acc[j][mb] = M::mma16(av, phi, acc[j][mb]);
+      acc[j][mb] = M::mma16(av, plo, acc[j][mb]);
     }
   };
 
-  // the ring: chunk c + NBUF - 1 is issued just before chunk c is consumed
-  // (unconditionally: past the end the descriptors are empty)
-  uint4 rk[NBUF][LPC], rv[NBUF][LPC];
+  // the ring: chunk c + NBUF - 1 is issued just before chunk c is staged
+  // (unconditionally: past the end the descriptors are empty). Chunk c goes to
+  // LDS tile c % 2; the barrier after staging also means every wave is done
+  // with chunk c - 1, so tile (c + 1) % 2 is free for the next chunk.
+  uint4 ring[NBUF][PPT];
   static_for<0, NBUF - 1>([&](auto S) {
     constexpr int s = decltype(S)::value;
-    issue(s, rk[s], rv[s], idr[s]);
+    issue(s, ring[s], idr[s]);
   });
   for (int cb = 0; cb < nch; cb += NBUF) {
     static_for<0, NBUF>([&](auto S) {
       constexpr int s = decltype(S)::value;
       constexpr int sn = (s + NBUF - 1) % NBUF;
       const int c = cb + s;
-      issue(c + NBUF - 1, rk[sn], rv[sn], idr[sn]);
+      issue(c + NBUF - 1, ring[sn], idr[sn]);
       __builtin_amdgcn_sched_barrier(0);
-      if (c < nch) consume(c, rk[s], rv[s]);
+      if (c < nch) {
+        const int buf = c & 1;
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+          uint16_t* dst = pisv[k] ? s_v[buf] : s_k[buf];
+          *(uint4*)(dst + plds[k]) = ring[s][k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < HPW; ++j)
+          if (hon[j]) consume(c, buf, j);
+      }
     });
   }
 
-  const float lt = quad_sum(l);
-  if (col_ok) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int64_t orow = ((int64_t)(r0 + p0 + r) * p.Hq + h) * D + 4 * q;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const f32x4 o = acc[mb] * inv;
-      store_out4<QO>(p, orow + 16 * mb, o[0], o[1], o[2], o[3]);
+  for (int j = 0; j < HPW; ++j) {
+    const float lt = quad_sum(l[j]);
+    if (hon[j] && col_ok) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int h = hk * p.G + g0 + w + 4 * j;
+      const int64_t orow = ((int64_t)(r0 + p0 + r) * p.Hq + h) * D + 4 * q;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const f32x4 o = acc[j][mb] * inv;
+        store_out4<QO>(p, orow + 16 * mb, o[0], o[1], o[2], o[3]);
+      }
     }
   }
-  if (bad_block && lane == 0 && p.status) atomicOr(p.status, kStatusBadBlock);
+  if (bad_block && tid == 0 && p.status) atomicOr(p.status, kStatusBadBlock);
 }
 
-// {ring slots, waves per SIMD, Q' in LDS} per head_dim (as the decode kernel's)
-constexpr int kPrefillCfg[3][3] = {{6, 2, 0}, {3, 2, 0}, {3, 1, 1}};
+// {ring slots, workgroups of four waves per CU} per head_dim
+constexpr int kPrefillCfg[3][2] = {{6, 2}, {4, 2}, {3, 1}};
 constexpr int pdim(int D) { return D == 64 ? 0 : D == 128 ? 1 : 2; }
 
 template <typename T, int D, int QO>
 hipError_t launch_p(const Params& p, const int32_t* cu_q, int max_q, int causal, hipStream_t s) {
   constexpr int NB_ = kPrefillCfg[pdim(D)][0], OCC = kPrefillCfg[pdim(D)][1];
-  constexpr bool QL = kPrefillCfg[pdim(D)][2] != 0;
-  dim3 grid((max_q + 15) / 16, p.Hq, p.B);
-  hipLaunchKernelGGL((prefill_kernel<T, D, NB_, OCC, QL, QO>), grid, dim3(64), 0, s, p, cu_q,
-                     causal);
+  const int nhg = (p.G + kHeadsPerGroup - 1) / kHeadsPerGroup;
+  dim3 grid((max_q + 15) / 16, p.Hkv * nhg, p.B);
+  hipLaunchKernelGGL((prefill_kernel<T, D, NB_, OCC, QO>), grid, dim3(kPrefillThreads), 0, s, p,
+                     cu_q, causal, nhg);
   return hipGetLastError();
 }
 
