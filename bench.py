@@ -83,7 +83,9 @@ class Workload:
         self.desc = pa.desc_for(self.q, self.k_pool, self.v_pool, self.table, layout=c.layout,
                                 partition_size=part, path=path, kv_shared=self.kv_shared)
         n = pa.workspace_size(self.desc)
-        self.ws = torch.empty(max(n, 256), dtype=torch.uint8, device="cuda")
+        # zeroed: the merged grid variant keeps arrival counters (zero between
+        # calls) at the start of its workspace
+        self.ws = torch.zeros(max(n, 256), dtype=torch.uint8, device="cuda")
         self.part = pa.partition_size(self.desc)
         self.path_name = pa.PATH_NAME[pa.resolved_path(self.desc)]
         self.kv_bytes = c.kv_bytes()
@@ -335,7 +337,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--also", type=str, default="3,5", help="comma-separated extra configs ('' for none)")
-    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "mfma_grid", "mfma_stream"])
+    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "mfma_grid", "mfma_stream",
+                                                   "mfma_fused"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", choices=["partition", "both", "copy", "prefill"], default=None)

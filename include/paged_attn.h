@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 /* Element type of the K and V caches. q and out are always float32. */
 typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype;
@@ -52,13 +52,26 @@ typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } 
  * KV head: batch * ceil(max_blocks_per_seq * block_size / 16) < 2^31), and
  * MFMA_GRID, one workgroup per partition (any block size and batch).
  * PA_PATH_MFMA picks MFMA_STREAM when it applies, else MFMA_GRID; AUTO picks
- * MFMA for 16-bit K/V and VALU for fp32. */
+ * MFMA for 16-bit K/V and VALU for fp32.
+ *
+ * MFMA_FUSED is MFMA_GRID with the partition merge done by the last partition
+ * workgroup of each (sequence, KV head) to finish, instead of by a second
+ * kernel (the single-launch variant of page "Paged Attention Kernel
+ * Architecture for BI-V100", section 2): one launch per call. Its workspace
+ * starts with batch * num_kv_heads int32 arrival counters (at offset 0), which
+ * must be zero when a call starts; every call leaves them zero, so zero the
+ * workspace once after allocating it (or after using it for anything else).
+ * Calls that share a workspace must not overlap in time. One wave reads all
+ * of a KV head's partition states, so it suits short contexts; it needs
+ * 2 * n_part * G + 16 <= 16 * head_dim, n_part = ceil(max_blocks_per_seq *
+ * block_size / partition_size) (else PA_E_PARTITION). */
 typedef enum pa_path {
   PA_PATH_AUTO = 0,
   PA_PATH_VALU = 1,
   PA_PATH_MFMA = 2,
   PA_PATH_MFMA_GRID = 3,
-  PA_PATH_MFMA_STREAM = 4
+  PA_PATH_MFMA_STREAM = 4,
+  PA_PATH_MFMA_FUSED = 5
 } pa_path;
 
 /* Status codes. */
@@ -75,7 +88,8 @@ typedef enum pa_path {
                               /* that is not a multiple of 16 bytes                  */
 #define PA_E_ALIGN (-7)       /* q, out, k_cache or v_cache not 16-byte aligned      */
 #define PA_E_PARTITION (-8)   /* partition_size not 0 and not a multiple of 32 in    */
-                              /* [32, 16384], or spanning more than 1024 blocks       */
+                              /* [32, 16384], or spanning more than 1024 blocks, or  */
+                              /* (MFMA_FUSED) 2 * n_part * G + 16 > 16 * head_dim    */
 #define PA_E_WORKSPACE (-9)   /* workspace NULL or smaller than required             */
 #define PA_E_PATH (-10)       /* path not a pa_path, an MFMA path asked for f32 K/V, */
                               /* or MFMA_STREAM asked for block_size < 16, batch     */
@@ -204,7 +218,8 @@ int paged_attn_decode_append(const pa_desc* desc, const void* q, const void* k_n
  * level 3 and section 6 phase 2) and reads only cache_seqlens and the
  * workspace. Calling the partition phase and then the combine phase on one
  * stream equals paged_attn_decode; the partition phase alone completes out only
- * when paged_attn_workspace_size() is 0. The combine phase is a no-op then.
+ * when paged_attn_workspace_size() is 0, or on PA_PATH_MFMA_FUSED (whose
+ * partition kernel merges too). The combine phase is a no-op then.
  */
 int paged_attn_partition_phase(const pa_desc* desc, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table,

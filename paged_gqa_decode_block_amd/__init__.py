@@ -21,6 +21,7 @@ from .block_manager import BlockManager, copy_blocks  # noqa: E402,F401
 
 _TORCH_DTYPE_NAME = {"torch.float32": "f32", "torch.float16": "f16", "torch.bfloat16": "bf16"}
 _ws_cache: dict = {}
+_ws_zero: dict = {}  # merged-grid workspaces: leading bytes known to be zero
 
 
 def _kv_dtype(t) -> str:
@@ -71,17 +72,29 @@ def _check_out(q, out):
 
 
 def workspace_for(desc: PaDesc, device):
-    """A cached device workspace of at least workspace_size(desc) bytes."""
+    """A cached device workspace of at least workspace_size(desc) bytes.
+
+    The merged-grid path (``mfma_fused``) gets a workspace of its own whose
+    leading batch * num_kv_heads int32 arrival counters are zero: allocated
+    zeroed, and zeroed again when a call needs more counters than the calls
+    before it left zero (each call leaves its own counters zero)."""
     import torch
 
     n = workspace_size(desc)
     if n == 0:
         return None
-    key = (str(device),)
+    fused = resolved_path(desc) == PA_PATH["mfma_fused"]
+    key = (str(device), fused)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < n:
-        ws = torch.empty(n, dtype=torch.uint8, device=device)
+        ws = (torch.zeros if fused else torch.empty)(n, dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
+        _ws_zero[key] = ws.numel() if fused else 0
+    if fused:
+        cnt_bytes = 4 * desc.batch * desc.num_kv_heads
+        if cnt_bytes > _ws_zero[key]:
+            ws[:cnt_bytes].zero_()
+        _ws_zero[key] = cnt_bytes
     return ws
 
 

@@ -13,8 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpagedattn.so")
 
 PA_DTYPE = {"f32": 0, "f16": 1, "bf16": 2}
-PA_PATH = {"auto": 0, "valu": 1, "mfma": 2, "mfma_grid": 3, "mfma_stream": 4}
-PATH_NAME = {1: "valu", 3: "mfma_grid", 4: "mfma_stream"}
+PA_PATH = {"auto": 0, "valu": 1, "mfma": 2, "mfma_grid": 3, "mfma_stream": 4, "mfma_fused": 5}
+PATH_NAME = {1: "valu", 3: "mfma_grid", 4: "mfma_stream", 5: "mfma_fused"}
 
 PA_OK = 0
 PA_E = {

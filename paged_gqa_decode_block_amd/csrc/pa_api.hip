@@ -63,9 +63,10 @@ int pick_path(const pa_desc* d) {
     case PA_PATH_MFMA:
     case PA_PATH_MFMA_GRID:
     case PA_PATH_MFMA_STREAM:
+    case PA_PATH_MFMA_FUSED:
       if (d->kv_dtype == PA_DTYPE_F32) return PA_E_PATH;
       if (!pa::mfma_supports(d->kv_dtype, d->head_dim, G)) return PA_E_SHAPE;
-      if (d->path == PA_PATH_MFMA_GRID) return PA_PATH_MFMA_GRID;
+      if (d->path == PA_PATH_MFMA_GRID || d->path == PA_PATH_MFMA_FUSED) return d->path;
       if (d->path == PA_PATH_MFMA_STREAM) return stream_ok ? PA_PATH_MFMA_STREAM : PA_E_PATH;
       return stream_ok ? PA_PATH_MFMA_STREAM : PA_PATH_MFMA_GRID;
   }
@@ -144,7 +145,7 @@ int validate(const pa_desc* d) {
   for (int i = 0; i < 6; ++i)
     if (st[i] <= 0 || (st[i] * eb) % 16) return PA_E_STRIDE;
   if (d->k_stride_token < d->head_dim || d->v_stride_token < d->head_dim) return PA_E_STRIDE;
-  if (d->path < PA_PATH_AUTO || d->path > PA_PATH_MFMA_STREAM) return PA_E_PATH;
+  if (d->path < PA_PATH_AUTO || d->path > PA_PATH_MFMA_FUSED) return PA_E_PATH;
   if ((d->flags & ~(PA_FLAG_KV_SHARED | PA_FLAG_QO_BF16)) || d->reserved) return PA_E_SHAPE;
   if (d->partition_size != 0) {
     const int ps = d->partition_size;
@@ -154,15 +155,26 @@ int validate(const pa_desc* d) {
   // the partition index is grid dimension y
   if ((max_tokens(d) + pick_partition(d) - 1) / pick_partition(d) > 65535) return PA_E_PARTITION;
   const int path = pick_path(d);
-  return path < 0 ? path : PA_OK;
+  if (path < 0) return path;
+  // the merged variant keeps every partition's max, sum and weight in LDS
+  if (path == PA_PATH_MFMA_FUSED) {
+    const int part = pick_partition(d);
+    const int64_t pmax = (max_tokens(d) + part - 1) / part;
+    if (2 * pmax * (d->num_q_heads / d->num_kv_heads) + 16 > pa::fused_merge_capacity(d->head_dim))
+      return PA_E_PARTITION;
+  }
+  return PA_OK;
 }
 
 // Workspace regions of a valid descriptor, as byte offsets (each 256-byte
-// aligned; off[kWsParts] is the total): partition states m, l, acc for every
-// (sequence, query head, partition), then for the streaming kernel the
-// partition links and one continuation state per wave. Kernels other than the
-// streaming one need nothing when one partition always suffices.
-enum { kWsM, kWsL, kWsAcc, kWsLink, kWsCm, kWsCl, kWsCacc, kWsCmore, kWsParts };
+// aligned; off[kWsParts] is the total): for the merged grid variant first an
+// arrival word per (sequence, KV head) (at offset 0 for every descriptor; zero
+// before the first call and left zero by every call), then partition states
+// m, l, acc for every (sequence, query head, partition), then for the
+// streaming kernel the partition links and one continuation state per wave.
+// Kernels other than the streaming one need nothing when one partition always
+// suffices.
+enum { kWsCnt, kWsM, kWsL, kWsAcc, kWsLink, kWsCm, kWsCl, kWsCacc, kWsCmore, kWsParts };
 void workspace_layout(const pa_desc* d, size_t* off) {
   const int part = pick_partition(d);
   const int64_t pmax = (max_tokens(d) + part - 1) / part;
@@ -181,6 +193,8 @@ void workspace_layout(const pa_desc* d, size_t* off) {
     sz[kWsCacc] = waves * G * d->head_dim * sizeof(float);
     sz[kWsCmore] = waves * sizeof(int32_t);
   }
+  if (pick_path(d) == PA_PATH_MFMA_FUSED && pmax > 1)
+    sz[kWsCnt] = (size_t)d->batch * d->num_kv_heads * sizeof(int32_t);
   off[0] = 0;
   for (int i = 0; i < kWsParts; ++i) off[i + 1] = off[i] + align256(sz[i]);
 }
@@ -236,7 +250,7 @@ const char* paged_attn_strerror(int status) {
     case PA_E_DTYPE: return "kv_dtype must be PA_DTYPE_F32, PA_DTYPE_F16 or PA_DTYPE_BF16";
     case PA_E_STRIDE: return "K/V strides must be positive multiples of 16 bytes, token stride >= head_dim";
     case PA_E_ALIGN: return "q, out, k_cache and v_cache must be 16-byte aligned";
-    case PA_E_PARTITION: return "partition_size must be 0 or a multiple of 32 in [32, 16384] spanning <= 1022 blocks";
+    case PA_E_PARTITION: return "partition_size must be 0 or a multiple of 32 in [32, 16384] spanning <= 1022 blocks (MFMA_FUSED: 2 * n_part * G + 16 <= 16 * head_dim)";
     case PA_E_WORKSPACE: return "workspace missing or smaller than paged_attn_workspace_size()";
     case PA_E_PATH: return "path must be a pa_path; the MFMA path needs f16 or bf16 K/V";
     case PA_E_LAUNCH: return "the HIP runtime refused a kernel launch";
@@ -311,6 +325,7 @@ int prepare(const pa_desc* desc, const void* q, const void* k_cache, const void*
       p.ws_cmore = (int32_t*)(ws + off[kWsCmore]);
       p.nwaves = stream_waves(desc);
     }
+    if (pick_path(desc) == PA_PATH_MFMA_FUSED && p.pmax > 1) p.ws_cnt = (int32_t*)(ws + off[kWsCnt]);
   }
   return PA_OK;
 }
@@ -322,7 +337,8 @@ int run_partition(const pa_desc* desc, const pa::Params& p, hipStream_t s) {
       e = pa::launch_partition_stream(p, desc->kv_dtype, stream_variant_for(desc),
                                       !(desc->flags & PA_FLAG_KV_SHARED) && stream_nt(), s);
       break;
-    case PA_PATH_MFMA_GRID: e = pa::launch_partition_mfma(p, desc->kv_dtype, s); break;
+    case PA_PATH_MFMA_GRID:
+    case PA_PATH_MFMA_FUSED: e = pa::launch_partition_mfma(p, desc->kv_dtype, s); break;
     default: e = pa::launch_partition_valu(p, desc->kv_dtype, s); break;
   }
   return e == hipSuccess ? PA_OK : PA_E_LAUNCH;
@@ -330,8 +346,8 @@ int run_partition(const pa_desc* desc, const pa::Params& p, hipStream_t s) {
 
 int run_combine(const pa::Params& p, hipStream_t s) {
   // without links (kernels other than the streaming one) a single partition
-  // was written out already
-  if (p.pmax <= 1 && !p.ws_link) return PA_OK;
+  // was written out already; the merged grid variant has no second kernel
+  if ((p.pmax <= 1 && !p.ws_link) || p.ws_cnt) return PA_OK;
   return pa::launch_combine(p, s) == hipSuccess ? PA_OK : PA_E_LAUNCH;
 }
 

@@ -28,6 +28,9 @@ struct Params {
   float* ws_cl;             // [waves, G]
   float* ws_cacc;           // [waves, G, D]
   int32_t* ws_cmore;        // [waves] 1 when the partition goes on into the next wave
+  // grid kernel with the merge in its last block (NULL otherwise): arrivals per
+  // (sequence, KV head), zero between calls
+  int32_t* ws_cnt;          // [B, Hkv]
   int32_t* status;          // optional
   int64_t ksb, ksh, kst;    // K strides (elements)
   int64_t vsb, vsh, vst;    // V strides
@@ -86,6 +89,9 @@ __host__ __device__ inline int stream_active_waves32(int n_chunks, int grid, int
 }
 bool valu_supports(int dtype, int D, int G);
 bool mfma_supports(int dtype, int D, int G);
+// Floats of LDS the grid kernel's merged variant has for 2 n_part G + 16 of
+// merge state.
+int fused_merge_capacity(int D);
 
 #if defined(__HIPCC__)
 

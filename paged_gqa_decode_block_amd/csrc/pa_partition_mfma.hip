@@ -24,6 +24,18 @@
 // when the sequence has one partition, the normalised output goes straight to
 // out. Tokens at or past L_b and tokens whose table entry is invalid are never
 // loaded; their scores are -inf.
+//
+// Merged variant (one launch): the same page, section 2, lets the last
+// partition block to finish do the merge instead of a second kernel. Every
+// block of a multi-partition sequence publishes its state with write-through
+// stores that are coherent across the device's L2 caches, waits for them to
+// complete, and counts itself in on a per-(sequence, KV head) arrival word. The
+// block that arrives last resets the word to zero for the next call and folds
+// the G x n_part states with the max-rescaling combine, reading them with loads
+// that see the other L2s' writes (no cache write-back or invalidate is needed).
+// One wave reads all of a KV head's states, so this pays off for short
+// contexts (few partitions) and loses to the separate combine kernel for long
+// ones.
 #include "pa_kernels.h"
 
 namespace pa {
@@ -71,13 +83,164 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 
+// Cache-policy bit of the merged variant's workspace traffic: stores write
+// through to memory and loads see what other L2s wrote (device scope).
+constexpr int kSc1 = 16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [ptr, ptr + bytes) (uniform across the wave); an
+// offset at or past `bytes` loads zeros and stores nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* ptr, int bytes) {
+  const uint64_t a = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// Merged variant, after the partition loop of partition `part` of
+// (sequence b, KV head hk): publish this block's states (lane (q, r): head r,
+// dims 16 mb + 4 q .. +3), count in, and if this block is the last of the
+// n_part to arrive, write out = sum_p w_p acc_p / sum_p w_p l_p with
+// w_p = 2^(m_p - max_p m_p) for the G heads. s_f: 16 D floats of LDS, at least
+// 2 n_part G + 16 of them (checked on the host).
+template <int D>
+__device__ __forceinline__ void publish_and_merge(const Params& p, int b, int hk, int part,
+                                                  int npart, const f32x4 (&acc)[D / 16], float m,
+                                                  float l, float* s_f) {
+  constexpr int MB = D / 16;
+  const int lane = threadIdx.x, r = lane & 15, q = lane >> 4;
+  const int G = p.G, pm = p.pmax;
+  // the KV head's states: head g, partition i at row g * pmax + i
+  const int64_t row0 = ((int64_t)b * p.Hq + (int64_t)hk * G) * pm;
+  const int nacc = G * pm * D * 4;
+  const __amdgpu_buffer_rsrc_t racc = ws_rsrc(p.ws_acc + row0 * D, nacc);
+  const __amdgpu_buffer_rsrc_t rm = ws_rsrc(p.ws_m + row0, G * pm * 4);
+  const __amdgpu_buffer_rsrc_t rl = ws_rsrc(p.ws_l + row0, G * pm * 4);
+  if (r < G) {
+    const int o = ((r * pm + part) * D + 4 * q) * 4;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[mb]), racc, o + 64 * mb,
+                                             0, kSc1);
+    if (q == 0) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), rm, (r * pm + part) * 4, 0, kSc1);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rl, (r * pm + part) * 4, 0, kSc1);
+    }
+  }
+  // All of this wave's stores have completed (and, written through, are visible
+  // device-wide) before it counts in.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int32_t* cnt = p.ws_cnt + (b * p.Hkv + hk);
+  int prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev != npart - 1) return;
+  // last to arrive: every other block's states were complete before it counted in
+  if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+
+  // Pass 1, lane (q, r) for head r: m and l of partitions i = q (mod 4) into
+  // LDS (16 per lane per round, loads in flight together), the head's max.
+  float* s_m = s_f;             // [n_part][G], then the weights w
+  float* s_l = s_f + npart * G;  // [n_part][G]
+  float* s_L = s_l + npart * G;  // [G] sum_p w_p l_p
+  float mx = -INFINITY;
+  for (int i0 = 0; i0 < npart; i0 += 64) {
+    float mv[16], lv[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int i = i0 + 4 * k + q;
+      const int o = (r < G && i < npart) ? (r * pm + i) * 4 : G * pm * 4;  // past the end: 0
+      mv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, o, 0, kSc1));
+      lv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, o, 0, kSc1));
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int i = i0 + 4 * k + q;
+      if (r < G && i < npart) {
+        s_m[i * G + r] = mv[k];
+        s_l[i * G + r] = lv[k];
+        mx = fmaxf(mx, mv[k]);
+      }
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mu = mx == -INFINITY ? 0.f : mx;
+  float ls = 0.f;
+  if (r < G) {
+    for (int i = q; i < npart; i += 4) {
+      const float w = exp2_fast(s_m[i * G + r] - mu);
+      s_m[i * G + r] = w;
+      ls += w * s_l[i * G + r];
+    }
+  }
+  ls += __shfl_xor(ls, 16);
+  ls += __shfl_xor(ls, 32);
+  if (r < G && q == 0) s_L[r] = ls;
+  __syncthreads();
+
+  // Pass 2: slot s = (head s / (D/4), dims 4 (s % (D/4)) .. +3); each lane
+  // folds 4 slots over 8 partitions per round (32 16-byte loads in flight).
+  constexpr int SPH = D / 4;  // slots per head
+  const int nslot = G * SPH;
+  for (int s0 = 0; s0 < nslot; s0 += 4 * 64) {
+    int hs[4], ob[4];
+    bool sv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sl = s0 + 64 * u + lane;
+      sv[u] = sl < nslot;
+      hs[u] = sv[u] ? sl / SPH : 0;
+      ob[u] = (hs[u] * pm * D + 4 * (sl % SPH)) * 4;
+    }
+    float4 a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i0 = 0; i0 < npart; i0 += 8) {
+      u32x4 x[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int i = i0 + k;
+          const int o = (sv[u] && i < npart) ? ob[u] + i * D * 4 : nacc;  // past the end: 0
+          x[u][k] = __builtin_amdgcn_raw_buffer_load_b128(racc, o, 0, kSc1);
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          // a partition past n_part loaded zeros; its (clamped) weight is finite
+          const float w = s_m[min(i0 + k, npart - 1) * G + hs[u]];
+          a[u].x += w * __uint_as_float(x[u][k][0]);
+          a[u].y += w * __uint_as_float(x[u][k][1]);
+          a[u].z += w * __uint_as_float(x[u][k][2]);
+          a[u].w += w * __uint_as_float(x[u][k][3]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (!sv[u]) continue;
+      const float tot = s_L[hs[u]];
+      const float inv = tot > 0.f ? 1.f / tot : 0.f;
+      const int sl = s0 + 64 * u + lane;
+      store_out4(p, ((int64_t)b * p.Hq + hk * G + hs[u]) * D + 4 * (sl % SPH), a[u].x * inv,
+                 a[u].y * inv, a[u].z * inv, a[u].w * inv);
+    }
+  }
+}
+
 // Waves per SIMD the register allocation is held to: 2 for d <= 128, 1 for d = 256.
 template <int D>
 struct Occ {
   static constexpr int waves = D <= 128 ? 2 : 1;
 };
 
-template <typename T, int D>
+template <typename T, int D, bool FUSED>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Occ<D>::waves)))
 partition_mfma_kernel(Params p) {
   typedef typename Mma<T>::vec V8;
@@ -299,6 +462,13 @@ partition_mfma_kernel(Params p) {
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
 
+  if constexpr (FUSED) {
+    if (npart > 1) {
+      __syncthreads();  // the V tile's LDS is reused by the merge
+      publish_and_merge<D>(p, b, hk, part, npart, acc, m, l, (float*)s_v);
+      return;
+    }
+  }
   if (r >= G) return;
   const int h = hk * G + r;
   if (npart == 1) {
@@ -325,7 +495,10 @@ partition_mfma_kernel(Params p) {
 template <typename T, int D>
 hipError_t launch_t(const Params& p, hipStream_t s) {
   dim3 grid(p.B * p.Hkv, p.pmax);
-  hipLaunchKernelGGL((partition_mfma_kernel<T, D>), grid, dim3(64), 0, s, p);
+  if (p.ws_cnt)
+    hipLaunchKernelGGL((partition_mfma_kernel<T, D, true>), grid, dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL((partition_mfma_kernel<T, D, false>), grid, dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -340,6 +513,8 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
 }
 
 }  // namespace
+
+int fused_merge_capacity(int D) { return 16 * D; }
 
 bool mfma_supports(int dtype, int D, int G) {
   return (dtype == 1 || dtype == 2) && (D == 64 || D == 128 || D == 256) && G >= 1 && G <= 16;

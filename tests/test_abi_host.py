@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), f"{name} not exported"
-    assert lib.paged_attn_abi_version() == 2
+    assert lib.paged_attn_abi_version() == 3
 
 
 def test_descriptor_layout_matches_c(tmp_path):
@@ -89,7 +89,11 @@ def test_valid_descriptor_and_resolved_path():
     (dict(partition_size=32768), -8),
     (dict(block_size=1, partition_size=2048), -8),  # spans more than the block-id table
     (dict(path=9), -10),
-    (dict(path=5), -10),
+    (dict(path=6), -10),
+    (dict(kv_dtype="f32", k_strides=(4096, 2048, 128), path="mfma_fused"), -10),
+    # the merged grid variant's LDS bound: 2 * 32 partitions * G 16 + 16 > 16 * 64
+    (dict(head_dim=64, k_strides=(2048, 1024, 64), num_q_heads=32, max_blocks_per_seq=64,
+          partition_size=32, path="mfma_fused"), -8),
     (dict(kv_dtype="f32", k_strides=(4096, 2048, 128), path="mfma"), -10),
     (dict(kv_dtype="f32", k_strides=(4096, 2048, 128), path="mfma_stream"), -10),
     (dict(block_size=8, k_strides=(2048, 1024, 128), path="mfma_stream"), -10),
@@ -132,6 +136,17 @@ def test_partition_size_choice_and_workspace():
     pmax = 256 // 64
     rows = 2 * 8 * pmax
     assert pa.workspace_size(d) == 2 * _al(rows * 4) + _al(rows * 128 * 4)
+    # the merged grid variant: arrival counters first (offset 0), then the states;
+    # nothing when one partition suffices; resolved as asked
+    d = _desc(partition_size=64, path="mfma_fused")
+    assert pa.PATH_NAME[pa.resolved_path(d)] == "mfma_fused"
+    assert pa.workspace_size(d) == _al(2 * 2 * 4) + 2 * _al(rows * 4) + _al(rows * 128 * 4)
+    assert pa.workspace_size(_desc(partition_size=512, path="mfma_fused")) == 0
+    # the LDS bound at its edge: 2 * 32 * 16 + 16 = 1040 > 1024, 2 * 31 * 16 + 16 = 1008
+    edge = dict(head_dim=64, k_strides=(2048, 1024, 64), num_q_heads=32, partition_size=32,
+                path="mfma_fused")
+    assert pa.validate(_desc(max_blocks_per_seq=62, **edge)) == 0
+    assert pa.validate(_desc(max_blocks_per_seq=64, **edge)) == -8
     # the streaming kernel: partition states, links, one continuation state per wave
     for part, mbs, batch in ((512, 16, 2), (64, 16, 2), (512, 2048, 64)):
         d = _desc(partition_size=part, max_blocks_per_seq=mbs, batch=batch)
