@@ -51,7 +51,7 @@ def kernel_hash() -> str:
 class Workload:
     """One generated configuration, copied to the GPU once."""
 
-    def __init__(self, k: int, torch, path: str):
+    def __init__(self, k: int, torch, path: str, partition: int | None = None):
         from paged_gqa_decode_block_amd import workload as W
         import paged_gqa_decode_block_amd as pa
 
@@ -80,6 +80,8 @@ class Workload:
         # several sequences (reference counts > 1): keep K/V loads cacheable
         self.kv_shared = c.ref_count is not None and int(c.ref_count.max()) > 1
         part = c.partition_size if k == 3 else 0  # the 100K-token workload fixes 512
+        if partition is not None:
+            part = partition
         self.desc = pa.desc_for(self.q, self.k_pool, self.v_pool, self.table, layout=c.layout,
                                 partition_size=part, path=path, kv_shared=self.kv_shared)
         n = pa.workspace_size(self.desc)
@@ -339,6 +341,9 @@ def main():
     ap.add_argument("--also", type=str, default="3,5", help="comma-separated extra configs ('' for none)")
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "mfma_grid", "mfma_stream",
                                                    "mfma_fused"])
+    ap.add_argument("--partition", type=int, default=None,
+                    help="partition size of every decode workload (default: the library's "
+                         "choice, 512 for the 100K-token workload)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", choices=["partition", "both", "copy", "prefill"], default=None)
@@ -371,7 +376,7 @@ def main():
         measure_prefill(1, torch, a.steps, a.warmup)
         return
 
-    wl = Workload(a.config, torch, a.path)
+    wl = Workload(a.config, torch, a.path, a.partition)
     if a.profile is not None:
         for _ in range(a.warmup):
             wl.call()
@@ -393,7 +398,7 @@ def main():
     for k in [int(x) for x in a.also.split(",") if x.strip()]:
         if k == a.config:
             continue
-        w2 = Workload(k, torch, a.path)
+        w2 = Workload(k, torch, a.path, a.partition)
         r2 = measure(w2, a.steps, a.warmup, flush_buf)
         log(f"[bench] {w2.case.name}: {r2['ms_per_step'] * 1e3:.1f} us/step, {r2['kv_gbs']:.0f} GB/s")
         also[w2.case.name] = {**w2.describe(), **{k2: (round(v, 4) if isinstance(v, float) else v)

@@ -31,13 +31,31 @@ int stream_variant_for(const pa_desc* d);
 // Partition size for a descriptor that passed validation of everything else.
 // Without a caller choice: 4096 tokens for the streaming kernel (its waves
 // split the work by chunks, so the partition size only sets how many partial
-// states are written and merged); for the other kernels 512, halved (down to
-// 64) while the busiest possible grid would hold fewer than 1024 work items.
+// states are written and merged); for the merged grid variant the rule below;
+// for the other kernels 512, halved (down to 64) while the busiest possible
+// grid would hold fewer than 1024 work items.
 int pick_partition(const pa_desc* d) {
   if (d->partition_size > 0) return d->partition_size;
   const int64_t T = max_tokens(d);
   if (pick_path(d) == PA_PATH_MFMA_STREAM) {
     int part = 4096;
+    while ((part >> ilog2(d->block_size)) + 2 > pa::kTableCap && part > 32) part >>= 1;
+    return part;
+  }
+  if (pick_path(d) == PA_PATH_MFMA_FUSED) {
+    // Fewer, longer partitions: the merge reads every partition state of a KV
+    // head in one wave. 1024, halved while the busiest grid would hold fewer
+    // than 1024 work items but not below min(1024, max_tokens / 16), then
+    // doubled while the merge state would not fit in LDS.
+    const int64_t lo = T / 16 < 1024 ? T / 16 : 1024;
+    const int G = d->num_q_heads / d->num_kv_heads;
+    int part = 1024;
+    while (part > 64 && part / 2 >= lo &&
+           (int64_t)d->batch * d->num_kv_heads * ((T + part - 1) / part) < 1024)
+      part >>= 1;
+    while (part < 16384 &&
+           2 * ((T + part - 1) / part) * G + 16 > pa::fused_merge_capacity(d->head_dim))
+      part <<= 1;
     while ((part >> ilog2(d->block_size)) + 2 > pa::kTableCap && part > 32) part >>= 1;
     return part;
   }

@@ -147,6 +147,22 @@ def test_partition_size_choice_and_workspace():
                 path="mfma_fused")
     assert pa.validate(_desc(max_blocks_per_seq=62, **edge)) == 0
     assert pa.validate(_desc(max_blocks_per_seq=64, **edge)) == -8
+    # automatic partition of the merged variant: 1024, halved while the grid is
+    # small but not below min(1024, max_tokens / 16), doubled to fit the LDS bound
+    fz = dict(path="mfma_fused", partition_size=0)
+    assert pa.partition_size(_desc(batch=8, num_q_heads=14, num_kv_heads=2, head_dim=64,
+                                   k_strides=(2048, 1024, 64), max_blocks_per_seq=256, **fz)) == 256
+    assert pa.partition_size(_desc(batch=64, num_q_heads=64, num_kv_heads=8,
+                                   k_strides=(16 * 16 * 128, 16 * 128, 128),
+                                   max_blocks_per_seq=2048, **fz)) == 1024
+    assert pa.partition_size(_desc(max_blocks_per_seq=4, **fz)) == 64   # 64 tokens
+    # 1 x 4 heads, 100000 tokens: 1024 is the floor; G = 16 at d = 64 needs more
+    assert pa.partition_size(_desc(batch=1, num_q_heads=24, num_kv_heads=4, head_dim=256,
+                                   k_strides=(4 * 16 * 256, 16 * 256, 256),
+                                   max_blocks_per_seq=6250, **fz)) == 1024
+    assert pa.partition_size(_desc(batch=1, num_q_heads=32, num_kv_heads=2, head_dim=64,
+                                   k_strides=(2048, 1024, 64), max_blocks_per_seq=6250,
+                                   **fz)) == 4096
     # the streaming kernel: partition states, links, one continuation state per wave
     for part, mbs, batch in ((512, 16, 2), (64, 16, 2), (512, 2048, 64)):
         d = _desc(partition_size=part, max_blocks_per_seq=mbs, batch=batch)
