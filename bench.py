@@ -51,7 +51,8 @@ def kernel_hash() -> str:
 class Workload:
     """One generated configuration, copied to the GPU once."""
 
-    def __init__(self, k: int, torch, path: str, partition: int | None = None):
+    def __init__(self, k: int, torch, path: str, partition: int | None = None,
+                 layout: str = "HND"):
         from paged_gqa_decode_block_amd import workload as W
         import paged_gqa_decode_block_amd as pa
 
@@ -71,8 +72,13 @@ class Workload:
             return x.to("cuda")[1:]
 
         self.q = torch.from_numpy(c.q).to("cuda")
-        self.k_pool = pool(c.k_store)
-        self.v_pool = pool(c.v_store)
+        if layout == "XPACKED":  # the same values, x-packed K / transposed V
+            self.k_pool = pool(W.to_xpacked(c.k_store, "k"))
+            self.v_pool = pool(W.to_xpacked(c.v_store, "v"))
+        else:
+            self.k_pool = pool(c.k_store)
+            self.v_pool = pool(c.v_store)
+        self.layout = layout if layout == "XPACKED" else c.layout
         self.table = torch.from_numpy(c.block_table).to("cuda")
         self.seqlens = torch.from_numpy(c.seqlens).to("cuda")
         self.out = torch.empty_like(self.q)
@@ -82,7 +88,7 @@ class Workload:
         part = c.partition_size if k == 3 else 0  # the 100K-token workload fixes 512
         if partition is not None:
             part = partition
-        self.desc = pa.desc_for(self.q, self.k_pool, self.v_pool, self.table, layout=c.layout,
+        self.desc = pa.desc_for(self.q, self.k_pool, self.v_pool, self.table, layout=self.layout,
                                 partition_size=part, path=path, kv_shared=self.kv_shared)
         n = pa.workspace_size(self.desc)
         # zeroed: the merged grid variant keeps arrival counters (zero between
@@ -109,7 +115,7 @@ class Workload:
         c = self.case
         return {
             "workload": c.name, "batch": c.B, "num_q_heads": c.Hq, "num_kv_heads": c.Hkv,
-            "head_dim": c.D, "block_size": c.bs, "kv_dtype": c.kv_dtype, "layout": c.layout,
+            "head_dim": c.D, "block_size": c.bs, "kv_dtype": c.kv_dtype, "layout": self.layout,
             "partition_size": self.part, "path": self.path_name, "kv_shared": self.kv_shared,
             "total_cached_tokens": int(c.seqlens.astype(np.int64).sum()),
             "num_physical_blocks": c.NB, "seed": 1000 + self.k,
@@ -190,7 +196,10 @@ def measure_append_graph(wl: Workload, steps: int) -> dict:
     t = (L - 1).clamp(min=0)
     blk = wl.table.long().gather(1, (t // c.bs).unsqueeze(1)).squeeze(1).clamp(min=0)
     off = t % c.bs
-    if c.layout == "HND":
+    if wl.layout == "XPACKED":  # K [NB, H, d/8, bs, 8], V [NB, H, d, bs]
+        kn = wl.k_pool[blk, :, :, off, :].reshape(c.B, c.Hkv, c.D)
+        vn = wl.v_pool[blk, :, :, off]
+    elif c.layout == "HND":
         kn, vn = wl.k_pool[blk, :, off, :], wl.v_pool[blk, :, off, :]
     else:
         kn, vn = wl.k_pool[blk, off, :, :], wl.v_pool[blk, off, :, :]
@@ -199,7 +208,7 @@ def measure_append_graph(wl: Workload, steps: int) -> dict:
 
     def step():
         pa.paged_attn_decode_append(wl.q, kn, vn, wl.k_pool, wl.v_pool, wl.table, Lm1, c.scale, out,
-                                    layout=c.layout, partition_size=wl.part, path=wl.path,
+                                    layout=wl.layout, partition_size=wl.part, path=wl.path,
                                     workspace=wl.ws, kv_shared=wl.kv_shared)
 
     step()
@@ -344,6 +353,9 @@ def main():
     ap.add_argument("--partition", type=int, default=None,
                     help="partition size of every decode workload (default: the library's "
                          "choice, 512 for the 100K-token workload)")
+    ap.add_argument("--layout", default="HND", choices=["HND", "XPACKED"],
+                    help="K/V cache layout of the decode workloads (XPACKED: K [NB, H_kv, d/8, "
+                         "bs, 8], V [NB, H_kv, d, bs], the same values)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", choices=["partition", "both", "copy", "prefill"], default=None)
@@ -376,7 +388,7 @@ def main():
         measure_prefill(1, torch, a.steps, a.warmup)
         return
 
-    wl = Workload(a.config, torch, a.path, a.partition)
+    wl = Workload(a.config, torch, a.path, a.partition, a.layout)
     if a.profile is not None:
         for _ in range(a.warmup):
             wl.call()
@@ -398,7 +410,7 @@ def main():
     for k in [int(x) for x in a.also.split(",") if x.strip()]:
         if k == a.config:
             continue
-        w2 = Workload(k, torch, a.path, a.partition)
+        w2 = Workload(k, torch, a.path, a.partition, a.layout)
         r2 = measure(w2, a.steps, a.warmup, flush_buf)
         log(f"[bench] {w2.case.name}: {r2['ms_per_step'] * 1e3:.1f} us/step, {r2['kv_gbs']:.0f} GB/s")
         also[w2.case.name] = {**w2.describe(), **{k2: (round(v, 4) if isinstance(v, float) else v)

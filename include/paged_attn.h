@@ -85,7 +85,9 @@ typedef enum pa_path {
 #define PA_E_BLOCK_SIZE (-4)  /* block_size not a power of two in [1, 1024]          */
 #define PA_E_DTYPE (-5)       /* kv_dtype not a pa_dtype                             */
 #define PA_E_STRIDE (-6)      /* a stride <= 0, token stride < head_dim, or a stride */
-                              /* that is not a multiple of 16 bytes                  */
+                              /* that is not a multiple of 16 bytes (with            */
+                              /* PA_FLAG_KV_XPACKED: token strides not x and 1, or a */
+                              /* head stride < block_size * head_dim)                */
 #define PA_E_ALIGN (-7)       /* q, out, k_cache or v_cache not 16-byte aligned      */
 #define PA_E_PARTITION (-8)   /* partition_size not 0 and not a multiple of 32 in    */
                               /* [32, 16384], or spanning more than 1024 blocks, or  */
@@ -109,6 +111,18 @@ typedef enum pa_path {
 #define PA_FLAG_QO_BF16 2    /* q and out are bf16 instead of fp32 (accumulation,     */
                              /* partial states and the combine stay fp32; out is      */
                              /* rounded to nearest even once, at the end)             */
+#define PA_FLAG_KV_XPACKED 4 /* the cache layout of page "Paged Attention Kernel      */
+                             /* Architecture for BI-V100", section 3: K is            */
+                             /* [num_blocks, num_kv_heads, d/x, block_size, x] with   */
+                             /* x = 16 bytes / element size, V is                     */
+                             /* [num_blocks, num_kv_heads, d, block_size]. Block and  */
+                             /* head strides come from the descriptor; each (block,   */
+                             /* head) tile is dense, so k_stride_token must be x and  */
+                             /* v_stride_token 1, and head strides >= block_size * d. */
+                             /* f16/bf16 K/V and block_size >= 8 only. Decode runs on */
+                             /* MFMA_GRID or MFMA_FUSED (AUTO and MFMA pick           */
+                             /* MFMA_GRID); VALU, MFMA_STREAM and paged_attn_prefill  */
+                             /* return PA_E_PATH. Append and copy_blocks accept it.   */
 
 /* Bits the kernels OR into the optional device status word. */
 #define PA_STATUS_BAD_BLOCK 1   /* an attended token's table entry was outside [0, NB) */

@@ -10,7 +10,7 @@ call. Build the library with ``python -m paged_gqa_decode_block_amd.build``.
 from __future__ import annotations
 
 from ._lib import (  # noqa: F401
-    EXPORTED, LIB_PATH, PA_DTYPE, PA_FLAG_KV_SHARED, PA_FLAG_QO_BF16, PA_PATH, PA_STATUS_BAD_BLOCK,
+    EXPORTED, LIB_PATH, PA_DTYPE, PA_FLAG_KV_SHARED, PA_FLAG_KV_XPACKED, PA_FLAG_QO_BF16, PA_PATH, PA_STATUS_BAD_BLOCK,
     PA_STATUS_BAD_SEQLEN, PATH_NAME,
     PaDesc, PagedAttnError, check_inputs, decode_append_raw, decode_raw, load_library, make_desc,
     partition_size, prefill_raw,
@@ -34,9 +34,27 @@ def _kv_dtype(t) -> str:
 def desc_for(q, k_cache, v_cache, block_table, *, layout="HND", partition_size=0, path="auto",
              kv_shared=False):
     """Descriptor for torch tensors. ``k_cache``/``v_cache`` are [NB, H_kv, bs, d]
-    ("HND") or [NB, bs, H_kv, d] ("NHD"), any strides with d contiguous.
+    ("HND") or [NB, bs, H_kv, d] ("NHD"), any strides with d contiguous; or
+    "XPACKED": K [NB, H_kv, d/x, bs, x] with x = 16 bytes / element and V
+    [NB, H_kv, d, bs], dense within each (block, head) tile.
     ``kv_shared`` says physical blocks may be listed by several sequences."""
     B, Hq, D = q.shape
+    if layout == "XPACKED":
+        NB, Hkv, dx, bs, x = k_cache.shape
+        if x * k_cache.element_size() != 16 or dx * x != D:
+            raise ValueError("x-packed k_cache must be [NB, H_kv, d/x, bs, x], x = 16 bytes / element")
+        if tuple(v_cache.shape) != (NB, Hkv, D, bs):
+            raise ValueError("x-packed v_cache must be [NB, H_kv, d, bs]")
+        if (k_cache.stride(4), k_cache.stride(3), k_cache.stride(2)) != (1, x, bs * x) or \
+                (v_cache.stride(3), v_cache.stride(2)) != (1, bs):
+            raise ValueError("x-packed K/V tiles must be dense within each (block, head)")
+        return make_desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                         num_blocks=NB, max_blocks_per_seq=block_table.shape[1],
+                         kv_dtype=_kv_dtype(k_cache),
+                         k_strides=(k_cache.stride(0), k_cache.stride(1), x),
+                         v_strides=(v_cache.stride(0), v_cache.stride(1), 1),
+                         partition_size=partition_size, path=path, kv_shared=kv_shared,
+                         qo_bf16=str(q.dtype) == "torch.bfloat16", xpacked=True)
     if layout == "HND":
         NB, Hkv, bs, D2 = k_cache.shape
         ks = (k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
@@ -46,7 +64,7 @@ def desc_for(q, k_cache, v_cache, block_table, *, layout="HND", partition_size=0
         ks = (k_cache.stride(0), k_cache.stride(2), k_cache.stride(1))
         vs = (v_cache.stride(0), v_cache.stride(2), v_cache.stride(1))
     else:
-        raise ValueError(f"layout must be 'HND' or 'NHD', got {layout!r}")
+        raise ValueError(f"layout must be 'HND', 'NHD' or 'XPACKED', got {layout!r}")
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("q, k_cache and v_cache disagree on shape")
     if k_cache.stride(3) != 1 or v_cache.stride(3) != 1:
@@ -152,7 +170,7 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cac
     if not q.is_cuda:
         raise ValueError("paged_attn_decode_append runs on the GPU; q is on the CPU")
     B, Hq, D = q.shape
-    Hkv = k_cache.shape[1] if layout == "HND" else k_cache.shape[2]
+    Hkv = k_cache.shape[2] if layout == "NHD" else k_cache.shape[1]
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         if t.dtype != k_cache.dtype or tuple(t.shape) != (B, Hkv, D) or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [B, H_kv, d] tensor of the cache's dtype")

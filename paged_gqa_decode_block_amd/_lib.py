@@ -25,6 +25,7 @@ PA_E = {
 }
 PA_FLAG_KV_SHARED = 1
 PA_FLAG_QO_BF16 = 2
+PA_FLAG_KV_XPACKED = 4
 PA_STATUS_BAD_BLOCK = 1
 PA_STATUS_BAD_SEQLEN = 2
 
@@ -143,7 +144,7 @@ def strerror(code: int) -> str:
 
 def make_desc(*, batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
               max_blocks_per_seq, kv_dtype, k_strides, v_strides=None, partition_size=0,
-              path="auto", kv_shared=False, qo_bf16=False) -> PaDesc:
+              path="auto", kv_shared=False, qo_bf16=False, xpacked=False) -> PaDesc:
     v_strides = k_strides if v_strides is None else v_strides
     return PaDesc(
         int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
@@ -151,7 +152,8 @@ def make_desc(*, batch, num_q_heads, num_kv_heads, head_dim, block_size, num_blo
         PA_DTYPE[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype),
         *[int(x) for x in k_strides], *[int(x) for x in v_strides], int(partition_size),
         PA_PATH[path] if isinstance(path, str) else int(path),
-        (PA_FLAG_KV_SHARED if kv_shared else 0) | (PA_FLAG_QO_BF16 if qo_bf16 else 0), 0)
+        (PA_FLAG_KV_SHARED if kv_shared else 0) | (PA_FLAG_QO_BF16 if qo_bf16 else 0)
+        | (PA_FLAG_KV_XPACKED if xpacked else 0), 0)
 
 
 def validate(desc: PaDesc) -> int:

@@ -101,8 +101,8 @@ def copy_blocks(k_cache, v_cache, pairs, *, layout="HND", status=None, stream=No
     if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2 or not pairs.is_contiguous():
         raise ValueError("pairs must be a contiguous int32 [n, 2] tensor")
     # a descriptor for the pools (q and the table only lend their shapes)
-    Hkv = k_cache.shape[1] if layout == "HND" else k_cache.shape[2]
-    D = k_cache.shape[3]
+    Hkv = k_cache.shape[2] if layout == "NHD" else k_cache.shape[1]
+    D = v_cache.shape[2] if layout == "XPACKED" else k_cache.shape[3]
     q = torch.empty(1, Hkv, D, dtype=torch.float32, device=k_cache.device)
     table = torch.empty(1, 1, dtype=torch.int32, device=k_cache.device)
     desc = desc_for(q, k_cache, v_cache, table, layout=layout)

@@ -71,12 +71,15 @@ int pick_partition(const pa_desc* d) {
 // PA_PATH_MFMA_STREAM (or an error).
 int pick_path(const pa_desc* d) {
   const int G = d->num_q_heads / d->num_kv_heads;
+  // the x-packed K / transposed V layout is read by the grid kernel only
+  const bool xp = (d->flags & PA_FLAG_KV_XPACKED) != 0;
   // the streaming kernel counts a batch's 16-token chunks (all KV heads) in 32 bits
   const bool stream_ok =
-      pa::stream_supports(d->kv_dtype, d->head_dim, G, d->block_size, d->batch) &&
+      !xp && pa::stream_supports(d->kv_dtype, d->head_dim, G, d->block_size, d->batch) &&
       (int64_t)d->batch * d->num_kv_heads * ((max_tokens(d) + 15) / 16) < ((int64_t)1 << 31);
   switch (d->path) {
     case PA_PATH_VALU:
+      if (xp) return PA_E_PATH;
       return pa::valu_supports(d->kv_dtype, d->head_dim, G) ? PA_PATH_VALU : PA_E_SHAPE;
     case PA_PATH_MFMA:
     case PA_PATH_MFMA_GRID:
@@ -91,6 +94,7 @@ int pick_path(const pa_desc* d) {
   // AUTO: matrix cores for 16-bit K/V, vector ALUs for fp32
   if (d->kv_dtype != PA_DTYPE_F32 && pa::mfma_supports(d->kv_dtype, d->head_dim, G))
     return stream_ok ? PA_PATH_MFMA_STREAM : PA_PATH_MFMA_GRID;
+  if (xp) return PA_E_PATH;
   if (pa::valu_supports(d->kv_dtype, d->head_dim, G)) return PA_PATH_VALU;
   return PA_E_SHAPE;
 }
@@ -158,13 +162,25 @@ int validate(const pa_desc* d) {
     return PA_E_DTYPE;
   if (max_tokens(d) > (int64_t)1 << 30) return PA_E_SHAPE;
   const int64_t eb = elem_bytes(d->kv_dtype);
+  const bool xp = (d->flags & PA_FLAG_KV_XPACKED) != 0;
   const int64_t st[6] = {d->k_stride_block, d->k_stride_head, d->k_stride_token,
                          d->v_stride_block, d->v_stride_head, d->v_stride_token};
   for (int i = 0; i < 6; ++i)
-    if (st[i] <= 0 || (st[i] * eb) % 16) return PA_E_STRIDE;
-  if (d->k_stride_token < d->head_dim || d->v_stride_token < d->head_dim) return PA_E_STRIDE;
+    if (st[i] <= 0 || (!(xp && i % 3 == 2) && (st[i] * eb) % 16)) return PA_E_STRIDE;
+  if (xp) {
+    // dense [d/x, bs, x] and [d, bs] tiles of 16-bit elements (x = 8); a piece
+    // of V^T is 8 consecutive tokens of one block, hence block_size >= 8
+    if (d->kv_dtype == PA_DTYPE_F32) return PA_E_PATH;
+    if (d->block_size < 8) return PA_E_BLOCK_SIZE;
+    if (d->k_stride_token != 8 || d->v_stride_token != 1) return PA_E_STRIDE;
+    const int64_t tile = (int64_t)d->block_size * d->head_dim;
+    if (d->k_stride_head < tile || d->v_stride_head < tile) return PA_E_STRIDE;
+  } else if (d->k_stride_token < d->head_dim || d->v_stride_token < d->head_dim) {
+    return PA_E_STRIDE;
+  }
   if (d->path < PA_PATH_AUTO || d->path > PA_PATH_MFMA_FUSED) return PA_E_PATH;
-  if ((d->flags & ~(PA_FLAG_KV_SHARED | PA_FLAG_QO_BF16)) || d->reserved) return PA_E_SHAPE;
+  if ((d->flags & ~(PA_FLAG_KV_SHARED | PA_FLAG_QO_BF16 | PA_FLAG_KV_XPACKED)) || d->reserved)
+    return PA_E_SHAPE;
   if (d->partition_size != 0) {
     const int ps = d->partition_size;
     if (ps < 32 || ps > 16384 || ps % 32) return PA_E_PARTITION;
@@ -270,7 +286,7 @@ const char* paged_attn_strerror(int status) {
     case PA_E_ALIGN: return "q, out, k_cache and v_cache must be 16-byte aligned";
     case PA_E_PARTITION: return "partition_size must be 0 or a multiple of 32 in [32, 16384] spanning <= 1022 blocks (MFMA_FUSED: 2 * n_part * G + 16 <= 16 * head_dim)";
     case PA_E_WORKSPACE: return "workspace missing or smaller than paged_attn_workspace_size()";
-    case PA_E_PATH: return "path must be a pa_path; the MFMA path needs f16 or bf16 K/V";
+    case PA_E_PATH: return "path must be a pa_path; the MFMA path needs f16 or bf16 K/V; the x-packed K/V layout runs on MFMA_GRID or MFMA_FUSED only";
     case PA_E_LAUNCH: return "the HIP runtime refused a kernel launch";
     case PA_E_TABLE: return "a block_table entry for an attended token is outside [0, num_blocks)";
     case PA_E_SEQLEN: return "a cache length is negative or beyond max_blocks_per_seq * block_size";
@@ -328,6 +344,7 @@ int prepare(const pa_desc* desc, const void* q, const void* k_cache, const void*
   p.qscale = scale * 1.4426950408889634f;  // log2(e): scores in base-2 units
   p.cus = cu_count();
   p.qo_bf16 = (desc->flags & PA_FLAG_QO_BF16) ? 1 : 0;
+  p.xpacked = (desc->flags & PA_FLAG_KV_XPACKED) ? 1 : 0;
   if (need > 0) {
     size_t off[kWsParts + 1];
     workspace_layout(desc, off);
@@ -427,7 +444,7 @@ int paged_attn_prefill(const pa_desc* desc, const void* q, const void* k_cache, 
                          status, true, p, false);
   if (rc != PA_OK || p.B == 0) return rc;
   if (!cu_seqlens_q) return PA_E_NULL;
-  if (desc->kv_dtype == PA_DTYPE_F32) return PA_E_PATH;
+  if (desc->kv_dtype == PA_DTYPE_F32 || (desc->flags & PA_FLAG_KV_XPACKED)) return PA_E_PATH;
   if (desc->block_size < 16 || max_seqlen_q < 0) return PA_E_SHAPE;
   if (max_seqlen_q == 0) return PA_OK;
   return pa::launch_prefill(p, desc->kv_dtype, cu_seqlens_q, max_seqlen_q, causal != 0,

@@ -33,7 +33,9 @@ namespace {
 bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 // The device copy of copy-on-write: workgroup (pair, KV head) copies that head's
-// block_size rows of d elements from block src to block dst, 16 bytes a thread.
+// block_size rows of d elements from block src to block dst, 16 bytes a thread
+// (with the x-packed layout a (block, head) tile is block_size * d dense
+// elements, copied as rows of d).
 __global__ void __launch_bounds__(256)
 copy_blocks_kernel(pa::Params p, const int32_t* pairs, int elem_bytes) {
   const int src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
@@ -212,6 +214,7 @@ int paged_attn_copy_blocks(const pa_desc* desc, void* k_cache, void* v_cache, co
   p.vsb = desc->v_stride_block;
   p.vsh = desc->v_stride_head;
   p.vst = desc->v_stride_token;
+  if (desc->flags & PA_FLAG_KV_XPACKED) p.kst = p.vst = desc->head_dim;  // dense bs x d tiles
   p.Hkv = desc->num_kv_heads;
   p.D = desc->head_dim;
   p.NB = desc->num_blocks;

@@ -43,6 +43,9 @@ struct Params {
   int len_add;              // tokens attended = cache_seqlens[b] + len_add (1 after an append)
   int qo_bf16;              // q and out are bf16 (else fp32)
   int nwaves;               // continuation slots in the workspace (streaming kernel)
+  int xpacked;              // K [NB, Hkv, D/8, bs, 8] and V [NB, Hkv, D, bs] (16-bit):
+                            // element (blk, h, t, i) of K at blk*ksb + h*ksh + (i/8)*8*bs
+                            // + 8*t + i%8, of V at blk*vsb + h*vsh + i*bs + t
 };
 
 enum { kStatusBadBlock = 1, kStatusBadSeqlen = 2 };

@@ -25,6 +25,12 @@
 // out. Tokens at or past L_b and tokens whose table entry is invalid are never
 // loaded; their scores are -inf.
 //
+// x-packed caches (the layout of the same page, section 3: K [blocks, heads,
+// d/8, bs, 8], V [blocks, heads, d, bs]): each lane's 16-byte K piece is the
+// same fragment as before, read from its row of the packed tile; V arrives as
+// V^T, 8 consecutive tokens of one dim per 16-byte read, is staged as V^T rows
+// and gives the P . V operand by plain 8-byte LDS reads (no transposing read).
+//
 // Merged variant (one launch): the same page, section 2, lets the last
 // partition block to finish do the merge instead of a second kernel. Every
 // block of a multi-partition sequence publishes its state with write-through
@@ -240,16 +246,17 @@ struct Occ {
   static constexpr int waves = D <= 128 ? 2 : 1;
 };
 
-template <typename T, int D, bool FUSED>
+template <typename T, int D, bool FUSED, bool XP>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Occ<D>::waves)))
 partition_mfma_kernel(Params p) {
   typedef typename Mma<T>::vec V8;
   constexpr int KS = D / 32;  // k-steps of a 16-token score tile
   constexpr int MB = D / 16;  // 16-dim output tiles
   constexpr bool kQInLds = D > 128;  // Q' fragments: LDS for d = 256, registers otherwise
-  // V register sets: two (refill distance 64 tokens) for d <= 128; one for d = 256,
+  // V register sets: two (refill distance 64 tokens) for d <= 128; one for d = 256
+  // and for the x-packed layout (whose V^T addressing needs more registers),
   // refilled with the next chunk as soon as it is staged in LDS.
-  constexpr int kVDist = D > 128 ? 32 : 64;
+  constexpr int kVDist = (D > 128 || XP) ? 32 : 64;
 
   __shared__ int s_ids[kTableCap];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[32 * D];
@@ -313,8 +320,14 @@ partition_mfma_kernel(Params p) {
   }
   __syncthreads();
 
-  const T* kbase = (const T*)p.k + (int64_t)hk * p.ksh + 8 * q;
-  const T* vbase = (const T*)p.v + (int64_t)hk * p.vsh + 8 * q;
+  // K: lane quad q reads dims 32 ks + 8 q .. +7 of a token. Default layouts:
+  // token rows of d elements (stride kst). x-packed: 16-byte piece 4 ks + q of
+  // the token is row 4 ks + q of the [d/8, bs, 8] tile (8 elements per token).
+  const int bs = 1 << p.bs_log2;
+  const T* kbase = (const T*)p.k + (int64_t)hk * p.ksh + (XP ? (int64_t)8 * bs * q : 8 * q);
+  const int64_t kks = XP ? (int64_t)32 * bs : 32;  // elements from dims 32 ks to 32 (ks + 1)
+  const int64_t kst = XP ? 8 : p.kst;
+  const T* vbase = (const T*)p.v + (int64_t)hk * p.vsh + (XP ? 0 : 8 * q);
 
   f32x4 acc[MB];
 #pragma unroll
@@ -324,8 +337,8 @@ partition_mfma_kernel(Params p) {
   // K or V of chunk c: lane (q, r) takes token c + 16*tau + r, dims
   // 32*ks + 8*q .. +7 (for K exactly the A-operand fragment of the score MFMA).
   // Tokens at or past t1, or behind an invalid table entry, are not loaded.
-  auto load_rows = [&](int c, const T* base, int64_t sblk, int64_t stok, uint4 (&dst)[2][KS],
-                       bool (&ok)[2]) {
+  auto load_rows = [&](int c, const T* base, int64_t sblk, int64_t stok, int64_t sks,
+                       uint4 (&dst)[2][KS], bool (&ok)[2]) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const int t = c + 16 * tau + r;
@@ -336,10 +349,47 @@ partition_mfma_kernel(Params p) {
       if (id >= 0) {
         const T* src = base + (int64_t)id * sblk + (int64_t)(t & bsm) * stok;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) dst[tau][ks] = *(const uint4*)(src + 32 * ks);
+        for (int ks = 0; ks < KS; ++ks) dst[tau][ks] = *(const uint4*)(src + sks * ks);
       }
     }
   };
+
+  // x-packed layout, V of chunk c from its [d, bs] tiles: piece j of the lane
+  // (pc = lane + 64 j) is dim pc / 4, tokens c + 8 (pc % 4) .. +7, 16 bytes of
+  // one block (bs >= 8). The piece holding t1 - 1 is read element by element up
+  // to it; pieces at or past t1 or behind an invalid entry are not read.
+  auto load_vt = [&](int c, uint4 (&dst)[2][KS]) {
+    // every piece of the lane has the same tokens (pc % 4 = lane % 4): one
+    // table lookup and one base address; piece j is 16 dims further
+    const int t = c + 8 * (lane & 3);
+    const int id = t < t1 ? s_ids[(t >> p.bs_log2) - j0] : -1;
+    const T* src = vbase + (int64_t)(id < 0 ? 0 : id) * p.vsb + (int64_t)(lane >> 2) * bs + (t & bsm);
+    const bool full = id >= 0 && t + 8 <= t1;
+    const bool tail = id >= 0 && t + 8 > t1;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const T* sp = src + (int64_t)16 * bs * (tau * KS + ks);
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (full) {
+          x = *(const uint4*)sp;
+        } else if (tail) {
+          uint32_t e[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) e[i] = t + i < t1 ? ((const uint16_t*)sp)[i] : 0u;
+          x = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                         e[6] | (e[7] << 16));
+        }
+        dst[tau][ks] = x;
+      }
+    }
+  };
+  // x-packed V^T tile in LDS: row d (a dim) holds the chunk's 32 tokens as four
+  // 16-byte octets, octet o stored at o ^ ((d >> 2) & 3), so that both the
+  // staging writes and the 8-byte fragment reads of 16 consecutive dims spread
+  // over all banks.
+  auto vt_slot = [](int d, int o) { return d * 32 + 8 * (o ^ ((d >> 2) & 3)); };
 
   // Per-lane pieces of the transposing V reads: lane (q, 4j + k) points at row
   // 16*tau + 4q + j, columns 16*mb + 4k .. +3.
@@ -353,17 +403,28 @@ partition_mfma_kernel(Params p) {
   // behind the compute.
   auto step = [&](int c, uint4 (&kr)[2][KS], bool (&okr)[2], uint4 (&vr)[2][KS]) {
     const bool refill = c + 64 < t1;
-    // ---- stage V in LDS (row-major, swizzled), then refill vr
+    // ---- stage V in LDS (row-major, swizzled; x-packed: V^T rows), then refill vr
+    if constexpr (XP) {
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int R = 16 * tau + r;
-      const int f = vswz(R);
+      for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        *(uint4*)(s_v + R * D + 8 * ((4 * ks + q) ^ f)) = vr[tau][ks];
+        for (int ks = 0; ks < KS; ++ks) {
+          const int pc = lane + 64 * (tau * KS + ks);
+          *(uint4*)(s_v + vt_slot(pc >> 2, pc & 3)) = vr[tau][ks];
+        }
+      if (c + kVDist < t1) load_vt(c + kVDist, vr);
+    } else {
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const int R = 16 * tau + r;
+        const int f = vswz(R);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          *(uint4*)(s_v + R * D + 8 * ((4 * ks + q) ^ f)) = vr[tau][ks];
+      }
+      bool dummy[2];
+      if (c + kVDist < t1) load_rows(c + kVDist, vbase, p.vsb, p.vst, 32, vr, dummy);
     }
-    bool dummy[2];
-    if (c + kVDist < t1) load_rows(c + kVDist, vbase, p.vsb, p.vst, vr, dummy);
 
     // ---- scores: two 16-token tiles, K . Q'hi + K . Q'lo
     f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -387,7 +448,7 @@ partition_mfma_kernel(Params p) {
     // token 16*tau + x was loaded iff lane x (quad 0) had a valid id for it
     const uint64_t bal0 = __ballot(okr[0]);
     const uint64_t bal1 = __ballot(okr[1]);
-    if (refill) load_rows(c + 64, kbase, p.ksb, p.kst, kr, okr);
+    if (refill) load_rows(c + 64, kbase, p.ksb, kst, kks, kr, okr);
 
     float sv[8];
 #pragma unroll
@@ -431,10 +492,17 @@ partition_mfma_kernel(Params p) {
     // element i%4 of the 8 bytes addressed by lane 4j + i/4, for j = 0..3).
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int pc = 2 * (mb ^ tj) + txor;
-      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s_v + trow + 8 * pc));
-      const s16x4 hi4 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s_v + 16 * D + trow + 8 * pc));
+      s16x4 lo4, hi4;
+      if constexpr (XP) {
+        // slots 0..3: tokens 4q .. 4q+3 (octet q / 2), 4..7: 16 + 4q .. (octet 2 + q / 2)
+        const int d = 16 * mb + r;
+        lo4 = *(const s16x4*)(s_v + vt_slot(d, q >> 1) + 4 * (q & 1));
+        hi4 = *(const s16x4*)(s_v + vt_slot(d, 2 + (q >> 1)) + 4 * (q & 1));
+      } else {
+        const int pc = 2 * (mb ^ tj) + txor;
+        lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s_v + trow + 8 * pc));
+        hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s_v + 16 * D + trow + 8 * pc));
+      }
       const V8 av = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[mb] = Mma<T>::mma(av, phi, acc[mb]);
       acc[mb] = Mma<T>::mma(av, plo, acc[mb]);
@@ -443,11 +511,19 @@ partition_mfma_kernel(Params p) {
 
   uint4 kA[2][KS], kB[2][KS], vA[2][KS], vB[kVDist == 64 ? 2 : 1][KS];
   bool okA[2], okB[2] = {false, false};
-  load_rows(t0, vbase, p.vsb, p.vst, vA, okA);
-  load_rows(t0, kbase, p.ksb, p.kst, kA, okA);
+  if constexpr (XP)
+    load_vt(t0, vA);
+  else
+    load_rows(t0, vbase, p.vsb, p.vst, 32, vA, okA);
+  load_rows(t0, kbase, p.ksb, kst, kks, kA, okA);
   if (t0 + 32 < t1) {
-    if constexpr (kVDist == 64) load_rows(t0 + 32, vbase, p.vsb, p.vst, vB, okB);
-    load_rows(t0 + 32, kbase, p.ksb, p.kst, kB, okB);
+    if constexpr (kVDist == 64) {
+      if constexpr (XP)
+        load_vt(t0 + 32, vB);
+      else
+        load_rows(t0 + 32, vbase, p.vsb, p.vst, 32, vB, okB);
+    }
+    load_rows(t0 + 32, kbase, p.ksb, kst, kks, kB, okB);
   }
   for (int c = t0; c < t1; c += 64) {
     step(c, kA, okA, vA);
@@ -495,10 +571,16 @@ partition_mfma_kernel(Params p) {
 template <typename T, int D>
 hipError_t launch_t(const Params& p, hipStream_t s) {
   dim3 grid(p.B * p.Hkv, p.pmax);
-  if (p.ws_cnt)
-    hipLaunchKernelGGL((partition_mfma_kernel<T, D, true>), grid, dim3(64), 0, s, p);
-  else
-    hipLaunchKernelGGL((partition_mfma_kernel<T, D, false>), grid, dim3(64), 0, s, p);
+  if (p.xpacked) {
+    if (p.ws_cnt)
+      hipLaunchKernelGGL((partition_mfma_kernel<T, D, true, true>), grid, dim3(64), 0, s, p);
+    else
+      hipLaunchKernelGGL((partition_mfma_kernel<T, D, false, true>), grid, dim3(64), 0, s, p);
+  } else if (p.ws_cnt) {
+    hipLaunchKernelGGL((partition_mfma_kernel<T, D, true, false>), grid, dim3(64), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((partition_mfma_kernel<T, D, false, false>), grid, dim3(64), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -159,6 +159,21 @@ def _pool_shape(layout: str, NB: int, Hkv: int, bs: int, D: int) -> tuple[int, .
     raise ValueError(f"unknown layout {layout!r}")
 
 
+def to_xpacked(store: np.ndarray, which: str) -> np.ndarray:
+    """The same values in the x-packed cache layout of page "Paged Attention
+    Kernel Architecture for BI-V100", section 3, from an HND pool
+    [NB, H_kv, bs, d]: K ("k") becomes [NB, H_kv, d/x, bs, x] with
+    x = 16 bytes / element, V ("v") becomes [NB, H_kv, d, bs]. Element
+    (blk, h, t, i) moves to [blk, h, i // x, t, i % x] and [blk, h, i, t]."""
+    NB, H, bs, D = store.shape
+    if which == "k":
+        x = 16 // store.itemsize
+        return np.ascontiguousarray(store.reshape(NB, H, bs, D // x, x).transpose(0, 1, 3, 2, 4))
+    if which == "v":
+        return np.ascontiguousarray(store.transpose(0, 1, 3, 2))
+    raise ValueError(which)
+
+
 def _draw_pool(rng: np.random.Generator, shape, kv_dtype: str, std: float) -> np.ndarray:
     """Fill a storage array block by block with N(0, std^2) draws rounded to kv_dtype.
 

@@ -224,12 +224,42 @@ def test_decode_argument_errors_return_before_device_work():
     assert pa.decode_raw(_desc(batch=0), **{**args, "q_ptr": 0}) == 0        # nothing to do
 
 
+def _xp(**kw):
+    # x-packed K [64, 2, 16, 16, 8] / V [64, 2, 128, 16]: block and head strides,
+    # token strides x = 8 and 1
+    base = dict(k_strides=(2 * 16 * 128, 16 * 128, 8), v_strides=(2 * 16 * 128, 16 * 128, 1),
+                xpacked=True)
+    base.update(kw)
+    return _desc(**base)
+
+
+def test_xpacked_layout_descriptor():
+    assert pa.validate(_xp()) == 0
+    # the grid kernels read it; AUTO and MFMA pick the grid kernel
+    assert pa.PATH_NAME[pa.resolved_path(_xp())] == "mfma_grid"
+    assert pa.PATH_NAME[pa.resolved_path(_xp(path="mfma"))] == "mfma_grid"
+    assert pa.PATH_NAME[pa.resolved_path(_xp(path="mfma_fused"))] == "mfma_fused"
+    assert pa.validate(_xp(path="mfma_stream")) == -10
+    assert pa.validate(_xp(path="valu")) == -10
+    assert pa.validate(_xp(kv_dtype="f32", k_strides=(4096, 2048, 4),
+                           v_strides=(4096, 2048, 1))) == -10
+    # token strides fixed by the layout; head stride holds the whole tile
+    assert pa.validate(_xp(k_strides=(4096, 2048, 128))) == -6
+    assert pa.validate(_xp(v_strides=(4096, 2048, 2))) == -6
+    assert pa.validate(_xp(k_strides=(4096, 1024, 8))) == -6
+    # a V^T piece is 8 tokens of one block
+    assert pa.validate(_xp(block_size=4, k_strides=(2 * 4 * 128, 4 * 128, 8),
+                           v_strides=(2 * 4 * 128, 4 * 128, 1))) == -4
+    assert pa.validate(_xp(block_size=8, k_strides=(2 * 8 * 128, 8 * 128, 8),
+                           v_strides=(2 * 8 * 128, 8 * 128, 1))) == 0
+
+
 def test_flags_field():
     assert pa.validate(_desc(kv_shared=True)) == 0
     assert pa.validate(_desc(qo_bf16=True)) == 0
     assert pa.validate(_desc(kv_shared=True, qo_bf16=True)) == 0
     d = _desc()
-    d.flags = 4  # unknown bit
+    d.flags = 8  # unknown bit
     assert pa.validate(d) == -2
     d = _desc()
     d.reserved = 1
@@ -261,6 +291,7 @@ def test_prefill_argument_errors():
     assert pa.prefill_raw(d, **{**args, "seqlens_k_ptr": 0}) == -1       # no key lengths
     assert pa.prefill_raw(d, **{**args, "q_ptr": good + 4}) == -7        # misaligned
     assert pa.prefill_raw(_desc(kv_dtype="f32", k_strides=(4096, 2048, 128)), **args) == -10
+    assert pa.prefill_raw(_xp(), **args) == -10   # x-packed caches: decode only
     assert pa.prefill_raw(_desc(block_size=8, k_strides=(2048, 1024, 128)), **args) == -2
     assert pa.prefill_raw(d, **{**args, "max_seqlen_q": -1}) == -2
     assert pa.prefill_raw(d, **{**args, "max_seqlen_q": 0}) == 0          # no rows

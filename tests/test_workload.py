@@ -105,3 +105,22 @@ def test_nhd_layout_same_tables_token_major_strides():
                      layout="NHD")
     assert np.array_equal(a.block_table, b.block_table)
     assert a.strides() == (64, 32, 8) and b.strides() == (64, 8, 16)
+
+
+@pytest.mark.parametrize("dtype,x", [(np.uint16, 8), (np.float32, 4)])
+def test_xpacked_layout_is_the_pages_indexing(dtype, x):
+    """to_xpacked against the layout's definition, element by element: K element
+    (blk, h, t, i) sits at [blk, h, i // x, t, i % x] of [NB, H, d/x, bs, x]
+    (x = 16 bytes / element) and V element (blk, h, t, i) at [blk, h, i, t]."""
+    rng = np.random.default_rng(7)
+    NB, H, bs, D = 3, 2, 8, 32
+    pool = rng.integers(0, 60000, size=(NB, H, bs, D)).astype(dtype)
+    kx, vx = W.to_xpacked(pool, "k"), W.to_xpacked(pool, "v")
+    assert kx.shape == (NB, H, D // x, bs, x) and vx.shape == (NB, H, D, bs)
+    assert kx.flags["C_CONTIGUOUS"] and vx.flags["C_CONTIGUOUS"]
+    for blk in range(NB):
+        for h in range(H):
+            for t in range(bs):
+                for i in range(D):
+                    assert kx[blk, h, i // x, t, i % x] == pool[blk, h, t, i]
+                    assert vx[blk, h, i, t] == pool[blk, h, t, i]
