@@ -384,8 +384,9 @@ def main():
         log(f"[bench] copied {n} bytes x {a.steps}")
         return
 
-    if a.profile == "prefill":
-        measure_prefill(1, torch, a.steps, a.warmup)
+    if a.profile == "prefill":  # the prefill workloads named by --prefill
+        for k in [int(x) for x in a.prefill.split(",") if x.strip()]:
+            measure_prefill(k, torch, a.steps, a.warmup)
         return
 
     wl = Workload(a.config, torch, a.path, a.partition, a.layout)

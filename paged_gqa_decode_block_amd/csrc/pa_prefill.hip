@@ -11,17 +11,21 @@
 // head, group of up to 8 of its query heads). The 256 threads load each
 // 16-token chunk of K and V once (d/64 16-byte pieces each, raw buffer loads
 // through descriptors cut to the chunk's attended rows, an invalid table entry
-// never dereferenced) into a ring of chunks in registers, and stage it into
-// one of two LDS tiles; after one barrier per chunk every wave computes its
-// query heads (head w, w + 4 of the group) against the tile:
+// never dereferenced) into a ring of chunks in registers, and stage two
+// consecutive chunks into one of two 32-token LDS tiles; after one barrier per
+// tile every wave computes its query heads (head w, w + 4 of the group)
+// against it:
 //
-//   scores  S^T[token, row] = K[token, :] . Q'[row, :]       16x16x32 MFMAs
+//   scores  S^T[token, row] = K[token, :] . Q'[row, :]       16x16x32 MFMAs,
+//           two 16-token halves
 //   update  running max m, sum l, output per row and head (base 2, lazily
 //           rescaled)
-//   output  O^T[dim, row] += V^T[dim, token] . P^T[token, row]  16x16x16
+//   output  O^T[dim, row] += V^T[dim, token] . P^T[token, row]  16x16x32 over
+//           the 32 tokens
 //
 // with the tile's 16 rows as the MFMA columns and Q' and P in hi + lo 16-bit
-// parts. The workgroup walks the tokens up to the tile's last row's key end; a
+// parts. (On gfx950 a 16x16x16 bf16 MFMA takes as long as a 16x16x32 one, so
+// the output product runs on 32-token tiles.) The workgroup walks the tokens up to the tile's last row's key end; a
 // token is masked per column, so each row ends at its own causal bound. No
 // partial state leaves the workgroup: each head's tile is normalised and
 // written at the end.
@@ -45,8 +49,8 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
   constexpr int PPT = D / 64;  // 16-byte pieces of a chunk per thread (4 D of them)
   constexpr int HPW = kHeadsPerGroup / 4;
   static_assert((NBUF - 1) * PPT <= 60, "ring deeper than the vector-memory counter");
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][16 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][16 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][32 * D];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -160,21 +164,30 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
   }
   const int tj = r >> 2, tk = r & 3;
 
-  // fold chunk cn (staged in LDS tile `buf`) into head slot j
-  auto consume = [&](int cn, int buf, int j) __attribute__((always_inline)) {
+  // fold 32-token tile tc (tokens 32 tc .., staged in LDS tile `buf`) into
+  // head slot j. P^T k-slot i of lane (q, r) holds token 16 (i / 4) + 4 q + i % 4,
+  // the score MFMA's output layout of the two halves.
+  auto consume = [&](int tc, int buf, int j) __attribute__((always_inline)) {
     const uint16_t* sk = s_k[buf];
     const uint16_t* sv_ = s_v[buf];
-    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const V8 a = *(const V8*)(sk + r * D + 8 * ((4 * ks + q) ^ (r & 7)));
-      st = M::mma32(a, qhi[j][ks], st);
-      st = M::mma32(a, qlo[j][ks], st);
-    }
-    float sv[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sv[k] = (16 * cn + 4 * q + k < kend_r) ? st[k] : -INFINITY;
-    const float mt = quad_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+      for (int tau = 0; tau < 2; ++tau) {
+        const V8 a = *(const V8*)(sk + (16 * tau + r) * D + 8 * ((4 * ks + q) ^ (r & 7)));
+        st[tau] = M::mma32(a, qhi[j][ks], st[tau]);
+        st[tau] = M::mma32(a, qlo[j][ks], st[tau]);
+      }
+    }
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      sv[i] = (32 * tc + 16 * (i >> 2) + 4 * q + (i & 3) < kend_r) ? st[i >> 2][i & 3] : -INFINITY;
+    float mx = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+    const float mt = quad_max(mx);
     const bool raise = mt > m[j] + 8.f;
     if (__ballot(raise)) {
       const float mn = raise ? mt : m[j];
@@ -185,56 +198,60 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
       m[j] = mn;
     }
     const float mu = m[j] == -INFINITY ? 0.f : m[j];
-    float pv[4];
+    float pv[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) pv[k] = exp2_fast(sv[k] - mu);
-    l[j] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-    typename M::e4 ph, pl2;
+    for (int i = 0; i < 8; ++i) pv[i] = exp2_fast(sv[i] - mu);
+    l[j] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+    V8 phi, plo;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const T hh = (T)pv[k];
-      ph[k] = hh;
-      pl2[k] = (T)(pv[k] - (float)hh);
+    for (int i = 0; i < 8; ++i) {
+      const T hh = (T)pv[i];
+      phi[i] = hh;
+      plo[i] = (T)(pv[i] - (float)hh);
     }
-    const V4 phi = M::pack(ph), plo = M::pack(pl2);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int pcol = 2 * (mb ^ tj) + ((tk >> 1) ^ (q & 1));
-      const s16x4 a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(sv_ + (4 * q + tj) * D + 8 * pcol + 4 * (tk & 1)));
-      const V4 av = __builtin_bit_cast(V4, a4);
-      acc[j][mb] = M::mma16(av, phi, acc[j][mb]);
-      acc[j][mb] = M::mma16(av, plo, acc[j][mb]);
+      const int o = (4 * q + tj) * D + 8 * pcol + 4 * (tk & 1);
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + o));
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + 16 * D + o));
+      const V8 av = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[j][mb] = M::mma32(av, phi, acc[j][mb]);
+      acc[j][mb] = M::mma32(av, plo, acc[j][mb]);
     }
   };
 
   // the ring: chunk c + NBUF - 1 is issued just before chunk c is staged
-  // (unconditionally: past the end the descriptors are empty). Chunk c goes to
-  // LDS tile c % 2; the barrier after staging also means every wave is done
-  // with chunk c - 1, so tile (c + 1) % 2 is free for the next chunk.
+  // (unconditionally: past the end the descriptors are empty, so an odd last
+  // chunk is paired with zeros). Chunk c goes to half c % 2 of 32-token LDS
+  // tile (c / 2) % 2; the barrier after a tile's second half also means every
+  // wave is done with the tile before, so the other tile is free.
+  const int nch2 = (nch + 1) & ~1;
   uint4 ring[NBUF][PPT];
   static_for<0, NBUF - 1>([&](auto S) {
     constexpr int s = decltype(S)::value;
     issue(s, ring[s], idr[s]);
   });
-  for (int cb = 0; cb < nch; cb += NBUF) {
+  for (int cb = 0; cb < nch2; cb += NBUF) {
     static_for<0, NBUF>([&](auto S) {
       constexpr int s = decltype(S)::value;
       constexpr int sn = (s + NBUF - 1) % NBUF;
       const int c = cb + s;
       issue(c + NBUF - 1, ring[sn], idr[sn]);
       __builtin_amdgcn_sched_barrier(0);
-      if (c < nch) {
-        const int buf = c & 1;
+      if (c < nch2) {
+        const int buf = (c >> 1) & 1, half = (c & 1) * 16 * D;
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
           uint16_t* dst = pisv[k] ? s_v[buf] : s_k[buf];
-          *(uint4*)(dst + plds[k]) = ring[s][k];
+          *(uint4*)(dst + half + plds[k]) = ring[s][k];
         }
-        __syncthreads();
+        if (c & 1) {
+          __syncthreads();
 #pragma unroll
-        for (int j = 0; j < HPW; ++j)
-          if (hon[j]) consume(c, buf, j);
+          for (int j = 0; j < HPW; ++j)
+            if (hon[j]) consume(c >> 1, buf, j);
+        }
       }
     });
   }
@@ -257,7 +274,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
 }
 
 // {ring slots, workgroups of four waves per CU} per head_dim
-constexpr int kPrefillCfg[3][2] = {{6, 2}, {4, 2}, {3, 1}};
+constexpr int kPrefillCfg[3][2] = {{6, 2}, {4, 2}, {2, 1}};
 constexpr int pdim(int D) { return D == 64 ? 0 : D == 128 ? 1 : 2; }
 
 template <typename T, int D, int QO>
