@@ -13,7 +13,7 @@
 // through descriptors cut to the chunk's attended rows, an invalid table entry
 // never dereferenced) into a ring of chunks in registers, and stage two
 // consecutive chunks into one of two 32-token LDS tiles; after one barrier per
-// tile every wave computes its query heads (head w, w + 4 of the group)
+// tile every wave computes its query heads (head w, w + NW, ... of the group)
 // against it:
 //
 //   scores  S^T[token, row] = K[token, :] . Q'[row, :]       16x16x32 MFMAs,
@@ -36,18 +36,22 @@
 namespace pa {
 namespace {
 
-constexpr int kPrefillThreads = 256;  // four waves
-constexpr int kHeadsPerGroup = 8;     // query heads per workgroup (two per wave)
+constexpr int kHeadsPerGroup = 8;  // query heads per workgroup: 8 / NW per wave
 
-template <typename T, int D, int NBUF, int OCC, int QO>
-__global__ void __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+// NW waves per workgroup (4: two heads per wave; 8: one head per wave, half
+// the registers, so that d = 256 runs two waves per SIMD), NBUF ring slots,
+// OCC waves per SIMD.
+template <typename T, int D, int NW, int NBUF, int OCC, int QO>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) {
   typedef Mx<T> M;
   typedef typename M::v8 V8;
   typedef typename M::v4 V4;
   constexpr int KS = D / 32, MB = D / 16;
-  constexpr int PPT = D / 64;  // 16-byte pieces of a chunk per thread (4 D of them)
-  constexpr int HPW = kHeadsPerGroup / 4;
+  constexpr int kThreads = 64 * NW;
+  constexpr int PPT = 4 * D / kThreads;  // 16-byte pieces of a chunk per thread (4 D of them)
+  constexpr int HPW = kHeadsPerGroup / NW;
+  static_assert(PPT * kThreads == 4 * D, "the workgroup loads a chunk in whole pieces");
   static_assert((NBUF - 1) * PPT <= 60, "ring deeper than the vector-memory counter");
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][32 * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][32 * D];
@@ -75,13 +79,13 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
   const int kend = causal ? min(L, max(0, L - ql + plast + 1)) : L;  // the tile's
   const int nch = (kend + 15) >> 4;
 
-  // this wave's query heads: g0 + w + 4 j of the KV head's group
+  // this wave's query heads: g0 + w + NW j of the KV head's group
   bool hon[HPW];
   V8 qhi[HPW][KS], qlo[HPW][KS];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
-    hon[j] = w + 4 * j < hcount;
-    const int h = hk * p.G + g0 + (hon[j] ? w + 4 * j : 0);
+    hon[j] = w + NW * j < hcount;
+    const int h = hk * p.G + g0 + (hon[j] ? w + NW * j : 0);
     const int64_t qrow = ((int64_t)(r0 + (col_ok ? p0 + r : 0)) * p.Hq + h) * D + 8 * q;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -106,7 +110,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
   bool pisv[PPT];
 #pragma unroll
   for (int k = 0; k < PPT; ++k) {
-    const int i = tid + kPrefillThreads * k;
+    const int i = tid + kThreads * k;
     // a wave's 64 pieces are consecutive and 2 D is a multiple of 64, so K or V
     // is the same across the wave: made visibly uniform for the descriptor choice
     pisv[k] = __builtin_amdgcn_readfirstlane(i >= 2 * D ? 1 : 0) != 0;
@@ -261,7 +265,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
     const float lt = quad_sum(l[j]);
     if (hon[j] && col_ok) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int h = hk * p.G + g0 + w + 4 * j;
+      const int h = hk * p.G + g0 + w + NW * j;
       const int64_t orow = ((int64_t)(r0 + p0 + r) * p.Hq + h) * D + 4 * q;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -273,16 +277,17 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
   if (bad_block && tid == 0 && p.status) atomicOr(p.status, kStatusBadBlock);
 }
 
-// {ring slots, workgroups of four waves per CU} per head_dim
-constexpr int kPrefillCfg[3][2] = {{6, 2}, {4, 2}, {2, 1}};
+// {waves per workgroup, ring slots, waves per SIMD} per head_dim
+constexpr int kPrefillCfg[3][3] = {{4, 6, 2}, {8, 4, 4}, {8, 4, 2}};
 constexpr int pdim(int D) { return D == 64 ? 0 : D == 128 ? 1 : 2; }
 
 template <typename T, int D, int QO>
 hipError_t launch_p(const Params& p, const int32_t* cu_q, int max_q, int causal, hipStream_t s) {
-  constexpr int NB_ = kPrefillCfg[pdim(D)][0], OCC = kPrefillCfg[pdim(D)][1];
+  constexpr int NW = kPrefillCfg[pdim(D)][0], NB_ = kPrefillCfg[pdim(D)][1],
+                OCC = kPrefillCfg[pdim(D)][2];
   const int nhg = (p.G + kHeadsPerGroup - 1) / kHeadsPerGroup;
   dim3 grid((max_q + 15) / 16, p.Hkv * nhg, p.B);
-  hipLaunchKernelGGL((prefill_kernel<T, D, NB_, OCC, QO>), grid, dim3(kPrefillThreads), 0, s, p,
+  hipLaunchKernelGGL((prefill_kernel<T, D, NW, NB_, OCC, QO>), grid, dim3(64 * NW), 0, s, p,
                      cu_q, causal, nhg);
   return hipGetLastError();
 }
