@@ -7,14 +7,14 @@
 // tokens [0, L_b - q_len_b + i]; a query with no token to attend gets zeros.
 // Otherwise every query attends all L_b tokens.
 //
-// One workgroup of four waves per (tile of 16 query rows of one sequence, KV
-// head, group of up to 8 of its query heads). The 256 threads load each
-// 16-token chunk of K and V once (d/64 16-byte pieces each, raw buffer loads
-// through descriptors cut to the chunk's attended rows, an invalid table entry
-// never dereferenced) into a ring of chunks in registers, and stage two
-// consecutive chunks into one of two 32-token LDS tiles; after one barrier per
-// tile every wave computes its query heads (head w, w + NW, ... of the group)
-// against it:
+// One workgroup per eight (16-row query tile, query head) units of one KV
+// head: 8 / hh consecutive tiles of a sequence times hh of the KV head's query
+// heads (hh = 8, or the largest power of two dividing G, so that no unit is
+// empty). Its threads load each 16-token chunk of K and V once (16-byte
+// pieces, raw buffer loads through descriptors cut to the chunk's attended
+// rows, an invalid table entry never dereferenced) into a ring of chunks in
+// registers, and stage two consecutive chunks into one of two 32-token LDS
+// tiles; after one barrier per tile every wave folds its units against it:
 //
 //   scores  S^T[token, row] = K[token, :] . Q'[row, :]       16x16x32 MFMAs,
 //           two 16-token halves
@@ -23,12 +23,12 @@
 //   output  O^T[dim, row] += V^T[dim, token] . P^T[token, row]  16x16x32 over
 //           the 32 tokens
 //
-// with the tile's 16 rows as the MFMA columns and Q' and P in hi + lo 16-bit
+// with a tile's 16 rows as the MFMA columns and Q' and P in hi + lo 16-bit
 // parts. (On gfx950 a 16x16x16 bf16 MFMA takes as long as a 16x16x32 one, so
-// the output product runs on 32-token tiles.) The workgroup walks the tokens up to the tile's last row's key end; a
-// token is masked per column, so each row ends at its own causal bound. No
-// partial state leaves the workgroup: each head's tile is normalised and
-// written at the end.
+// the output product runs on 32-token tiles.) The workgroup walks the tokens
+// up to its last tile's last row's key end; a token is masked per column, so
+// each row ends at its own causal bound. No partial state leaves the
+// workgroup: each unit is normalised and written at the end.
 //
 // Requires 16-bit K/V and block_size >= 16.
 #include "pa_mfma_util.h"
@@ -36,14 +36,15 @@
 namespace pa {
 namespace {
 
-constexpr int kHeadsPerGroup = 8;  // query heads per workgroup: 8 / NW per wave
+constexpr int kHeadsPerGroup = 8;  // (tile, head) units per workgroup: 8 / NW per wave
 
 // NW waves per workgroup (4: two heads per wave; 8: one head per wave, half
 // the registers, so that d = 256 runs two waves per SIMD), NBUF ring slots,
 // OCC waves per SIMD.
 template <typename T, int D, int NW, int NBUF, int OCC, int QO>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
-prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) {
+prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, int hh,
+               int ntiles) {
   typedef Mx<T> M;
   typedef typename M::v8 V8;
   typedef typename M::v4 V4;
@@ -59,34 +60,40 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int r = lane & 15, q = lane >> 4;
+  // The workgroup's 8 (tile, head) units: tpw = 8 / hh consecutive 16-row
+  // tiles times hh query heads of KV head hk (heads g0 .. g0 + hh - 1 of its
+  // group). Each K/V chunk it loads serves all eight.
+  const int tpw = kHeadsPerGroup / hh;
   const int b = blockIdx.z;
-  const int hk = (int)blockIdx.y / nhg, g0 = ((int)blockIdx.y % nhg) * kHeadsPerGroup;
-  const int hcount = min(kHeadsPerGroup, p.G - g0);
-  const int p0 = 16 * (int)blockIdx.x;
+  const int hk = (int)blockIdx.y / nhg, g0 = ((int)blockIdx.y % nhg) * hh;
+  const int hcount = min(hh, p.G - g0);
+  const int pw0 = 16 * tpw * (int)blockIdx.x;  // first row of the workgroup's tiles
   const int r0 = cu_q[b];
   const int ql = cu_q[b + 1] - r0;
   // rows beyond the grid would be left unwritten: report
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0 && p.status &&
-      (ql < 0 || ql > 16 * (int)gridDim.x))
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0 && p.status && (ql < 0 || ql > 16 * ntiles))
     atomicOr(p.status, kStatusBadSeqlen);
-  if (p0 >= ql) return;  // the whole workgroup
+  if (pw0 >= ql) return;  // the whole workgroup
   const int L = clamped_len(p, b, blockIdx.x == 0 && blockIdx.y == 0 && tid == 0);
-
-  // column r: query position p0 + r of the sequence; its keys are [0, kend_r)
-  const bool col_ok = p0 + r < ql;
-  const int kend_r = !col_ok ? 0 : causal ? min(L, max(0, L - ql + p0 + r + 1)) : L;
-  const int plast = min(p0 + 15, ql - 1);
-  const int kend = causal ? min(L, max(0, L - ql + plast + 1)) : L;  // the tile's
+  const int plast = min(pw0 + 16 * tpw - 1, ql - 1);
+  const int kend = causal ? min(L, max(0, L - ql + plast + 1)) : L;  // the last tile's
   const int nch = (kend + 15) >> 4;
 
-  // this wave's query heads: g0 + w + NW j of the KV head's group
-  bool hon[HPW];
+  // slot j of this wave: unit u = w + NW j, tile u / hh, head u % hh. Column r
+  // is query position p0s + r of the sequence; its keys are [0, kend_r).
+  bool hon[HPW], col_ok[HPW];
+  int kend_r[HPW], p0s[HPW], hls[HPW];
   V8 qhi[HPW][KS], qlo[HPW][KS];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
-    hon[j] = w + NW * j < hcount;
-    const int h = hk * p.G + g0 + (hon[j] ? w + NW * j : 0);
-    const int64_t qrow = ((int64_t)(r0 + (col_ok ? p0 + r : 0)) * p.Hq + h) * D + 8 * q;
+    const int u = w + NW * j, tl = u / hh;
+    hls[j] = u - tl * hh;
+    p0s[j] = pw0 + 16 * tl;
+    col_ok[j] = p0s[j] + r < ql;
+    hon[j] = hls[j] < hcount && p0s[j] < ql;
+    kend_r[j] = !col_ok[j] ? 0 : causal ? min(L, max(0, L - ql + p0s[j] + r + 1)) : L;
+    const int h = hk * p.G + g0 + (hon[j] ? hls[j] : 0);
+    const int64_t qrow = ((int64_t)(r0 + (col_ok[j] ? p0s[j] + r : 0)) * p.Hq + h) * D + 8 * q;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const float4 a = load_q4<QO>(p, qrow + 32 * ks);
@@ -94,7 +101,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
       const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float y = col_ok ? x[k] * p.qscale : 0.f;
+        const float y = col_ok[j] ? x[k] * p.qscale : 0.f;
         const T hh = (T)y;
         qhi[j][ks][k] = hh;
         qlo[j][ks][k] = (T)(y - (float)hh);
@@ -102,7 +109,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
     }
   }
 
-  // the pieces this thread loads: piece i = tid + 256 k of the chunk's 4 D
+  // the pieces this thread loads: piece i = tid + 64 NW k of the chunk's 4 D
   // (K pieces first): row, 16-byte column and whether it is V
   const int bsm = (1 << p.bs_log2) - 1;
   const int kst_bytes = (int)(p.kst * (int)sizeof(T)), vst_bytes = (int)(p.vst * (int)sizeof(T));
@@ -187,7 +194,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
     float sv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      sv[i] = (32 * tc + 16 * (i >> 2) + 4 * q + (i & 3) < kend_r) ? st[i >> 2][i & 3] : -INFINITY;
+      sv[i] = (32 * tc + 16 * (i >> 2) + 4 * q + (i & 3) < kend_r[j]) ? st[i >> 2][i & 3] : -INFINITY;
     float mx = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
@@ -263,10 +270,10 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg) 
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const float lt = quad_sum(l[j]);
-    if (hon[j] && col_ok) {
+    if (hon[j] && col_ok[j]) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int h = hk * p.G + g0 + w + NW * j;
-      const int64_t orow = ((int64_t)(r0 + p0 + r) * p.Hq + h) * D + 4 * q;
+      const int h = hk * p.G + g0 + hls[j];
+      const int64_t orow = ((int64_t)(r0 + p0s[j] + r) * p.Hq + h) * D + 4 * q;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const f32x4 o = acc[j][mb] * inv;
@@ -285,10 +292,21 @@ template <typename T, int D, int QO>
 hipError_t launch_p(const Params& p, const int32_t* cu_q, int max_q, int causal, hipStream_t s) {
   constexpr int NW = kPrefillCfg[pdim(D)][0], NB_ = kPrefillCfg[pdim(D)][1],
                 OCC = kPrefillCfg[pdim(D)][2];
-  const int nhg = (p.G + kHeadsPerGroup - 1) / kHeadsPerGroup;
-  dim3 grid((max_q + 15) / 16, p.Hkv * nhg, p.B);
+  // heads per workgroup: 8 when they divide G; else the largest power of two
+  // dividing G, with 8 / hh tiles per workgroup so that no unit is idle, if
+  // there are that many tiles (else 8, the last group partly empty)
+  const int ntiles = (max_q + 15) / 16;
+  int hh = kHeadsPerGroup;
+  if (p.G % kHeadsPerGroup) {
+    int h2 = 1;
+    while (2 * h2 < kHeadsPerGroup && p.G % (2 * h2) == 0) h2 *= 2;
+    if (ntiles >= kHeadsPerGroup / h2) hh = h2;
+  }
+  const int tpw = kHeadsPerGroup / hh;
+  const int nhg = (p.G + hh - 1) / hh;
+  dim3 grid((ntiles + tpw - 1) / tpw, p.Hkv * nhg, p.B);
   hipLaunchKernelGGL((prefill_kernel<T, D, NW, NB_, OCC, QO>), grid, dim3(64 * NW), 0, s, p,
-                     cu_q, causal, nhg);
+                     cu_q, causal, nhg, hh, ntiles);
   return hipGetLastError();
 }
 

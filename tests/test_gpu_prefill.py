@@ -68,6 +68,10 @@ CASES = [
     ("d256_g6", 12, 2, 256, 16, "bf16", "HND", [700, 33], [65, 33]),
     ("d128_nhd_bs32", 8, 1, 128, 32, "bf16", "NHD", [250, 64], [31, 64]),
     ("d128_g1", 4, 4, 128, 64, "f16", "HND", [129, 200], [129, 3]),
+    # G = 12: four heads times two tiles per workgroup; G = 2 at d = 64: two
+    # units per wave on different tiles
+    ("d128_g12", 24, 2, 128, 16, "bf16", "HND", [400, 90], [70, 90]),
+    ("d64_g2_tiles", 8, 4, 64, 16, "bf16", "HND", [1000, 20], [200, 20]),
 ]
 
 
