@@ -28,10 +28,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8.0 TB/s
 METRIC = "decode attention KV GB/s (% of MI355X HBM peak) + seq-heads/s, 1 GPU"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
+# sources of the streaming partition kernel (the dominant one) and its launch:
+# HBM counter readings taken on other sources are not reported as its traffic
 KERNEL_SOURCES = ["paged_gqa_decode_block_amd/csrc/pa_partition_stream.hip",
-                  "paged_gqa_decode_block_amd/csrc/pa_partition_mfma.hip",
-                  "paged_gqa_decode_block_amd/csrc/pa_partition_valu.hip",
-                  "paged_gqa_decode_block_amd/csrc/pa_combine.hip",
+                  "paged_gqa_decode_block_amd/csrc/pa_mfma_util.h",
                   "paged_gqa_decode_block_amd/csrc/pa_kernels.h",
                   "paged_gqa_decode_block_amd/csrc/pa_api.hip"]
 

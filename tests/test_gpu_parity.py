@@ -294,6 +294,35 @@ def test_stream_kernel_continuation_chains(torch_cuda):
         assert np.abs(got - want).max() <= 3e-3, ps
 
 
+@pytest.mark.parametrize("path", ["mfma_stream", "mfma_grid", "valu"])
+def test_poisoned_workspace_is_never_used(torch_cuda, path):
+    """Every byte of the workspace set to 0xFF before each call (NaN in every
+    float slot, -1 in every link): the combine reads partition slots up to the
+    workspace's row length before it knows a sequence's own partition count,
+    and must drop the stale ones. Sequences of 0, 1, a few and many partitions
+    share one batch, so most rows hold slots past their own count."""
+    torch = torch_cuda
+    rng = np.random.default_rng(910)
+    L = [0, 1, 33, 700, 5000, 64, 2049]
+    case, _, _ = paged_case(rng, B=len(L), Hq=16, Hkv=2, D=128, bs=16, kv_dtype="bf16",
+                            seqlens=L, spare=3)
+    want = run_oracle(case)
+    dev = to_device(torch, case)
+    for ps in (32, 64, 512):
+        desc = pa.desc_for(dev["q"], dev["k"], dev["v"], dev["table"], partition_size=ps,
+                           path=path)
+        ws = torch.full((max(pa.workspace_size(desc), 256),), 0xFF, dtype=torch.uint8,
+                        device="cuda")
+        for rep in range(2):
+            ws.fill_(0xFF)
+            out = pa.paged_attn_decode(dev["q"], dev["k"], dev["v"], dev["table"],
+                                       dev["seqlens"], case.scale, partition_size=ps, path=path,
+                                       workspace=ws)
+            got = out.cpu().numpy().astype(np.float64)
+            assert np.isfinite(got).all(), (path, ps, rep)
+            assert np.abs(got - want).max() <= 3e-3, (path, ps, rep)
+
+
 def test_partition_then_combine_phase_equals_decode(torch_cuda):
     """The two phases called one after the other give the one-call result bit
     for bit (same workspace, same stream)."""
