@@ -10,6 +10,10 @@ measured too and reported under "also". Prints one JSON line on stdout; progress
   python bench.py [--steps K] [--warmup W] [--config 4] [--also 3]
   python bench.py --profile partition   # only partition-kernel launches (for rocprofv3)
   python bench.py --profile copy        # a 1 GiB device copy (counter calibration)
+
+Next to the decode numbers it reports plain HBM read rates on the same GPU
+(libpaprobe.so: a 2 GiB buffer read sequentially and as 4 / 8 KB tiles in random
+order) and the fp64 CPU oracle timed on a bounded sample (all threads and one).
 """
 from __future__ import annotations
 
@@ -163,6 +167,7 @@ def measure(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
     part_ms = time_each(torch, lambda: wl.call("partition"), steps)
     wl.call()  # leave the workspace of a complete call behind for the combine timing
     comb_ms = time_steps(torch, lambda: wl.call("combine"), steps)
+    step_each = time_each(torch, wl.call, steps)
     cold_ms = time_each(torch, wl.call, max(5, steps // 4), flush=lambda: flush_buf.add_(1))
     c = wl.case
     t = ms / 1e3
@@ -174,6 +179,7 @@ def measure(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
         "partition_kernel_us_p10_p90": [float(np.percentile(part_ms, 10) * 1e3),
                                         float(np.percentile(part_ms, 90) * 1e3)],
         "combine_kernel_us": float(comb_ms * 1e3),
+        "step_us_p10_p50_p90": [float(np.percentile(step_each, x) * 1e3) for x in (10, 50, 90)],
         "cold_ms_median": float(np.median(cold_ms)),
         "cold_kv_gbs": wl.kv_bytes / (np.median(cold_ms) / 1e3) / 1e9,
         "kv_bytes": wl.kv_bytes,
@@ -299,6 +305,67 @@ def roofline(wl: Workload, r: dict) -> dict:
     return out
 
 
+def read_probe(torch, steps: int = 10) -> dict:
+    """Plain HBM read rates on the same GPU, for context next to the decode
+    kernel: a 2 GiB buffer read front to back, and the same buffer read as 4 KB
+    and 8 KB tiles in a seeded random order (the K tile of one (block, KV head)
+    at head_dim 128 and 256), one tile per wave at a time, 16-byte
+    non-temporal loads (libpaprobe.so)."""
+    import ctypes
+
+    from paged_gqa_decode_block_amd import build as B
+
+    if not os.path.exists(B.PROBE_LIB):
+        raise RuntimeError(f"{B.PROBE_LIB} is missing: build it with python -m "
+                           "paged_gqa_decode_block_amd.build")
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.pa_probe_stream_read.argtypes = [vp, i64, vp, i32, vp]
+    lib.pa_probe_tile_gather.argtypes = [vp, vp, i32, i32, vp, i32, vp]
+    nbytes = 1 << 31
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 8 * cus
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4 * blocks, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    out = {"buffer_bytes": nbytes, "loads": "16-byte non-temporal", "workgroups": blocks}
+
+    def timed(fn) -> float:
+        for _ in range(3):
+            fn()
+        ms = time_steps(torch, fn, steps)
+        return nbytes / (ms / 1e3) / 1e9
+
+    def run(rc):
+        if rc != 0:
+            raise RuntimeError(f"read probe launch failed ({rc})")
+
+    out["stream_read_gbs"] = round(timed(lambda: run(lib.pa_probe_stream_read(
+        buf.data_ptr(), nbytes, sink.data_ptr(), blocks, st.cuda_stream))), 1)
+    rng = np.random.default_rng(7)
+    for kb in (4, 8):
+        ntiles = nbytes // (kb * 1024)
+        tiles = torch.from_numpy(rng.permutation(ntiles).astype(np.int32)).to("cuda")
+        out[f"tile_gather_{kb}k_gbs"] = round(timed(lambda: run(lib.pa_probe_tile_gather(
+            buf.data_ptr(), tiles.data_ptr(), ntiles, kb * 1024, sink.data_ptr(), blocks,
+            st.cuda_stream))), 1)
+        del tiles
+    del buf, sink
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl: Workload, budget_s: float) -> dict:
     """The fp64 oracle on a bounded sample of (sequence, head) pairs of the same
     workload, extrapolated to the whole batch by cached-token count."""
@@ -333,8 +400,19 @@ def cpu_baseline(wl: Workload, budget_s: float) -> dict:
     tok_sample = int(c.seqlens[pairs_all[:used, 0]].astype(np.int64).sum())
     tok_all = int(c.seqlens.astype(np.int64).sum()) * c.Hq
     t_full = t_used * tok_all / tok_sample
+    # one thread on a slice of the same sample, sized to about a sixth of the budget
+    n1 = max(1, min(used, int(used * (budget_s / 6) / max(t_used * threads, 1e-3))))
+    t0 = time.perf_counter()
+    O.paged_attn_decode(c.q, c.k_pool, c.v_pool, c.block_table, c.seqlens, c.scale,
+                        kv_dtype=c.kv_dtype, block_size=c.bs, num_kv_heads=c.Hkv,
+                        layout=c.layout, pairs=pairs_all[:n1], nthreads=1)
+    t1 = time.perf_counter() - t0
+    tok1 = int(c.seqlens[pairs_all[:n1, 0]].astype(np.int64).sum())
+    t1_full = t1 * tok_all / max(tok1, 1)
     return {"value": round(wl.kv_bytes / t_full / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_thread": {"value": round(wl.kv_bytes / t1_full / 1e9, 4), "unit": "GB/s",
+                              "sample": f"{n1} pairs ({tok1} head-tokens) in {t1:.2f}s"},
             "sample": f"{used} of {c.B * c.Hq} (sequence, query head) pairs of {c.name} "
                       f"({tok_sample} of {tok_all} head-tokens) in {t_used:.2f}s, "
                       "extrapolated by head-token count (best of up to 3 runs when the whole batch fits)",
@@ -344,7 +422,7 @@ def cpu_baseline(wl: Workload, budget_s: float) -> dict:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--also", type=str, default="3,5", help="comma-separated extra configs ('' for none)")
@@ -358,6 +436,7 @@ def main():
                          "bs, 8], V [NB, H_kv, d, bs], the same values)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the plain read-rate probes")
     ap.add_argument("--profile", choices=["partition", "both", "copy", "prefill"], default=None)
     ap.add_argument("--prefill", type=str, default="1,2",
                     help="comma-separated prefill workloads to time ('' for none)")
@@ -424,6 +503,12 @@ def main():
     for k in [int(x) for x in a.prefill.split(",") if x.strip()]:
         r3 = measure_prefill(k, torch, max(5, a.steps // 5), 3)
         prefill[r3["workload"]] = r3
+    probe = None
+    if not a.no_probe:
+        probe = read_probe(torch)
+        probe["decode_kernel_vs_stream_read"] = round(rl["achieved"] / probe["stream_read_gbs"], 4)
+        log(f"[bench] plain reads: {probe['stream_read_gbs']:.0f} GB/s sequential, "
+            f"{probe['tile_gather_4k_gbs']:.0f} / {probe['tile_gather_8k_gbs']:.0f} GB/s as 4 / 8 KB tiles")
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")
@@ -447,6 +532,7 @@ def main():
         "detail": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()},
         "roofline": rl,
         "cpu_baseline": cpu,
+        "read_probe": probe,
         "also": also,
         "prefill": prefill,
     }

@@ -3,7 +3,8 @@
 Usage: python -m paged_gqa_decode_block_amd.build [-j N]
 
 Each csrc/*.hip compiles to an object in _build/ (in parallel), then they link
-into paged_gqa_decode_block_amd/libpagedattn.so. Every HIP translation unit is
+into paged_gqa_decode_block_amd/libpagedattn.so; probe/pa_read_probe.hip links
+into libpaprobe.so (read-rate probes used by the benchmark only). Every HIP translation unit is
 built with packed-FP32 instruction selection turned off.
 """
 from __future__ import annotations
@@ -20,6 +21,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
+# read-rate probes for the benchmark's context line (not part of the decode path)
+PROBE_SRC = os.path.join(HERE, "probe", "pa_read_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libpaprobe.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -57,7 +61,20 @@ def build(jobs: int | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+def build_probe() -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    obj = _compile(PROBE_SRC)
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe link failed:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
