@@ -475,8 +475,8 @@ partition_stream_kernel(Params p) {
 // the default): {NBUF, OCC, Q' in LDS} for head_dim 64, 128, 256.
 constexpr int kNumVariants = 4;
 constexpr int kVariants[kNumVariants][3][3] = {
-    {{6, 2, 0}, {3, 2, 0}, {3, 1, 1}},   // 0
-    {{12, 1, 0}, {6, 1, 0}, {2, 1, 1}},  // 1
+    {{6, 2, 0}, {3, 2, 0}, {2, 1, 1}},   // 0
+    {{12, 1, 0}, {6, 1, 0}, {3, 1, 1}},  // 1
     {{4, 4, 0}, {2, 3, 0}, {4, 1, 1}},   // 2
     {{8, 2, 1}, {4, 2, 1}, {3, 1, 1}},   // 3 (d = 256 at two waves per SIMD would spill)
 };

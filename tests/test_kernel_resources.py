@@ -23,7 +23,7 @@ READELF = shutil.which("llvm-readelf") or "/opt/rocm/llvm/bin/llvm-readelf"
 BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
 # default ring variant per head_dim: (ring slots, waves per SIMD, Q' in LDS)
-DEFAULT_STREAM = {64: (6, 2, 0), 128: (3, 2, 0), 256: (3, 1, 1)}
+DEFAULT_STREAM = {64: (6, 2, 0), 128: (3, 2, 0), 256: (2, 1, 1)}
 
 
 def _private_segment_sizes(lib: str) -> dict[str, int]:
