@@ -323,6 +323,29 @@ def test_poisoned_workspace_is_never_used(torch_cuda, path):
             assert np.abs(got - want).max() <= 3e-3, (path, ps, rep)
 
 
+@pytest.mark.parametrize("D,Hq,Hkv,part", [(256, 24, 4, 512), (128, 16, 2, 64)])
+def test_stream_kernel_one_sequence_table_fill(torch_cuda, D, Hq, Hkv, part):
+    """One long sequence whose block table it fills exactly, to one token or
+    one block short, or to half: the streaming kernel's shares then fall on
+    stream ends in different places; unread slots are NaN, so any read of a
+    wrong table entry or of a slot past the length would show."""
+    torch = torch_cuda
+    bs = 16
+    for i, (L, mbs) in enumerate([(12800, 800), (12799, 800), (12784, 800), (6400, 800)]):
+        rng = np.random.default_rng(950 + i)
+        case, _, _ = paged_case(rng, B=1, Hq=Hq, Hkv=Hkv, D=D, bs=bs, kv_dtype="bf16",
+                                seqlens=[L], spare=mbs)
+        pages = -(-L // bs)
+        table = np.full((1, mbs), -1, dtype=np.int32)
+        table[0, :pages] = case.block_table[0, :pages]
+        case.block_table = table
+        case.MBS = mbs
+        want = run_oracle(case)
+        got = run_gpu(torch, case, path="mfma_stream", partition_size=part)
+        assert np.isfinite(got).all(), (L, mbs)
+        assert np.abs(got - want).max() <= 3e-3, (L, mbs)
+
+
 def test_partition_then_combine_phase_equals_decode(torch_cuda):
     """The two phases called one after the other give the one-call result bit
     for bit (same workspace, same stream)."""
