@@ -22,15 +22,15 @@
 // 4u .. 4u+3 of a 64-dim slice (float4 loads) and partitions p = s, s + S, ....
 // Each thread folds its partitions with the same max-rescaling op, a batch of
 // partitions' loads in flight per round, so no pass over all maxima has to
-// finish first; the S stripes' states then meet in LDS. S is 16, or 64 (32
-// beyond 256) when there are more than 64 partitions, so one round usually
-// covers them all.
+// finish first; the S stripes' states then meet in LDS. S is 4 or 8 when there
+// are at most that many partitions, 16 up to 64, and 64 (32 beyond 256) above,
+// so one round usually covers them all.
 #include "pa_kernels.h"
 
 namespace pa {
 namespace {
 
-// kStripes: partition stripes (16, 32 or 64); kBatch: partitions per thread per
+// kStripes: partition stripes (4, 8, 16, 32 or 64); kBatch: partitions per thread per
 // round (1, 4 or 8); both chosen from the partition count.
 template <int kStripes, int kBatch>
 __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
@@ -182,7 +182,13 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
 
 hipError_t launch_combine(const Params& p, hipStream_t s) {
   dim3 grid(p.D / 64, p.Hq, p.B);
-  if (p.pmax <= 16)
+  // stripes sized to the partition count: with few partitions per sequence
+  // (long partitions over a large batch) small workgroups leave no thread idle
+  if (p.pmax <= 4)
+    hipLaunchKernelGGL((combine_kernel<4, 1>), grid, dim3(64), 0, s, p);
+  else if (p.pmax <= 8)
+    hipLaunchKernelGGL((combine_kernel<8, 1>), grid, dim3(128), 0, s, p);
+  else if (p.pmax <= 16)
     hipLaunchKernelGGL((combine_kernel<16, 1>), grid, dim3(256), 0, s, p);
   else if (p.pmax <= 64)
     hipLaunchKernelGGL((combine_kernel<16, 4>), grid, dim3(256), 0, s, p);
