@@ -11,6 +11,13 @@
 // issue is unconditional and its table reads travel in ring order, so the wait
 // before each chunk covers that chunk's loads only.
 //
+// At head_dim 256 a share belongs to a pair of waves (one workgroup) that split
+// the head dims: each loads, stages and folds 128 of them, and their partial
+// scores meet in LDS once per chunk (one barrier), so both keep the same
+// softmax state while each holds half of the output. That keeps a wave at
+// d = 128's registers and two waves per SIMD, so one wave's folding overlaps
+// the other's loads.
+//
 // Partial states stay per partition (PART tokens of a stream): a piece of a
 // partition that starts at the partition's first chunk goes to the partition's
 // slot together with a link; a share that begins inside a partition leaves that
@@ -65,23 +72,33 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 
 // NBUF: ring slots (chunks in flight + 1), (NBUF - 1) * 2 * LPC <= 63 so the
 // vector-memory counter can track them all. OCC: waves per SIMD the register
-// allocation is held to. POL: cache policy of the K/V loads.
-template <typename T, int D, int NBUF, int OCC, int POL, bool QL, int QO>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+// allocation is held to. POL: cache policy of the K/V loads. DS: waves sharing
+// one share (1, or 2: a workgroup of two waves splits the head dims, each
+// loading, staging and folding D / 2 of them; their partial scores are added
+// through LDS once per chunk, so both hold the same softmax state).
+template <typename T, int D, int NBUF, int OCC, int POL, bool QL, int QO, int DS>
+__global__ void __launch_bounds__(64 * DS) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 partition_stream_kernel(Params p) {
   typedef Mx<T> M;
   typedef typename M::v8 V8;
   typedef typename M::v4 V4;
-  typedef Cfg<D> C;
+  constexpr int DW = D / DS;  // head dims this wave loads and folds
+  typedef Cfg<DW> C;
   constexpr int LPC = C::LPC, KS = C::KS, MB = C::MB;
+  static_assert(DS == 1 || DS == 2, "one wave or a pair per share");
   static_assert((NBUF - 1) * 2 * LPC <= 63, "ring deeper than the vector-memory counter");
 
   constexpr bool kQLds = QL;  // Q' fragments in LDS (else in registers)
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[16 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[16 * D];
-  __shared__ __attribute__((aligned(16))) V8 s_q[kQLds ? 2 : 1][kQLds ? KS : 1][64];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[DS][16 * DW];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[DS][16 * DW];
+  __shared__ __attribute__((aligned(16))) V8 s_q[DS][kQLds ? 2 : 1][kQLds ? KS : 1][64];
+  // partial scores of the pair, double-buffered by chunk parity
+  __shared__ __attribute__((aligned(16))) f32x4 s_x[DS == 2 ? 2 : 1][DS][64];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  // which half of the head dims this wave holds (0 when DS = 1), uniform
+  const int half = DS == 2 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
+  int par = 0;  // chunk parity of the score exchange
   const int r = lane & 15, q = lane >> 4;
   const int G = p.G, Hkv = p.Hkv, PART = p.part;
   const int CPP = PART >> 4;  // chunks per partition
@@ -180,11 +197,12 @@ partition_stream_kernel(Params p) {
 
   // byte offsets of this lane's 16-byte piece of row s*RPI + rowL in a chunk
   const int kst_bytes = (int)(p.kst * (int)sizeof(T)), vst_bytes = (int)(p.vst * (int)sizeof(T));
+  const int hoff = half * DW * (int)sizeof(T);  // this wave's dims within a row
   int koffs[LPC], voffs[LPC];
 #pragma unroll
   for (int s = 0; s < LPC; ++s) {
-    koffs[s] = (s * C::RPI + rowL) * kst_bytes + 16 * cc;
-    voffs[s] = (s * C::RPI + rowL) * vst_bytes + 16 * cc;
+    koffs[s] = (s * C::RPI + rowL) * kst_bytes + 16 * cc + hoff;
+    voffs[s] = (s * C::RPI + rowL) * vst_bytes + 16 * cc + hoff;
   }
 
   // ---- 2. segments: the share's runs of chunks within one (b, KV head) -------
@@ -221,7 +239,7 @@ partition_stream_kernel(Params p) {
       float4 qa[KS], qb[KS];
       {
         const bool hv = r < G;
-        const int64_t qrow = ((int64_t)b * p.Hq + hk * G + (hv ? r : 0)) * D + 8 * q;
+        const int64_t qrow = ((int64_t)b * p.Hq + hk * G + (hv ? r : 0)) * D + half * DW + 8 * q;
         // every lane loads (padded heads read head 0's row, a valid address)
         // and make_q zeroes padded heads: no branch around the loads
 #pragma unroll
@@ -248,8 +266,8 @@ partition_stream_kernel(Params p) {
             lo[k] = (T)(y - (float)h);
           }
           if constexpr (kQLds) {
-            s_q[0][ks][lane] = hi;
-            s_q[1][ks][lane] = lo;
+            s_q[half][0][ks][lane] = hi;
+            s_q[half][1][ks][lane] = lo;
           } else {
             qhi[ks] = hi;
             qlo[ks] = lo;
@@ -318,7 +336,7 @@ partition_stream_kernel(Params p) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
             *(float4*)(ap + 16 * mb) = make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
-          if (q == 0) {
+          if (q == 0 && half == 0) {
             *mp = m;
             *lp = lt;
           }
@@ -327,7 +345,7 @@ partition_stream_kernel(Params p) {
           const int h = hk * G + r;
           if (direct) {
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
-            const int64_t orow = ((int64_t)b * p.Hq + h) * D + 4 * q;
+            const int64_t orow = ((int64_t)b * p.Hq + h) * D + half * DW + 4 * q;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
               const f32x4 o = acc[mb] * inv;
@@ -335,13 +353,13 @@ partition_stream_kernel(Params p) {
             }
           } else if (is_main) {
             const int64_t row = ((int64_t)b * p.Hq + h) * p.pmax + pp;
-            store(p.ws_acc + row * D + 4 * q, p.ws_m + row, p.ws_l + row);
+            store(p.ws_acc + row * D + half * DW + 4 * q, p.ws_m + row, p.ws_l + row);
           } else {
             const int64_t row = (int64_t)blockIdx.x * G + r;
-            store(p.ws_cacc + row * D + 4 * q, p.ws_cm + row, p.ws_cl + row);
+            store(p.ws_cacc + row * D + half * DW + 4 * q, p.ws_cm + row, p.ws_cl + row);
           }
         }
-        if (lane == 0) {
+        if (lane == 0 && half == 0) {
           if (is_main)
             p.ws_link[((int64_t)b * Hkv + hk) * p.pmax + pp] =
                 direct ? -2 : covers_end ? -1 : (int)blockIdx.x + 2;  // wave x + 1, plus one
@@ -360,21 +378,28 @@ partition_stream_kernel(Params p) {
 #pragma unroll
         for (int s = 0; s < LPC; ++s) {
           const int R = s * C::RPI + rowL;
-          *(uint4*)(s_k + R * D + 8 * (cc ^ (R & 7))) = rk[s];
-          *(uint4*)(s_v + R * D + 8 * (cc ^ vswz(R))) = rv[s];
+          *(uint4*)(s_k[half] + R * DW + 8 * (cc ^ (R & 7))) = rk[s];
+          *(uint4*)(s_v[half] + R * DW + 8 * (cc ^ vswz(R))) = rv[s];
         }
         // scores of the 16 tokens: lane (q, r) gets tokens 4q..4q+3 of head r
         f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const V8 a = *(const V8*)(s_k + r * D + 8 * ((4 * ks + q) ^ (r & 7)));
+          const V8 a = *(const V8*)(s_k[half] + r * DW + 8 * ((4 * ks + q) ^ (r & 7)));
           if constexpr (kQLds) {
-            st = M::mma32(a, s_q[0][ks][lane], st);
-            st = M::mma32(a, s_q[1][ks][lane], st);
+            st = M::mma32(a, s_q[half][0][ks][lane], st);
+            st = M::mma32(a, s_q[half][1][ks][lane], st);
           } else {
             st = M::mma32(a, qhi[ks], st);
             st = M::mma32(a, qlo[ks], st);
           }
+        }
+        if constexpr (DS == 2) {
+          // both waves add the two halves in the same order: equal scores
+          s_x[par][half][lane] = st;
+          __syncthreads();
+          st = s_x[par][0][lane] + s_x[par][1][lane];
+          par ^= 1;
         }
         float sv[4];
 #pragma unroll
@@ -414,7 +439,7 @@ partition_stream_kernel(Params p) {
         for (int mb = 0; mb < MB; ++mb) {
           const int pc = 2 * (mb ^ tj) + ((tk >> 1) ^ (q & 1));
           const s16x4 a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(s_v + (4 * q + tj) * D + 8 * pc + 4 * (tk & 1)));
+              (lds_s16x4*)(s_v[half] + (4 * q + tj) * DW + 8 * pc + 4 * (tk & 1)));
           const V4 av = __builtin_bit_cast(V4, a4);
           acc[mb] = M::mma16(av, phi, acc[mb]);
           acc[mb] = M::mma16(av, plo, acc[mb]);
@@ -471,14 +496,16 @@ partition_stream_kernel(Params p) {
   if (__ballot(bad_block) && lane == 0 && p.status) atomicOr(p.status, kStatusBadBlock);
 }
 
-// Ring depth / occupancy / Q' placement variants per head_dim (variant 0 is
-// the default): {NBUF, OCC, Q' in LDS} for head_dim 64, 128, 256.
+// Ring depth / occupancy / Q' placement / dim split variants per head_dim
+// (variant 0 is the default): {NBUF, OCC, Q' in LDS, DS} for head_dim 64, 128,
+// 256. At d = 256 one wave holding all dims needs one SIMD to itself; a pair
+// splitting them runs at two waves per SIMD like d = 128.
 constexpr int kNumVariants = 4;
-constexpr int kVariants[kNumVariants][3][3] = {
-    {{6, 2, 0}, {3, 2, 0}, {2, 1, 1}},   // 0
-    {{12, 1, 0}, {6, 1, 0}, {3, 1, 1}},  // 1
-    {{4, 4, 0}, {2, 3, 0}, {4, 1, 1}},   // 2
-    {{8, 2, 1}, {4, 2, 1}, {3, 1, 1}},   // 3 (d = 256 at two waves per SIMD would spill)
+constexpr int kVariants[kNumVariants][3][4] = {
+    {{6, 2, 0, 1}, {3, 2, 0, 1}, {2, 2, 0, 2}},   // 0
+    {{12, 1, 0, 1}, {6, 1, 0, 1}, {2, 1, 1, 1}},  // 1
+    {{4, 4, 0, 1}, {2, 3, 0, 1}, {3, 2, 1, 2}},   // 2
+    {{8, 2, 1, 1}, {4, 2, 1, 1}, {3, 2, 0, 2}},   // 3
 };
 constexpr int dim_index(int D) { return D == 64 ? 0 : D == 128 ? 1 : 2; }
 
@@ -486,10 +513,11 @@ template <typename T, int D, int V, int POL, int QO>
 hipError_t launch_t(const Params& p, hipStream_t s) {
   constexpr int NBUF = kVariants[V][dim_index(D)][0], OCC = kVariants[V][dim_index(D)][1];
   constexpr bool QL = kVariants[V][dim_index(D)][2] != 0;
+  constexpr int DS = kVariants[V][dim_index(D)][3];
   const int64_t bound = (int64_t)p.B * p.Hkv * (((int64_t)p.MBS << p.bs_log2) + 15) / 16;
-  const int waves = stream_grid(D, V, p.cus, bound);
-  hipLaunchKernelGGL((partition_stream_kernel<T, D, NBUF, OCC, POL, QL, QO>), dim3(waves), dim3(64),
-                     0, s, p);
+  const int workers = stream_grid(D, V, p.cus, bound);  // waves, or pairs when DS = 2
+  hipLaunchKernelGGL((partition_stream_kernel<T, D, NBUF, OCC, POL, QL, QO, DS>), dim3(workers),
+                     dim3(64 * DS), 0, s, p);
   return hipGetLastError();
 }
 
@@ -525,8 +553,8 @@ bool stream_supports(int dtype, int D, int G, int block_size, int batch) {
 
 int stream_grid(int D, int variant, int cus, int64_t chunk_bound) {
   const int v = variant >= 0 && variant < kNumVariants ? variant : 0;
-  const int occ = kVariants[v][dim_index(D)][1];
-  return stream_active_waves(chunk_bound, 4 * occ * cus, cus);
+  const int occ = kVariants[v][dim_index(D)][1], ds = kVariants[v][dim_index(D)][3];
+  return stream_active_waves(chunk_bound, 4 * occ * cus / ds, cus);
 }
 
 hipError_t launch_partition_stream(const Params& p, int dtype, int variant, bool nt, hipStream_t s) {

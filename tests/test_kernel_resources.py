@@ -22,8 +22,9 @@ from paged_gqa_decode_block_amd import LIB_PATH
 READELF = shutil.which("llvm-readelf") or "/opt/rocm/llvm/bin/llvm-readelf"
 BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
-# default ring variant per head_dim: (ring slots, waves per SIMD, Q' in LDS)
-DEFAULT_STREAM = {64: (6, 2, 0), 128: (3, 2, 0), 256: (2, 1, 1)}
+# default ring variant per head_dim: (ring slots, waves per SIMD, Q' in LDS); at d = 256
+# a pair of waves splits the head dims
+DEFAULT_STREAM = {64: (6, 2, 0), 128: (3, 2, 0), 256: (2, 2, 0)}
 
 
 def _private_segment_sizes(lib: str) -> dict[str, int]:
