@@ -22,7 +22,8 @@
 // 4u .. 4u+3 of a 64-dim slice (float4 loads) and partitions p = s, s + S, ....
 // Each thread folds its partitions with the same max-rescaling op, a batch of
 // partitions' loads in flight per round, so no pass over all maxima has to
-// finish first; the S stripes' states then meet in LDS. S is 4 or 8 when there
+// finish first; the S stripes' states then meet, four per wave by cross-lane
+// exchanges and the waves' through LDS. S is 4 or 8 when there
 // are at most that many partitions, 16 up to 64, and 64 (32 beyond 256) above,
 // so one round usually covers them all.
 #include "pa_kernels.h"
@@ -34,6 +35,7 @@ namespace {
 // round (1, 4 or 8); both chosen from the partition count.
 template <int kStripes, int kBatch>
 __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
+  static_assert(kStripes % 4 == 0, "whole waves of four stripes");
   const int b = blockIdx.z, h = blockIdx.y;
   const int tid = threadIdx.x;
   const int u = tid & 15, s = tid >> 4;
@@ -148,23 +150,39 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
     Ms = bm;
   }
 
-  __shared__ float4 s_a[kStripes][16];
-  __shared__ float s_m[kStripes], s_l[kStripes];
-  s_a[s][u] = A;
-  if (u == 0) {
-    s_m[s] = Ms;
-    s_l[s] = Ls;
+  // Merge the stripes: the four stripes of a wave (lanes 16 apart, same dims)
+  // by two cross-lane exchanges, then the waves' states through LDS.
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    const float om = __shfl_xor(Ms, off), ol = __shfl_xor(Ls, off);
+    float4 oa;
+    oa.x = __shfl_xor(A.x, off);
+    oa.y = __shfl_xor(A.y, off);
+    oa.z = __shfl_xor(A.z, off);
+    oa.w = __shfl_xor(A.w, off);
+    merge(Ms, Ls, A, om, ol, oa);
+  }
+  constexpr int kWaves = kStripes / 4;
+  __shared__ float4 s_a[kWaves][16];
+  __shared__ float s_m[kWaves], s_l[kWaves];
+  const int wv = tid >> 6;
+  if ((tid & 63) < 16) {
+    s_a[wv][u] = A;
+    if (u == 0) {
+      s_m[wv] = Ms;
+      s_l[wv] = Ls;
+    }
   }
   __syncthreads();
   if (tid < 16) {
     float M = s_m[0];
 #pragma unroll
-    for (int k = 1; k < kStripes; ++k) M = fmaxf(M, s_m[k]);
+    for (int k = 1; k < kWaves; ++k) M = fmaxf(M, s_m[k]);
     const float mu = M == -INFINITY ? 0.f : M;
     float tot = 0.f;
     float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int k = 0; k < kStripes; ++k) {
+    for (int k = 0; k < kWaves; ++k) {
       const float w = exp2_fast(s_m[k] - mu);
       tot += w * s_l[k];
       num.x += w * s_a[k][tid].x;
