@@ -57,12 +57,13 @@ def run_gpu(torch, case, dev=None, *, path="auto", partition_size=None, status=N
 
 
 def paths_for(case):
-    """Every kernel that can run this case: VALU always; for 16-bit K/V the
-    one-workgroup-per-partition MFMA kernel and, for block_size >= 16 and at
-    most 1024 sequences, the persistent streaming MFMA kernel."""
+    """Every kernel that can run this case: VALU for groups of up to 8 heads;
+    for 16-bit K/V the one-workgroup-per-partition MFMA kernel and, for
+    block_size >= 16 and at most 1024 sequences, the persistent streaming MFMA
+    kernel."""
     if case.kv_dtype == "f32":
         return ["valu"]
-    out = ["valu", "mfma_grid"]
+    out = (["valu"] if case.Hq // case.Hkv <= 8 else []) + ["mfma_grid"]
     if case.bs >= 16 and case.B <= 1024:
         out.append("mfma_stream")
     return out
@@ -84,6 +85,10 @@ SMALL = [
     ("bf16_d128_g5_bs64", 2, 10, 2, 128, 64, "bf16", "HND", [300, 64], 96),
     ("f16_d256_g8_part2048", 2, 16, 2, 256, 16, "f16", "HND", [2500, 2048], 2048),
     ("bf16_empty_and_one", 4, 8, 2, 128, 16, "bf16", "HND", [0, 1, 0, 17], 32),
+    # d = 256 (a pair of waves per share in the streaming kernel): token-major
+    # rows, the largest group, 32-token blocks; and one head per group in fp16
+    ("bf16_d256_g16_nhd_bs32", 2, 32, 2, 256, 32, "bf16", "NHD", [1500, 47], 512),
+    ("f16_d256_g1", 3, 2, 2, 256, 16, "f16", "HND", [33, 700, 1], 64),
 ]
 
 
