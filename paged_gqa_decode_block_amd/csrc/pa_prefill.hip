@@ -83,6 +83,9 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   // is query position p0s + r of the sequence; its keys are [0, kend_r).
   bool hon[HPW], col_ok[HPW];
   int kend_r[HPW], p0s[HPW], hls[HPW];
+  // kfull[j]: the least key end over slot j's valid columns (the whole wave
+  // agrees); a 32-token tile ending at or below it needs no mask
+  int kfull[HPW];
   V8 qhi[HPW][KS], qlo[HPW][KS];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
@@ -92,6 +95,10 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
     col_ok[j] = p0s[j] + r < ql;
     hon[j] = hls[j] < hcount && p0s[j] < ql;
     kend_r[j] = !col_ok[j] ? 0 : causal ? min(L, max(0, L - ql + p0s[j] + r + 1)) : L;
+    int kf = col_ok[j] ? kend_r[j] : 0x7fffffff;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) kf = min(kf, __shfl_xor(kf, off));
+    kfull[j] = __builtin_amdgcn_readfirstlane(kf);
     const int h = hk * p.G + g0 + (hon[j] ? hls[j] : 0);
     const int64_t qrow = ((int64_t)(r0 + (col_ok[j] ? p0s[j] + r : 0)) * p.Hq + h) * D + 8 * q;
 #pragma unroll
@@ -192,9 +199,14 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
       }
     }
     float sv[8];
+    if (32 * tc + 32 <= kfull[j]) {  // every valid column attends the whole tile
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      sv[i] = (32 * tc + 16 * (i >> 2) + 4 * q + (i & 3) < kend_r[j]) ? st[i >> 2][i & 3] : -INFINITY;
+      for (int i = 0; i < 8; ++i) sv[i] = st[i >> 2][i & 3];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        sv[i] = (32 * tc + 16 * (i >> 2) + 4 * q + (i & 3) < kend_r[j]) ? st[i >> 2][i & 3] : -INFINITY;
+    }
     float mx = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
