@@ -4,8 +4,10 @@ A step is one decode call (partition kernel + combine kernel) over the whole
 synthetic batch, inputs resident in HBM. Default workload: the 64-sequence
 large-GQA bf16 batch (B=64, H_q=64, H_kv=8, d=128, bs=16, lengths log-uniform in
 [1024, 32768], 10% spare blocks); the 100K-token Qwen3.6-shaped batch (B=1,
-H_q=24, H_kv=4, d=256, partition 512) and the prefix-shared 256-sequence batch are
-measured too and reported under "also". Prints one JSON line on stdout; progress goes to stderr.
+H_q=24, H_kv=4, d=256, partition 512), the prefix-shared 256-sequence batch, and
+(for information: they fit in the caches) the tiny fp32 example and the Qwen2-shaped
+fp16 batch are measured too and reported under "also". Prints one JSON line on
+stdout; progress goes to stderr.
 
   python bench.py [--steps K] [--warmup W] [--config 4] [--also 3]
   python bench.py --profile partition   # only partition-kernel launches (for rocprofv3)
@@ -184,6 +186,8 @@ def measure(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
         "cold_kv_gbs": wl.kv_bytes / (np.median(cold_ms) / 1e3) / 1e9,
         "kv_bytes": wl.kv_bytes,
         "unique_kv_bytes": wl.unique_kv_bytes,
+        # prefix-shared blocks counted once (equal to kv_gbs when no block is shared)
+        "unique_kv_gbs": wl.unique_kv_bytes / t / 1e9,
     }
 
 
@@ -425,7 +429,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=4)
-    ap.add_argument("--also", type=str, default="3,5", help="comma-separated extra configs ('' for none)")
+    ap.add_argument("--also", type=str, default="3,5,1,2",
+                    help="comma-separated extra configs ('' for none); 1 and 2 fit in the caches "
+                         "and are reported for information")
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "mfma_grid", "mfma_stream",
                                                    "mfma_fused"])
     ap.add_argument("--partition", type=int, default=None,

@@ -51,8 +51,11 @@ typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } 
  * 16-token chunks (block_size >= 16, batch <= 1024, fewer than 2^31 chunks per
  * KV head: batch * ceil(max_blocks_per_seq * block_size / 16) < 2^31), and
  * MFMA_GRID, one workgroup per partition (any block size and batch).
- * PA_PATH_MFMA picks MFMA_STREAM when it applies, else MFMA_GRID; AUTO picks
- * MFMA for 16-bit K/V and VALU for fp32.
+ * PA_PATH_MFMA picks MFMA_STREAM when it applies and the batch's K/V bound
+ * (batch * num_kv_heads * max_blocks_per_seq * block_size * head_dim * 2
+ * elements) is at least 256 MB, else MFMA_GRID (on smaller batches the
+ * persistent waves' start-up is not amortised); AUTO picks MFMA that way for
+ * 16-bit K/V and VALU for fp32.
  *
  * MFMA_FUSED is MFMA_GRID with the partition merge done by the last partition
  * workgroup of each (sequence, KV head) to finish, instead of by a second

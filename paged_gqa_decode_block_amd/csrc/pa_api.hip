@@ -24,6 +24,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int64_t max_tokens(const pa_desc* d) { return (int64_t)d->max_blocks_per_seq * d->block_size; }
 
 int pick_path(const pa_desc* d);
+bool stream_pays(const pa_desc* d);
 int cu_count();
 int stream_variant();
 int stream_variant_for(const pa_desc* d);
@@ -67,6 +68,20 @@ int pick_partition(const pa_desc* d) {
   return part;
 }
 
+// Whether the persistent streaming kernel beats the one-workgroup-per-
+// partition grid kernel: only on batches whose K/V (bounded by
+// max_blocks_per_seq * block_size tokens per sequence) reaches 256 MB. Below
+// that each persistent wave gets a short share and its start-up (lengths,
+// table, then K/V, about 10 us) is not amortised, while the grid kernel starts
+// every partition at once: on one MI355X the grid kernel measured 0.6-0.9x the
+// streaming kernel's time up to 270 MB and the streaming kernel won from
+// 400 MB (the 100K-token batch) up.
+bool stream_pays(const pa_desc* d) {
+  const int64_t elem = d->kv_dtype == PA_DTYPE_F32 ? 4 : 2;
+  const int64_t bytes = (int64_t)d->batch * d->num_kv_heads * max_tokens(d) * d->head_dim * elem * 2;
+  return bytes >= ((int64_t)256 << 20);
+}
+
 // The kernel a descriptor runs on: PA_PATH_VALU, PA_PATH_MFMA_GRID or
 // PA_PATH_MFMA_STREAM (or an error).
 int pick_path(const pa_desc* d) {
@@ -89,11 +104,11 @@ int pick_path(const pa_desc* d) {
       if (!pa::mfma_supports(d->kv_dtype, d->head_dim, G)) return PA_E_SHAPE;
       if (d->path == PA_PATH_MFMA_GRID || d->path == PA_PATH_MFMA_FUSED) return d->path;
       if (d->path == PA_PATH_MFMA_STREAM) return stream_ok ? PA_PATH_MFMA_STREAM : PA_E_PATH;
-      return stream_ok ? PA_PATH_MFMA_STREAM : PA_PATH_MFMA_GRID;
+      return stream_ok && stream_pays(d) ? PA_PATH_MFMA_STREAM : PA_PATH_MFMA_GRID;
   }
   // AUTO: matrix cores for 16-bit K/V, vector ALUs for fp32
   if (d->kv_dtype != PA_DTYPE_F32 && pa::mfma_supports(d->kv_dtype, d->head_dim, G))
-    return stream_ok ? PA_PATH_MFMA_STREAM : PA_PATH_MFMA_GRID;
+    return stream_ok && stream_pays(d) ? PA_PATH_MFMA_STREAM : PA_PATH_MFMA_GRID;
   if (xp) return PA_E_PATH;
   if (pa::valu_supports(d->kv_dtype, d->head_dim, G)) return PA_PATH_VALU;
   return PA_E_SHAPE;

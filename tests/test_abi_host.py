@@ -63,12 +63,20 @@ def _desc(**kw):
 
 def test_valid_descriptor_and_resolved_path():
     assert pa.validate(_desc()) == 0
-    assert pa.PATH_NAME[pa.resolved_path(_desc())] == "mfma_stream"
-    assert pa.PATH_NAME[pa.resolved_path(_desc(path="mfma"))] == "mfma_stream"
-    assert pa.PATH_NAME[pa.resolved_path(_desc(path="mfma_grid"))] == "mfma_grid"
+    # below 256 MB of K/V (by the max_blocks_per_seq bound) the grid kernel; at
+    # and above it the streaming kernel, where it applies
+    big = dict(max_blocks_per_seq=8192, num_blocks=16384)   # 2 * 2 * 131072 * 128 * 2 * 2 B = 256 MiB
+    assert pa.PATH_NAME[pa.resolved_path(_desc())] == "mfma_grid"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(path="mfma"))] == "mfma_grid"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(path="mfma_stream"))] == "mfma_stream"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(**big))] == "mfma_stream"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(path="mfma", **big))] == "mfma_stream"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(max_blocks_per_seq=8191, num_blocks=16384))] == "mfma_grid"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(path="mfma_grid", **big))] == "mfma_grid"
     # the streaming kernel needs block_size >= 16 and at most 1024 sequences
-    assert pa.PATH_NAME[pa.resolved_path(_desc(block_size=8, k_strides=(2048, 1024, 128)))] == "mfma_grid"
-    assert pa.PATH_NAME[pa.resolved_path(_desc(batch=1025))] == "mfma_grid"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(block_size=8, max_blocks_per_seq=16384, num_blocks=32768,
+                                               k_strides=(2048, 1024, 128)))] == "mfma_grid"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(batch=1025, **big))] == "mfma_grid"
     assert pa.PATH_NAME[pa.resolved_path(_desc(kv_dtype="f32", k_strides=(4096, 2048, 128)))] == "valu"
     assert pa.PATH_NAME[pa.resolved_path(_desc(path="valu"))] == "valu"
 
@@ -165,7 +173,7 @@ def test_partition_size_choice_and_workspace():
                                    **fz)) == 4096
     # the streaming kernel: partition states, links, one continuation state per wave
     for part, mbs, batch in ((512, 16, 2), (64, 16, 2), (512, 2048, 64)):
-        d = _desc(partition_size=part, max_blocks_per_seq=mbs, batch=batch)
+        d = _desc(partition_size=part, max_blocks_per_seq=mbs, batch=batch, path="mfma_stream")
         assert pa.PATH_NAME[pa.resolved_path(d)] == "mfma_stream"
         pmax = -(-mbs * 16 // part)
         rows = batch * 8 * pmax
@@ -175,7 +183,9 @@ def test_partition_size_choice_and_workspace():
         assert pa.workspace_size(d) == want, (part, mbs, batch)
     # automatic choice: 4096 for the streaming kernel; for the others 512,
     # halved while the grid would be small
-    assert pa.partition_size(_desc(batch=1, max_blocks_per_seq=6250, num_blocks=6250)) == 4096
+    assert pa.partition_size(_desc(batch=1, max_blocks_per_seq=6250, num_blocks=6250,
+                                   path="mfma_stream")) == 4096
+    assert pa.partition_size(_desc(batch=1, max_blocks_per_seq=16384, num_blocks=16384)) == 4096
     auto = pa.partition_size(_desc(batch=1, max_blocks_per_seq=6250, num_blocks=6250, path="mfma_grid"))
     assert auto in (64, 128, 256, 512)
     big = pa.partition_size(_desc(batch=64, num_kv_heads=8, num_q_heads=64, path="mfma_grid",
