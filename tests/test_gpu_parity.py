@@ -571,3 +571,32 @@ def test_bf16_q_and_out(torch_cuda, kv_dtype):
             assert torch.equal(o16, o32.to(torch.bfloat16)), (path, ps)
             got = o16.float().cpu().numpy().astype(np.float64)
             assert (np.abs(got - want) <= TOL[kv_dtype] + np.abs(want) * 2.0 ** -8).all(), (path, ps)
+
+
+def test_bf16_q_and_out_d256_and_merged_variant():
+    """bf16 q / out at head_dim 256 (the streaming kernel's pair of waves) and
+    on the single-launch merged variant: bit for bit the fp32 path's output
+    rounded to bf16, and within the K/V tolerance plus half a bf16 ulp of the
+    oracle."""
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rng = np.random.default_rng(99)
+    q = W.from_storage(W.to_storage(rng.standard_normal((3, 12, 256)).astype(np.float32), "bf16"),
+                       "bf16").astype(np.float32)
+    case, _, _ = paged_case(rng, B=3, Hq=12, Hkv=2, D=256, bs=16, kv_dtype="bf16",
+                            seqlens=[3000, 1, 700], q=q)
+    want = run_oracle(case)
+    dev = to_device(torch, case)
+    q16 = dev["q"].to(torch.bfloat16)
+    args = (dev["k"], dev["v"], dev["table"], dev["seqlens"], case.scale)
+    for path in ("mfma_stream", "mfma_grid", "mfma_fused"):
+        for ps in (256, 0):
+            o32 = pa.paged_attn_decode(dev["q"], *args, partition_size=ps, path=path)
+            o16 = pa.paged_attn_decode(q16, *args, partition_size=ps, path=path)
+            torch.cuda.synchronize()
+            assert o16.dtype == torch.bfloat16
+            assert torch.equal(o16, o32.to(torch.bfloat16)), (path, ps)
+            got = o16.float().cpu().numpy().astype(np.float64)
+            assert (np.abs(got - want) <= 3e-3 + np.abs(want) * 2.0 ** -8).all(), (path, ps)
