@@ -313,8 +313,9 @@ def read_probe(torch, steps: int = 10) -> dict:
     """Plain HBM read rates on the same GPU, for context next to the decode
     kernel: a 2 GiB buffer read front to back, and the same buffer read as 4 KB
     and 8 KB tiles in a seeded random order (the K tile of one (block, KV head)
-    at head_dim 128 and 256), one tile per wave at a time, 16-byte
-    non-temporal loads (libpaprobe.so)."""
+    at head_dim 128 and 256) by one-wave workgroups with three tiles in flight
+    each, the decode kernel's shape; 16-byte non-temporal loads
+    (libpaprobe.so)."""
     import ctypes
 
     from paged_gqa_decode_block_amd import build as B
@@ -332,7 +333,9 @@ def read_probe(torch, steps: int = 10) -> dict:
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     sink = torch.zeros(4 * blocks, dtype=torch.int32, device="cuda")
     st = torch.cuda.current_stream()
-    out = {"buffer_bytes": nbytes, "loads": "16-byte non-temporal", "workgroups": blocks}
+    out = {"buffer_bytes": nbytes, "loads": "16-byte non-temporal",
+           "sequential": f"{blocks} workgroups of 256 threads",
+           "tiles": f"{blocks} one-wave workgroups, three tiles in flight per wave"}
 
     def timed(fn) -> float:
         for _ in range(3):
@@ -513,6 +516,11 @@ def main():
     if not a.no_probe:
         probe = read_probe(torch)
         probe["decode_kernel_vs_stream_read"] = round(rl["achieved"] / probe["stream_read_gbs"], 4)
+        # against the gather of the workload's own K tile size (one block of one KV head)
+        tile_kb = wl.case.bs * wl.case.D * (4 if wl.case.kv_dtype == "f32" else 2) // 1024
+        if tile_kb in (4, 8):
+            probe["decode_kernel_vs_tile_gather"] = round(
+                rl["achieved"] / probe[f"tile_gather_{tile_kb}k_gbs"], 4)
         log(f"[bench] plain reads: {probe['stream_read_gbs']:.0f} GB/s sequential, "
             f"{probe['tile_gather_4k_gbs']:.0f} / {probe['tile_gather_8k_gbs']:.0f} GB/s as 4 / 8 KB tiles")
     cpu = None

@@ -8,10 +8,11 @@
 //                         non-temporal loads, grid-stride (the sequential
 //                         ceiling);
 //   pa_probe_tile_gather  whole tiles of tile_bytes (a multiple of 1 KB) read
-//                         in the order a table gives, one tile per wave at a
-//                         time, 16-byte non-temporal loads (the shape of a
-//                         paged K/V read: one (block, KV head) tile per
-//                         16-token chunk).
+//                         in the order a table gives, one wave per workgroup
+//                         with three tiles in flight, 16-byte non-temporal
+//                         loads (the shape of the decode kernel's paged K/V
+//                         reads: one (block, KV head) tile per 16-token
+//                         chunk, a short ring of chunks per wave).
 //
 // Both fold what they read into one word per thread and store it only if it
 // equals a constant the data practically never produces, so the loads stay
@@ -42,21 +43,29 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restric
   if (acc == kNever) sink[blockIdx.x] = acc;
 }
 
-__global__ void __launch_bounds__(256) tile_gather_kernel(const char* __restrict__ pool,
-                                                          const int32_t* __restrict__ tiles,
-                                                          int ntiles, int tile_kb, uint32_t* sink) {
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * 4;
+// One wave per workgroup; wave w reads tiles w, w + n, w + 2n, ... (n waves),
+// three tiles in flight (all loads of three tiles issued before any is used).
+__global__ void __launch_bounds__(64) tile_gather_kernel(const char* __restrict__ pool,
+                                                         const int32_t* __restrict__ tiles,
+                                                         int ntiles, int tile_kb, uint32_t* sink) {
+  const int lane = threadIdx.x;
+  const int wave = blockIdx.x;
+  const int nwaves = gridDim.x;
   uint32_t acc = 0;
-  for (int t = wave; t < ntiles; t += nwaves) {
-    const u32x4* base = (const u32x4*)(pool + (int64_t)tiles[t] * tile_kb * 1024) + lane;
-    u32x4 v[16];
+  for (int t0 = wave; t0 < ntiles; t0 += 3 * nwaves) {
+    u32x4 v[3][16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      v[j] = j < tile_kb ? __builtin_nontemporal_load(base + 64 * j) : u32x4{0, 0, 0, 0};
+    for (int k = 0; k < 3; ++k) {
+      const int t = t0 + k * nwaves;
+      const u32x4* base = (const u32x4*)(pool + (int64_t)tiles[t < ntiles ? t : t0] * tile_kb * 1024) + lane;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+      for (int j = 0; j < 16; ++j)
+        v[k][j] = (t < ntiles && j < tile_kb) ? __builtin_nontemporal_load(base + 64 * j) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc ^= v[k][j].x ^ v[k][j].y ^ v[k][j].z ^ v[k][j].w;
   }
   if (acc == kNever) sink[wave] = acc;
 }
@@ -71,13 +80,14 @@ extern "C" int pa_probe_stream_read(const void* buf, int64_t bytes, uint32_t* si
   return (int)hipGetLastError();
 }
 
-// sink holds at least blocks * 4 words; tile_bytes is 1..16 KB in whole KB
+// blocks: waves (one per workgroup); sink holds at least blocks words; tile_bytes is
+// 1..16 KB in whole KB
 extern "C" int pa_probe_tile_gather(const void* pool, const int32_t* tiles, int ntiles,
                                     int tile_bytes, uint32_t* sink, int blocks, hipStream_t s) {
   if (!pool || !tiles || !sink || ntiles <= 0 || tile_bytes <= 0 || tile_bytes % 1024 ||
       tile_bytes > 16384 || blocks <= 0)
     return -1;
-  hipLaunchKernelGGL(tile_gather_kernel, dim3(blocks), dim3(256), 0, s, (const char*)pool, tiles, ntiles,
+  hipLaunchKernelGGL(tile_gather_kernel, dim3(blocks), dim3(64), 0, s, (const char*)pool, tiles, ntiles,
                      tile_bytes / 1024, sink);
   return (int)hipGetLastError();
 }
