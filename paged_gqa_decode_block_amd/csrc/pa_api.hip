@@ -220,7 +220,8 @@ int validate(const pa_desc* d) {
 // arrival word per (sequence, KV head) (at offset 0 for every descriptor; zero
 // before the first call and left zero by every call), then partition states
 // m, l, acc for every (sequence, query head, partition), then for the
-// streaming kernel the partition links and one continuation state per wave.
+// streaming kernel the partition links and one continuation state per wave
+// (per pair of waves at head_dim 256).
 // Kernels other than the streaming one need nothing when one partition always
 // suffices.
 enum { kWsCnt, kWsM, kWsL, kWsAcc, kWsLink, kWsCm, kWsCl, kWsCacc, kWsCmore, kWsParts };

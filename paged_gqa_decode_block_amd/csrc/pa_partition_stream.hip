@@ -3,8 +3,8 @@
 // The split-KV decomposition (page "Paged Attention Kernel Architecture for
 // BI-V100", sections 4 and 6) is counted in 16-token chunks: each (sequence b,
 // KV head) token stream has ceil(L_b / 16) of them, numbered sequence by
-// sequence, KV head by KV head. One or two waves per SIMD are launched (a
-// multiple of the compute-unit count) and the waves in use take equal
+// sequence, KV head by KV head. Two waves per SIMD (by default) are launched
+// (a multiple of the compute-unit count) and the waves in use take equal
 // contiguous shares of the chunks, so every compute unit streams the same number
 // of bytes. A share mostly walks one stream. Along a stream the wave keeps a
 // ring of NBUF 16-token chunks of K and V in flight in registers; the ring's
