@@ -107,13 +107,14 @@ class Workload:
         self.stream = torch.cuda.current_stream()
         torch.cuda.synchronize()
 
-    def call(self, phase="both"):
+    def call(self, phase="both", stream=None):
         import paged_gqa_decode_block_amd as pa
 
+        st = self.stream.cuda_stream if stream is None else stream
         rc = pa.decode_raw(self.desc, self.q.data_ptr(), self.k_pool.data_ptr(),
                            self.v_pool.data_ptr(), self.table.data_ptr(), self.seqlens.data_ptr(),
                            self.case.scale, self.out.data_ptr(), self.ws.data_ptr(),
-                           self.ws.numel(), 0, self.stream.cuda_stream, phase)
+                           self.ws.numel(), 0, st, phase)
         if rc != 0:
             raise pa.PagedAttnError(rc, "bench: ")
 
@@ -170,6 +171,22 @@ def measure(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
     wl.call()  # leave the workspace of a complete call behind for the combine timing
     comb_ms = time_steps(torch, lambda: wl.call("combine"), steps)
     step_each = time_each(torch, wl.call, steps)
+    # the same step captured once in a HIP graph and replayed (the call
+    # allocates nothing and never synchronises, so it captures as is)
+    wl.call()
+    torch.cuda.synchronize()
+    eager_out = wl.out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wl.call(stream=torch.cuda.current_stream().cuda_stream)
+    same = True
+    for _ in range(3):
+        wl.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        same = same and bool(torch.equal(wl.out, eager_out))
+    graph_ms = time_steps(torch, g.replay, steps)
+    del g
     cold_ms = time_each(torch, wl.call, max(5, steps // 4), flush=lambda: flush_buf.add_(1))
     c = wl.case
     t = ms / 1e3
@@ -182,6 +199,8 @@ def measure(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
                                         float(np.percentile(part_ms, 90) * 1e3)],
         "combine_kernel_us": float(comb_ms * 1e3),
         "step_us_p10_p50_p90": [float(np.percentile(step_each, x) * 1e3) for x in (10, 50, 90)],
+        "graph_step_us": float(graph_ms * 1e3),
+        "graph_output_equals_step": same,
         "cold_ms_median": float(np.median(cold_ms)),
         "cold_kv_gbs": wl.kv_bytes / (np.median(cold_ms) / 1e3) / 1e9,
         "kv_bytes": wl.kv_bytes,
