@@ -53,7 +53,7 @@ typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } 
  * MFMA_GRID, one workgroup per partition (any block size and batch).
  * PA_PATH_MFMA picks MFMA_STREAM when it applies and the batch's K/V bound
  * (batch * num_kv_heads * max_blocks_per_seq * block_size * head_dim * 2
- * elements) is at least 256 MB, else MFMA_GRID (on smaller batches the
+ * elements) is at least 160 MB, else MFMA_GRID (on smaller batches the
  * persistent waves' start-up is not amortised); AUTO picks MFMA that way for
  * 16-bit K/V and VALU for fp32.
  *

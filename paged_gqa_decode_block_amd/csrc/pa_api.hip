@@ -70,16 +70,16 @@ int pick_partition(const pa_desc* d) {
 
 // Whether the persistent streaming kernel beats the one-workgroup-per-
 // partition grid kernel: only on batches whose K/V (bounded by
-// max_blocks_per_seq * block_size tokens per sequence) reaches 256 MB. Below
+// max_blocks_per_seq * block_size tokens per sequence) reaches 160 MB. Below
 // that each persistent wave gets a short share and its start-up (lengths,
 // table, then K/V, about 10 us) is not amortised, while the grid kernel starts
-// every partition at once: on one MI355X the grid kernel measured 0.6-0.9x the
-// streaming kernel's time up to 270 MB and the streaming kernel won from
-// 400 MB (the 100K-token batch) up.
+// every partition at once. On one MI355X the grid kernel took 0.6-0.9x the
+// streaming kernel's time up to 128 MB; from 192 MB the streaming kernel was
+// faster in three of four shapes and from 320 MB in all.
 bool stream_pays(const pa_desc* d) {
   const int64_t elem = d->kv_dtype == PA_DTYPE_F32 ? 4 : 2;
   const int64_t bytes = (int64_t)d->batch * d->num_kv_heads * max_tokens(d) * d->head_dim * elem * 2;
-  return bytes >= ((int64_t)256 << 20);
+  return bytes >= ((int64_t)160 << 20);
 }
 
 // The kernel a descriptor runs on: PA_PATH_VALU, PA_PATH_MFMA_GRID or

@@ -63,15 +63,15 @@ def _desc(**kw):
 
 def test_valid_descriptor_and_resolved_path():
     assert pa.validate(_desc()) == 0
-    # below 256 MB of K/V (by the max_blocks_per_seq bound) the grid kernel; at
+    # below 160 MB of K/V (by the max_blocks_per_seq bound) the grid kernel; at
     # and above it the streaming kernel, where it applies
-    big = dict(max_blocks_per_seq=8192, num_blocks=16384)   # 2 * 2 * 131072 * 128 * 2 * 2 B = 256 MiB
+    big = dict(max_blocks_per_seq=5120, num_blocks=16384)   # 2 * 2 * 81920 * 128 * 2 * 2 B = 160 MiB
     assert pa.PATH_NAME[pa.resolved_path(_desc())] == "mfma_grid"
     assert pa.PATH_NAME[pa.resolved_path(_desc(path="mfma"))] == "mfma_grid"
     assert pa.PATH_NAME[pa.resolved_path(_desc(path="mfma_stream"))] == "mfma_stream"
     assert pa.PATH_NAME[pa.resolved_path(_desc(**big))] == "mfma_stream"
     assert pa.PATH_NAME[pa.resolved_path(_desc(path="mfma", **big))] == "mfma_stream"
-    assert pa.PATH_NAME[pa.resolved_path(_desc(max_blocks_per_seq=8191, num_blocks=16384))] == "mfma_grid"
+    assert pa.PATH_NAME[pa.resolved_path(_desc(max_blocks_per_seq=5119, num_blocks=16384))] == "mfma_grid"
     assert pa.PATH_NAME[pa.resolved_path(_desc(path="mfma_grid", **big))] == "mfma_grid"
     # the streaming kernel needs block_size >= 16 and at most 1024 sequences
     assert pa.PATH_NAME[pa.resolved_path(_desc(block_size=8, max_blocks_per_seq=16384, num_blocks=32768,
@@ -185,7 +185,7 @@ def test_partition_size_choice_and_workspace():
     # halved while the grid would be small
     assert pa.partition_size(_desc(batch=1, max_blocks_per_seq=6250, num_blocks=6250,
                                    path="mfma_stream")) == 4096
-    assert pa.partition_size(_desc(batch=1, max_blocks_per_seq=16384, num_blocks=16384)) == 4096
+    assert pa.partition_size(_desc(max_blocks_per_seq=5120, num_blocks=16384)) == 4096
     auto = pa.partition_size(_desc(batch=1, max_blocks_per_seq=6250, num_blocks=6250, path="mfma_grid"))
     assert auto in (64, 128, 256, 512)
     big = pa.partition_size(_desc(batch=64, num_kv_heads=8, num_q_heads=64, path="mfma_grid",
