@@ -9,6 +9,13 @@ H_q=24, H_kv=4, d=256, partition 512), the prefix-shared 256-sequence batch, and
 fp16 batch are measured too and reported under "also". Prints one JSON line on
 stdout; progress goes to stderr.
 
+Each step is timed two ways: flushed (a 1 GiB read evicts the L2s and the
+256 MB MALL before every timed step, an event pair around the step alone; the
+median of the K steps is ``ms_per_step`` and ``value``) and warm (K back-to-back
+steps between one event pair, reported as ``warm_ms_per_step``). The CPU
+baseline leg also compares the last timed step's whole output with the fp64
+oracle (``max_abs_err``, ``parity``).
+
   python bench.py [--steps K] [--warmup W] [--config 4] [--also 3]
   python bench.py --profile partition   # only partition-kernel launches (for rocprofv3)
   python bench.py --profile copy        # a 1 GiB device copy (counter calibration)
@@ -58,13 +65,15 @@ class Workload:
     """One generated configuration, copied to the GPU once."""
 
     def __init__(self, k: int, torch, path: str, partition: int | None = None,
-                 layout: str = "HND"):
+                 layout: str = "HND", case=None):
         from paged_gqa_decode_block_amd import workload as W
         import paged_gqa_decode_block_amd as pa
 
-        t = time.time()
-        self.case = c = W.make_config(k)
-        log(f"[bench] generated config {k} ({c.name}) in {time.time() - t:.1f}s")
+        if case is None:  # the tests hand in a case they generated already
+            t = time.time()
+            case = W.make_config(k)
+            log(f"[bench] generated config {k} ({case.name}) in {time.time() - t:.1f}s")
+        self.case = c = case
         self.k = k
         self.torch = torch
         self.path = path
@@ -158,10 +167,21 @@ def time_each(torch, fn, steps: int, flush=None) -> np.ndarray:
     return np.array([a.elapsed_time(b) for a, b in ev])
 
 
+def flush_caches(flush_buf):
+    """Evict the decode's data from the L2s and the 256 MB MALL: read a 1 GiB
+    buffer (a read, so no dirty lines are left to be written back during the
+    next step)."""
+    flush_buf.sum()
+
+
 def measure(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
+    """The step timed two ways: flushed (each step after a cache flush, its own
+    event pair; the median is the headline) and warm (``steps`` back-to-back
+    calls between one event pair)."""
     torch = wl.torch
     for _ in range(warmup):
         wl.call()
+    cold_ms = time_each(torch, wl.call, steps, flush=lambda: flush_caches(flush_buf))
     ms = time_steps(torch, wl.call, steps)
     # the partition kernel alone: one event pair around `steps` back-to-back
     # launches on the launch stream (average launch duration), plus per-launch
@@ -187,22 +207,25 @@ def measure(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
         same = same and bool(torch.equal(wl.out, eager_out))
     graph_ms = time_steps(torch, g.replay, steps)
     del g
-    cold_ms = time_each(torch, wl.call, max(5, steps // 4), flush=lambda: flush_buf.add_(1))
+    wl.call()
+    torch.cuda.synchronize()
     c = wl.case
-    t = ms / 1e3
+    cold = float(np.median(cold_ms))
+    t = cold / 1e3
     return {
-        "ms_per_step": ms,
+        "ms_per_step": cold,
         "kv_gbs": wl.kv_bytes / t / 1e9,
         "seq_heads_per_s": c.B * c.Hq / t,
+        "cold_step_us_p10_p50_p90": [float(np.percentile(cold_ms, x) * 1e3) for x in (10, 50, 90)],
+        "warm_ms_per_step": ms,
+        "warm_kv_gbs": wl.kv_bytes / (ms / 1e3) / 1e9,
         "partition_kernel_us": float(part_avg_ms * 1e3),
         "partition_kernel_us_p10_p90": [float(np.percentile(part_ms, 10) * 1e3),
                                         float(np.percentile(part_ms, 90) * 1e3)],
         "combine_kernel_us": float(comb_ms * 1e3),
-        "step_us_p10_p50_p90": [float(np.percentile(step_each, x) * 1e3) for x in (10, 50, 90)],
+        "warm_step_us_p10_p50_p90": [float(np.percentile(step_each, x) * 1e3) for x in (10, 50, 90)],
         "graph_step_us": float(graph_ms * 1e3),
         "graph_output_equals_step": same,
-        "cold_ms_median": float(np.median(cold_ms)),
-        "cold_kv_gbs": wl.kv_bytes / (np.median(cold_ms) / 1e3) / 1e9,
         "kv_bytes": wl.kv_bytes,
         "unique_kv_bytes": wl.unique_kv_bytes,
         # prefix-shared blocks counted once (equal to kv_gbs when no block is shared)
@@ -375,6 +398,19 @@ def read_probe(torch, steps: int = 10) -> dict:
         out[f"tile_gather_{kb}k_gbs"] = round(timed(lambda: run(lib.pa_probe_tile_gather(
             buf.data_ptr(), tiles.data_ptr(), ntiles, kb * 1024, sink.data_ptr(), blocks,
             st.cuda_stream))), 1)
+        if kb == 8:
+            # one read of as many bytes as the 100K-token decode moves (409.6 MB,
+            # 50000 random 8 KB tiles): the bare gather's time for that size,
+            # start-up and tail included
+            n3 = 409_600_000 // 8192
+            for _ in range(3):
+                run(lib.pa_probe_tile_gather(buf.data_ptr(), tiles.data_ptr(), n3, 8192,
+                                             sink.data_ptr(), blocks, st.cuda_stream))
+            ms3 = time_steps(torch, lambda: run(lib.pa_probe_tile_gather(
+                buf.data_ptr(), tiles.data_ptr(), n3, 8192, sink.data_ptr(), blocks,
+                st.cuda_stream)), steps)
+            out["tile_gather_8k_409mb_us"] = round(ms3 * 1e3, 2)
+            out["tile_gather_8k_409mb_gbs"] = round(n3 * 8192 / (ms3 / 1e3) / 1e9, 1)
         del tiles
     del buf, sink
     torch.cuda.empty_cache()
@@ -390,6 +426,30 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+PARITY_TOL = {"f32": 1e-5, "f16": 3e-3, "bf16": 3e-3}
+
+
+def cpu_baseline_parity(wl: Workload, got: np.ndarray) -> dict:
+    """Part of the CPU-baseline leg: the fp64 oracle over the whole batch of the
+    workload, compared element by element with the output of the last timed
+    step (``got``, [B, H_q, d] as floats). The tolerance is the one the GPU
+    tests hold: 1e-5 for fp32 K/V, 3e-3 for 16-bit K/V."""
+    from oracle import oracle as O
+
+    c = wl.case
+    t0 = time.perf_counter()
+    want = O.paged_attn_decode(c.q, c.k_pool, c.v_pool, c.block_table, c.seqlens, c.scale,
+                               kv_dtype=c.kv_dtype, block_size=c.bs, num_kv_heads=c.Hkv,
+                               layout=c.layout)
+    dt = time.perf_counter() - t0
+    finite = bool(np.isfinite(got).all())
+    err = float(np.abs(got.astype(np.float64) - want).max()) if got.size else 0.0
+    tol = PARITY_TOL[c.kv_dtype]
+    return {"max_abs_err": err, "tol": tol, "values": int(got.size), "finite": finite,
+            "pass": finite and err <= tol, "oracle_seconds": round(dt, 2),
+            "compared": "every (sequence, query head, dim) output of the last timed step"}
 
 
 def cpu_baseline(wl: Workload, budget_s: float) -> dict:
@@ -509,10 +569,12 @@ def main():
 
     flush_buf = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > 256 MB MALL
     r = measure(wl, a.steps, a.warmup, flush_buf)
+    got = wl.out.float().cpu().numpy()  # the last timed step's output
     r.update(measure_append_graph(wl, a.steps))
     log(f"[bench] {wl.case.name}: append + decode step as a graph replay "
         f"{r['append_graph_step_us']:.1f} us (output equals the plain step: {r['append_output_equals_decode']})")
-    log(f"[bench] {wl.case.name}: {r['ms_per_step'] * 1e3:.1f} us/step, {r['kv_gbs']:.0f} GB/s")
+    log(f"[bench] {wl.case.name}: {r['ms_per_step'] * 1e3:.1f} us/step flushed "
+        f"({r['warm_ms_per_step'] * 1e3:.1f} warm), {r['kv_gbs']:.0f} GB/s")
     rl = roofline(wl, r)
     also = {}
     for k in [int(x) for x in a.also.split(",") if x.strip()]:
@@ -520,11 +582,16 @@ def main():
             continue
         w2 = Workload(k, torch, a.path, a.partition, a.layout)
         r2 = measure(w2, a.steps, a.warmup, flush_buf)
-        log(f"[bench] {w2.case.name}: {r2['ms_per_step'] * 1e3:.1f} us/step, {r2['kv_gbs']:.0f} GB/s")
+        log(f"[bench] {w2.case.name}: {r2['ms_per_step'] * 1e3:.1f} us/step flushed "
+            f"({r2['warm_ms_per_step'] * 1e3:.1f} warm), {r2['kv_gbs']:.0f} GB/s")
         also[w2.case.name] = {**w2.describe(), **{k2: (round(v, 4) if isinstance(v, float) else v)
                                                   for k2, v in r2.items()},
                               "pct_hbm_peak": round(100 * r2["kv_gbs"] / HBM_PEAK_GBS, 2),
                               "roofline": roofline(w2, r2)}
+        if not a.no_cpu_baseline:
+            also[w2.case.name]["parity"] = cpu_baseline_parity(w2, w2.out.float().cpu().numpy())
+            log(f"[bench] {w2.case.name}: max-abs error vs the oracle "
+                f"{also[w2.case.name]['parity']['max_abs_err']:.2e}")
         del w2
         torch.cuda.empty_cache()
     prefill = {}
@@ -543,9 +610,12 @@ def main():
         log(f"[bench] plain reads: {probe['stream_read_gbs']:.0f} GB/s sequential, "
             f"{probe['tile_gather_4k_gbs']:.0f} / {probe['tile_gather_8k_gbs']:.0f} GB/s as 4 / 8 KB tiles")
     cpu = None
+    parity = None
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")
         cpu = cpu_baseline(wl, a.cpu_seconds)
+        parity = cpu_baseline_parity(wl, got)
+        log(f"[bench] {wl.case.name}: max-abs error vs the oracle {parity['max_abs_err']:.2e}")
     line = {
         "metric": METRIC,
         "value": round(r["kv_gbs"], 1),
@@ -565,6 +635,8 @@ def main():
         "detail": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()},
         "roofline": rl,
         "cpu_baseline": cpu,
+        "max_abs_err": None if parity is None else parity["max_abs_err"],
+        "parity": parity,
         "read_probe": probe,
         "also": also,
         "prefill": prefill,

@@ -71,6 +71,11 @@ class OracleError(RuntimeError):
     pass
 
 
+def default_threads() -> int:
+    """Worker threads when the caller names none: the host's cores, at most 16."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def pool_strides(layout: str, Hkv: int, bs: int, D: int) -> tuple[int, int, int]:
     """(block, head, token) strides in elements for the two supported pool layouts."""
     if layout == "HND":  # [NB, H_kv, bs, D]
@@ -112,7 +117,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_table, seqlens, scale, *, kv_dtyp
     pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
     out = np.zeros((pairs.shape[0], D), dtype=np.float64)
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        nthreads = default_threads()
     rc = lib.oracle_paged_attn_pairs(
         B, Hq, num_kv_heads, D, block_size, NB, MBS, _DTYPE_CODE[kv_dtype],
         q.ctypes.data, k_pool.ctypes.data, v_pool.ctypes.data, ks.ctypes.data, ks.ctypes.data,
@@ -124,7 +129,8 @@ def paged_attn_decode(q, k_pool, v_pool, block_table, seqlens, scale, *, kv_dtyp
 
 
 def paged_attn_prefill(q, k_pool, v_pool, block_table, cu_seqlens_q, seqlens_k, scale, *, causal,
-                       kv_dtype, block_size, num_kv_heads, layout="HND", pairs=None):
+                       kv_dtype, block_size, num_kv_heads, layout="HND", pairs=None,
+                       nthreads=None):
     """fp64 outputs of the paged varlen prefill.
 
     ``q`` is ``[total_q, H_q, D]``; rows ``cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1``
@@ -133,7 +139,10 @@ def paged_attn_prefill(q, k_pool, v_pool, block_table, cu_seqlens_q, seqlens_k, 
     (the new ones included). With ``causal`` row i of a sequence with q_len
     queries and L keys attends tokens ``[0, L - q_len + i]`` (none when that is
     negative, giving zeros), else all L. Returns ``[total_q, H_q, D]`` float64,
-    or ``[len(pairs), D]`` for an ``[n, 2]`` array of (row, h).
+    or ``[len(pairs), D]`` for an ``[n, 2]`` array of (row, h). The pairs are
+    split into ``nthreads`` contiguous slices, each computed by its own call
+    into the C function on a worker thread (the calls release the GIL); the
+    arithmetic of every pair is the same whatever the split.
     """
     lib = _load()
     q = np.ascontiguousarray(q, dtype=np.float32)
@@ -156,11 +165,27 @@ def paged_attn_prefill(q, k_pool, v_pool, block_table, cu_seqlens_q, seqlens_k, 
         pairs = np.stack([rr.ravel(), hh.ravel()], axis=1)
     pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
     out = np.zeros((pairs.shape[0], D), dtype=np.float64)
-    rc = lib.oracle_paged_prefill_pairs(
-        B, Hq, num_kv_heads, D, block_size, NB, MBS, _DTYPE_CODE[kv_dtype],
-        q.ctypes.data, k_pool.ctypes.data, v_pool.ctypes.data, ks.ctypes.data, ks.ctypes.data,
-        table.ctypes.data, cu.ctypes.data, sk.ctypes.data, int(bool(causal)),
-        float(np.float32(scale)), pairs.ctypes.data, pairs.shape[0], out.ctypes.data)
+    n = pairs.shape[0]
+    if nthreads is None:
+        nthreads = default_threads()
+    nthreads = max(1, min(int(nthreads), n))
+
+    def run(lo, hi):
+        return lib.oracle_paged_prefill_pairs(
+            B, Hq, num_kv_heads, D, block_size, NB, MBS, _DTYPE_CODE[kv_dtype],
+            q.ctypes.data, k_pool.ctypes.data, v_pool.ctypes.data, ks.ctypes.data, ks.ctypes.data,
+            table.ctypes.data, cu.ctypes.data, sk.ctypes.data, int(bool(causal)),
+            float(np.float32(scale)), pairs[lo:hi].ctypes.data, hi - lo, out[lo:hi].ctypes.data)
+
+    cuts = [n * i // nthreads for i in range(nthreads + 1)]
+    if nthreads == 1:
+        codes = [run(0, n)]
+    else:
+        import concurrent.futures as cf
+
+        with cf.ThreadPoolExecutor(nthreads) as ex:
+            codes = list(ex.map(run, cuts[:-1], cuts[1:]))
+    rc = next((c for c in codes if c != 0), 0)
     if rc != 0:
         raise OracleError(f"oracle: {ERRORS.get(rc, rc)}")
     return out.reshape(total_q, Hq, D) if full else out

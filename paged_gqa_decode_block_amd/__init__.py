@@ -22,6 +22,7 @@ from .block_manager import BlockManager, copy_blocks  # noqa: E402,F401
 _TORCH_DTYPE_NAME = {"torch.float32": "f32", "torch.float16": "f16", "torch.bfloat16": "bf16"}
 _ws_cache: dict = {}
 _ws_zero: dict = {}  # merged-grid workspaces: leading bytes known to be zero
+_ws_retired: list = []  # outgrown workspaces, kept alive for graphs captured with them
 
 
 def _kv_dtype(t) -> str:
@@ -89,29 +90,51 @@ def _check_out(q, out):
         raise ValueError("out must be a contiguous tensor of q's shape and dtype")
 
 
-def workspace_for(desc: PaDesc, device):
-    """A cached device workspace of at least workspace_size(desc) bytes.
+def _on_stream(torch, stream, device):
+    """Context in which torch enqueues on the raw stream handle ``stream``."""
+    import contextlib
 
-    The merged-grid path (``mfma_fused``) gets a workspace of its own whose
+    if int(stream) == torch.cuda.current_stream(device).cuda_stream:
+        return contextlib.nullcontext()
+    return torch.cuda.stream(torch.cuda.ExternalStream(int(stream), device=device))
+
+
+def workspace_for(desc: PaDesc, device, stream=None):
+    """A cached device workspace of at least workspace_size(desc) bytes for calls
+    enqueued on ``stream`` (a raw stream handle; torch's current stream when
+    None).
+
+    One workspace is kept per (device, stream, merged-grid or not): calls on one
+    stream are ordered, so they may share it; calls on different streams get
+    different ones. A workspace that a later call outgrows is replaced but never
+    freed, because a HIP graph captured with it keeps its address and may still
+    be replayed. The merged-grid path (``mfma_fused``) gets a workspace whose
     leading batch * num_kv_heads int32 arrival counters are zero: allocated
-    zeroed, and zeroed again when a call needs more counters than the calls
-    before it left zero (each call leaves its own counters zero)."""
+    zeroed, and zeroed again, on the launch stream, when a call needs more
+    counters than the calls before it left zero (each call leaves its own
+    counters zero)."""
     import torch
 
     n = workspace_size(desc)
     if n == 0:
         return None
+    if stream is None:
+        stream = torch.cuda.current_stream(device).cuda_stream
     fused = resolved_path(desc) == PA_PATH["mfma_fused"]
-    key = (str(device), fused)
+    key = (str(device), int(stream), fused)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < n:
-        ws = (torch.zeros if fused else torch.empty)(n, dtype=torch.uint8, device=device)
+        if ws is not None:
+            _ws_retired.append(ws)
+        with _on_stream(torch, stream, device):
+            ws = (torch.zeros if fused else torch.empty)(n, dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
         _ws_zero[key] = ws.numel() if fused else 0
     if fused:
         cnt_bytes = 4 * desc.batch * desc.num_kv_heads
         if cnt_bytes > _ws_zero[key]:
-            ws[:cnt_bytes].zero_()
+            with _on_stream(torch, stream, device):
+                ws[:cnt_bytes].zero_()
         _ws_zero[key] = cnt_bytes
     return ws
 
@@ -140,12 +163,12 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, ou
     if out is None:
         out = torch.empty_like(q)
     _check_out(q, out)
-    if workspace is None:
-        workspace = workspace_for(desc, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
+    if workspace is None:
+        workspace = workspace_for(desc, q.device, stream)
     rc = decode_raw(
         desc, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
         cache_seqlens.data_ptr(), float(scale), out.data_ptr(),
@@ -180,12 +203,12 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cac
     if out is None:
         out = torch.empty_like(q)
     _check_out(q, out)
-    if workspace is None:
-        workspace = workspace_for(desc, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
+    if workspace is None:
+        workspace = workspace_for(desc, q.device, stream)
     rc = decode_append_raw(
         desc, q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
         v_cache.data_ptr(), block_table.data_ptr(), cache_seqlens.data_ptr(), float(scale),

@@ -514,8 +514,11 @@ hipError_t launch_t(const Params& p, hipStream_t s) {
   constexpr int NBUF = kVariants[V][dim_index(D)][0], OCC = kVariants[V][dim_index(D)][1];
   constexpr bool QL = kVariants[V][dim_index(D)][2] != 0;
   constexpr int DS = kVariants[V][dim_index(D)][3];
-  const int64_t bound = (int64_t)p.B * p.Hkv * (((int64_t)p.MBS << p.bs_log2) + 15) / 16;
-  const int workers = stream_grid(D, V, p.cus, bound);  // waves, or pairs when DS = 2
+  // The grid is the host's wave count (waves, or pairs when DS = 2), the same
+  // number that sized the workspace's continuation slots: one slot per
+  // workgroup of the launch.
+  const int workers = p.nwaves;
+  if (workers <= 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((partition_stream_kernel<T, D, NBUF, OCC, POL, QL, QO, DS>), dim3(workers),
                      dim3(64 * DS), 0, s, p);
   return hipGetLastError();

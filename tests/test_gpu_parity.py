@@ -10,7 +10,7 @@ import pytest
 
 import paged_gqa_decode_block_amd as pa
 from paged_gqa_decode_block_amd import workload as W
-from util_cases import paged_case, run_oracle
+from util_cases import config_case, config_oracle, paged_case, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -131,60 +131,7 @@ def test_peaked_softmax_keeps_tolerance(torch_cuda):
             assert np.abs(got - want).max() <= 3e-3, (dt, path)
 
 
-# --- the five workloads ------------------------------------------------------
-
-_CASES = {}
-
-
-def config_case(k):
-    if k not in _CASES:
-        _CASES.clear()  # keep one large workload in host memory at a time
-        _CASES[k] = W.make_config(k)
-    return _CASES[k]
-
-
-def sample_pairs(case, n, rng):
-    """All (b, h) pairs when few, else a sample that covers every sequence, every
-    KV head, the shortest and the longest sequence."""
-    if case.B * case.Hq <= n:
-        return None
-    b = np.concatenate([np.arange(case.B), rng.integers(0, case.B, size=max(0, n - case.B))])
-    h = rng.integers(0, case.Hq, size=b.size)
-    h[: case.Hkv] = np.arange(case.Hkv) * case.G
-    b[: case.Hkv] = int(np.argmax(case.seqlens))
-    b[case.Hkv: 2 * case.Hkv] = int(np.argmin(case.seqlens))
-    h[case.Hkv: 2 * case.Hkv] = np.arange(case.Hkv) * case.G + case.G - 1
-    return np.stack([b[:n], h[:n]], axis=1)
-
-
-@pytest.mark.parametrize("k,path", [(1, "valu")] + [
-    (k, path) for k in (2, 3, 4, 5) for path in ("mfma_stream", "mfma_grid", "valu")])
-def test_config_matches_oracle(torch_cuda, k, path):
-    case = config_case(k)
-    rng = np.random.default_rng(k)
-    pairs = sample_pairs(case, 192, rng)
-    want = run_oracle(case, pairs=pairs)
-    got = run_gpu(torch_cuda, case, path=path)
-    assert np.isfinite(got).all()
-    if pairs is not None:
-        got = got[pairs[:, 0], pairs[:, 1]]
-    err = np.abs(got - want).max()
-    print(f"config {k} {path}: max-abs error {err:.3e}")
-    assert err <= TOL[case.kv_dtype]
-
-
-def test_config5_shared_blocks_cacheable_loads(torch_cuda):
-    """The prefix-shared workload with the shared-blocks flag (cacheable K/V
-    loads) and the library's own partition choice."""
-    case = config_case(5)
-    rng = np.random.default_rng(55)
-    pairs = sample_pairs(case, 192, rng)
-    want = run_oracle(case, pairs=pairs)
-    for path in ("mfma_stream", "auto"):
-        got = run_gpu(torch_cuda, case, path=path, partition_size=0, kv_shared=True)
-        assert np.isfinite(got).all()
-        assert np.abs(got[pairs[:, 0], pairs[:, 1]] - want).max() <= 3e-3, path
-
+# --- the five workloads at full size are in test_gpu_configs.py ---------------
 
 def test_config1_combine_path(torch_cuda):
     """Config 1 with 32-token partitions: sequence 2 spans three partitions."""
@@ -279,11 +226,11 @@ def test_stream_kernel_thousand_sequences(torch_cuda):
     rng = np.random.default_rng(800)
     L = rng.integers(0, 120, size=1000)
     case, _, _ = paged_case(rng, B=1000, Hq=4, Hkv=2, D=64, bs=16, kv_dtype="bf16", seqlens=L)
-    pairs = np.stack([np.arange(1000), rng.integers(0, 4, size=1000)], axis=1)
-    want = run_oracle(case, pairs=pairs)
+    want = run_oracle(case)
     for ps in (32, 64):
         got = run_gpu(torch_cuda, case, path="mfma_stream", partition_size=ps)
-        assert np.abs(got[pairs[:, 0], pairs[:, 1]] - want).max() <= 3e-3, ps
+        assert np.isfinite(got).all(), ps
+        assert np.abs(got - want).max() <= 3e-3, ps
 
 
 def test_stream_kernel_continuation_chains(torch_cuda):
@@ -292,7 +239,7 @@ def test_stream_kernel_continuation_chains(torch_cuda):
     chunks), so each partition is pieced together from ten or more waves'
     continuation states."""
     case = config_case(3)
-    want = run_oracle(case)
+    want = config_oracle(3)
     for ps in (4096, 8192):
         got = run_gpu(torch_cuda, case, path="mfma_stream", partition_size=ps)
         assert np.isfinite(got).all()

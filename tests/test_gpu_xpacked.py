@@ -16,8 +16,7 @@ import pytest
 import paged_gqa_decode_block_amd as pa
 from paged_gqa_decode_block_amd import workload as W
 from test_gpu_parity import (  # noqa: F401  (torch_cuda is a fixture)
-    TOL, _append_case, _append_host, _new_token, config_case, run_gpu, sample_pairs, to_device,
-    torch_cuda)
+    TOL, _append_case, _append_host, _new_token, run_gpu, to_device, torch_cuda)
 from util_cases import paged_case, run_oracle
 
 pytestmark = pytest.mark.gpu
@@ -77,28 +76,6 @@ def test_xpacked_small_cases(torch_cuda, idx):
             ref = run_gpu(torch, case, dev_hnd, path="mfma_grid" if path == "auto" else path,
                           partition_size=ps)
             assert np.array_equal(got, ref), (name, path, ps)
-
-
-@pytest.mark.parametrize("k", [2, 3, 4, 5])
-def test_xpacked_configs(torch_cuda, k):
-    torch = torch_cuda
-    case = config_case(k)
-    if case.layout != "HND":
-        pytest.skip("workloads are drawn in the default layout")
-    rng = np.random.default_rng(k)
-    pairs = sample_pairs(case, 192, rng)
-    want = run_oracle(case, pairs=pairs)
-    ps = case.partition_size if k == 3 else 0
-    dev = to_device_xp(torch, case)
-    got = run_xp(torch, case, dev, partition_size=ps)
-    del dev
-    torch.cuda.empty_cache()
-    assert np.isfinite(got).all()
-    if pairs is not None:
-        got = got[pairs[:, 0], pairs[:, 1]]
-    err = np.abs(got - want).max()
-    print(f"config {k} x-packed: max-abs error {err:.3e}")
-    assert err <= TOL[case.kv_dtype]
 
 
 def test_xpacked_append(torch_cuda):

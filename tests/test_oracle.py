@@ -32,14 +32,23 @@ def test_f16_decoder_all_bit_patterns():
 
 
 def test_bf16_decoder_all_bit_patterns():
-    """bfloat16 is the upper half of binary32: compare with the widened bit pattern."""
+    """The oracle's bfloat16 decoder equals torch's own bfloat16 -> float64
+    widening (an implementation independent of the oracle's) on all 2^16
+    patterns: zeros of both signs, subnormals, normals, infinities and NaNs."""
+    import torch
+
     bits = np.arange(1 << 16, dtype=np.uint16)
     got = O.decode16(bits, "bf16")
-    with np.errstate(invalid="ignore"):
-        want = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(np.isnan(got), np.isnan(want))
     ok = ~np.isnan(want)
     assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))   # -0.0 stays negative
+    # spot values from the bfloat16 layout: 1 sign, 8 exponent (bias 127), 7 fraction bits
+    spots = {0x3F80: 1.0, 0xC000: -2.0, 0x3F81: 1.0 + 2.0 ** -7, 0x0001: 2.0 ** -133,
+             0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0x0080: 2.0 ** -126, 0x7F80: math.inf}
+    for b, v in spots.items():
+        assert O.decode16(np.array([b], dtype=np.uint16), "bf16")[0] == v, hex(b)
 
 
 # --- the docs page's worked example ----------------------------------------

@@ -89,3 +89,26 @@ def run_oracle(case, **kw):
     return O.paged_attn_decode(
         case.q, case.k_pool, case.v_pool, case.block_table, case.seqlens, case.scale,
         kv_dtype=case.kv_dtype, block_size=case.bs, num_kv_heads=case.Hkv, layout=case.layout, **kw)
+
+
+# One generated workload (and its whole-batch oracle output) is kept at a time:
+# the large ones take seconds to draw and gigabytes of host memory.
+_CONFIG = {}
+
+
+def config_case(k):
+    """Decode workload k (``workload.make_config``), cached while it is the
+    most recently requested one."""
+    if _CONFIG.get("k") != k:
+        _CONFIG.clear()
+        _CONFIG["k"] = k
+        _CONFIG["case"] = W.make_config(k)
+    return _CONFIG["case"]
+
+
+def config_oracle(k):
+    """The oracle's output for every (sequence, query head) of workload k."""
+    case = config_case(k)
+    if "want" not in _CONFIG:
+        _CONFIG["want"] = run_oracle(case)
+    return _CONFIG["want"]
