@@ -24,7 +24,8 @@
  *   - All array pointers given to paged_attn_decode are DEVICE pointers owned by
  *     the caller; the library never frees or keeps them after the call returns.
  *   - Nothing here allocates device memory. Partial results live in a caller
- *     workspace of paged_attn_workspace_size() bytes.
+ *     workspace of paged_attn_workspace_size() bytes (paged_attn_decode_static:
+ *     in a static array inside the library).
  *   - Functions return PA_OK (0) or a negative PA_E_* code; on error nothing is
  *     launched and nothing aborts. paged_attn_strerror() names the code.
  *   - Sizes are in elements unless they say bytes.
@@ -39,7 +40,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 /* Element type of the K and V caches. q and out are always float32. */
 typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype;
@@ -105,6 +106,8 @@ typedef enum pa_path {
 #define PA_E_SEQLEN (-13)     /* (check_inputs) a cache length < 0 or > MBS * bs     */
 #define PA_E_NOMEM (-14)      /* (block manager) not enough free blocks              */
 #define PA_E_SEQ (-15)        /* (block manager) unknown sequence, index or length   */
+#define PA_E_SCRATCH (-16)    /* (paged_attn_decode_static) the call needs more      */
+                              /* workspace than PA_STATIC_SCRATCH_BYTES               */
 
 /* pa_desc.flags bits. */
 #define PA_FLAG_KV_SHARED 1  /* physical blocks may be listed by several sequences   */
@@ -191,6 +194,35 @@ int paged_attn_decode(const pa_desc* desc, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_table,
                       const int32_t* cache_seqlens, float scale, void* out, void* workspace,
                       size_t workspace_bytes, int32_t* status, void* stream);
+
+/*
+ * paged_attn_decode without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, results and rules as
+ * paged_attn_decode, minus workspace and workspace_bytes: the partial states
+ * live in a static device array inside the library, PA_STATIC_SCRATCH_BYTES
+ * bytes on each device the library runs on, held until the process ends. Its
+ * address is looked up once per device, on the first call made with that
+ * device current. Nothing is allocated and nothing synchronises; the call
+ * enqueues the same kernels as paged_attn_decode on `stream`.
+ *
+ *   - A descriptor whose paged_attn_workspace_size() exceeds
+ *     PA_STATIC_SCRATCH_BYTES returns PA_E_SCRATCH and launches nothing (the
+ *     library's own partition choice keeps batches of up to a few million
+ *     cached tokens below it; a small explicit partition_size raises the need).
+ *   - PA_PATH_MFMA_FUSED returns PA_E_PATH: its arrival counters would have to
+ *     be zero in the shared array.
+ *   - Every call on a device uses that device's one array, which keeps the last
+ *     call's contents (no call relies on them). Calls that may overlap in time
+ *     on one device -- on different streams, or from several host threads
+ *     without ordering -- race on it; order them on one stream.
+ *   - PA_E_LAUNCH also reports a failure to look up the array's address.
+ */
+#define PA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int paged_attn_decode_static(const pa_desc* desc, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_table,
+                             const int32_t* cache_seqlens, float scale, void* out,
+                             int32_t* status, void* stream);
 
 /*
  * The decode step with the new token (page "Paged attention", decoding path:

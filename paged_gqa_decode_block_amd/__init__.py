@@ -11,8 +11,9 @@ from __future__ import annotations
 
 from ._lib import (  # noqa: F401
     EXPORTED, LIB_PATH, PA_DTYPE, PA_FLAG_KV_SHARED, PA_FLAG_KV_XPACKED, PA_FLAG_QO_BF16, PA_PATH, PA_STATUS_BAD_BLOCK,
-    PA_STATUS_BAD_SEQLEN, PATH_NAME,
-    PaDesc, PagedAttnError, check_inputs, decode_append_raw, decode_raw, load_library, make_desc,
+    PA_STATIC_SCRATCH_BYTES, PA_STATUS_BAD_SEQLEN, PATH_NAME,
+    PaDesc, PagedAttnError, check_inputs, decode_append_raw, decode_raw, decode_static_raw,
+    load_library, make_desc,
     partition_size, prefill_raw,
     resolved_path, strerror, validate, workspace_size,
 )
@@ -177,6 +178,36 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, ou
         status.data_ptr() if status is not None else 0, int(stream), phase)
     if rc != 0:
         raise PagedAttnError(rc, "paged_attn_decode: ")
+    return out
+
+
+def paged_attn_decode_static(q, k_cache, v_cache, block_table, cache_seqlens, scale, out, *,
+                             layout="HND", partition_size=0, path="auto", status=None, stream=None,
+                             kv_shared=False):
+    """``paged_attn_decode`` on the library's static scratch instead of a
+    workspace (paged_attn_decode_static in the C ABI): allocates nothing, so
+    ``out`` must be given. Raises PagedAttnError with PA_E_SCRATCH when the call
+    would need more than PA_STATIC_SCRATCH_BYTES of workspace. Calls that may
+    overlap in time on one GPU share the scratch and race; keep them on one
+    stream."""
+    import torch
+
+    if not q.is_cuda:
+        raise ValueError("paged_attn_decode_static runs on the GPU; q is on the CPU")
+    _check_q_tables(torch, q, block_table, cache_seqlens)
+    desc = desc_for(q, k_cache, v_cache, block_table, layout=layout,
+                    partition_size=partition_size, path=path, kv_shared=kv_shared)
+    _check_out(q, out)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = decode_static_raw(desc, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                           block_table.data_ptr(), cache_seqlens.data_ptr(), float(scale),
+                           out.data_ptr(), status.data_ptr() if status is not None else 0,
+                           int(stream))
+    if rc != 0:
+        raise PagedAttnError(rc, "paged_attn_decode_static: ")
     return out
 
 

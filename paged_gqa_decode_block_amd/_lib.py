@@ -21,8 +21,9 @@ PA_E = {
     -1: "PA_E_NULL", -2: "PA_E_SHAPE", -3: "PA_E_HEAD_DIM", -4: "PA_E_BLOCK_SIZE",
     -5: "PA_E_DTYPE", -6: "PA_E_STRIDE", -7: "PA_E_ALIGN", -8: "PA_E_PARTITION",
     -9: "PA_E_WORKSPACE", -10: "PA_E_PATH", -11: "PA_E_LAUNCH", -12: "PA_E_TABLE",
-    -13: "PA_E_SEQLEN",
+    -13: "PA_E_SEQLEN", -14: "PA_E_NOMEM", -15: "PA_E_SEQ", -16: "PA_E_SCRATCH",
 }
+PA_STATIC_SCRATCH_BYTES = 32 << 20
 PA_FLAG_KV_SHARED = 1
 PA_FLAG_QO_BF16 = 2
 PA_FLAG_KV_XPACKED = 4
@@ -30,7 +31,8 @@ PA_STATUS_BAD_BLOCK = 1
 PA_STATUS_BAD_SEQLEN = 2
 
 EXPORTED = (
-    "paged_attn_decode", "paged_attn_decode_append", "paged_attn_partition_phase",
+    "paged_attn_decode", "paged_attn_decode_static", "paged_attn_decode_append",
+    "paged_attn_partition_phase",
     "paged_attn_combine_phase", "paged_attn_prefill",
     "paged_attn_workspace_size", "paged_attn_validate", "paged_attn_partition_size", "paged_attn_resolved_path", "paged_attn_check_inputs",
     "paged_attn_strerror", "paged_attn_abi_version",
@@ -90,6 +92,8 @@ def load_library(path: str = LIB_PATH):
     dp = ctypes.POINTER(PaDesc)
     lib.paged_attn_decode.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz, vp, vp]
     lib.paged_attn_decode.restype = i32
+    lib.paged_attn_decode_static.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+    lib.paged_attn_decode_static.restype = i32
     lib.paged_attn_decode_append.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                              sz, vp, vp]
     lib.paged_attn_decode_append.restype = i32
@@ -198,6 +202,17 @@ def prefill_raw(desc: PaDesc, q_ptr: int, k_ptr: int, v_ptr: int, table_ptr: int
         ctypes.byref(desc), q_ptr or None, k_ptr or None, v_ptr or None, table_ptr or None,
         cu_q_ptr or None, seqlens_k_ptr or None, int(max_seqlen_q), int(bool(causal)),
         ctypes.c_float(scale), out_ptr or None, status_ptr or None, stream or None))
+
+
+def decode_static_raw(desc: PaDesc, q_ptr: int, k_ptr: int, v_ptr: int, table_ptr: int,
+                      seqlens_ptr: int, scale: float, out_ptr: int, status_ptr: int,
+                      stream: int) -> int:
+    """Direct call of paged_attn_decode_static (no workspace argument) with
+    integer device addresses."""
+    return int(load_library().paged_attn_decode_static(
+        ctypes.byref(desc), q_ptr or None, k_ptr or None, v_ptr or None, table_ptr or None,
+        seqlens_ptr or None, ctypes.c_float(scale), out_ptr or None, status_ptr or None,
+        stream or None))
 
 
 def decode_raw(desc: PaDesc, q_ptr: int, k_ptr: int, v_ptr: int, table_ptr: int, seqlens_ptr: int,

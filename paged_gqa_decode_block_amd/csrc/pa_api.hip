@@ -4,6 +4,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/paged_attn.h"
 #include "pa_kernels.h"
 
@@ -308,6 +310,7 @@ const char* paged_attn_strerror(int status) {
     case PA_E_SEQLEN: return "a cache length is negative or beyond max_blocks_per_seq * block_size";
     case PA_E_NOMEM: return "not enough free blocks in the block manager";
     case PA_E_SEQ: return "unknown sequence, or a block index or length outside it";
+    case PA_E_SCRATCH: return "the call needs more workspace than the library's static scratch (PA_STATIC_SCRATCH_BYTES) holds; pass a workspace to paged_attn_decode instead";
   }
   return "unknown status";
 }
@@ -417,6 +420,59 @@ int paged_attn_decode(const pa_desc* desc, const void* q, const void* k_cache, c
   rc = run_partition(desc, p, (hipStream_t)stream);
   if (rc != PA_OK) return rc;
   return run_combine(p, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free decode ---------------------------------------------
+// The library's own workspace for paged_attn_decode_static: one static array per
+// device, zero-initialised when the code object is loaded, held until the
+// process ends. Host code never passes the array's name to a kernel (on the host
+// it is a stand-in, not a device address); it uses the address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[PA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Address of the current device's scratch array, or nullptr when the runtime
+// cannot say which device is current or where the array is.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode_static(const pa_desc* desc, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_table,
+                             const int32_t* cache_seqlens, float scale, void* out,
+                             int32_t* status, void* stream) {
+  const int rc = validate(desc);
+  if (rc != PA_OK) return rc;
+  // the merged grid variant keeps arrival counters that would have to be zero
+  if (pick_path(desc) == PA_PATH_MFMA_FUSED) return PA_E_PATH;
+  const size_t need = paged_attn_workspace_size(desc);
+  if (need > PA_STATIC_SCRATCH_BYTES) return PA_E_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && desc->batch > 0) {
+    ws = scratch_for_current_device();
+    if (!ws) return PA_E_LAUNCH;
+  }
+  return paged_attn_decode(desc, q, k_cache, v_cache, block_table, cache_seqlens, scale, out, ws,
+                           need > 0 ? PA_STATIC_SCRATCH_BYTES : 0, status, stream);
 }
 
 int paged_attn_decode_append(const pa_desc* desc, const void* q, const void* k_new,

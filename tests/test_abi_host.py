@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), f"{name} not exported"
-    assert lib.paged_attn_abi_version() == 3
+    assert lib.paged_attn_abi_version() == 4
 
 
 def test_descriptor_layout_matches_c(tmp_path):
@@ -308,3 +308,35 @@ def test_prefill_argument_errors():
     assert pa.prefill_raw(_desc(batch=0), **{**args, "cu_q_ptr": 0}) == 0  # no sequences
     # no workspace is involved, whatever the decode would need
     assert pa.workspace_size(d) > 0
+
+
+def test_decode_static_refuses_before_device_work():
+    """The allocation-free decode checks the descriptor, the path and the
+    workspace it would need against its static scratch before it touches any
+    device: too large a need returns PA_E_SCRATCH, the merged grid variant
+    PA_E_PATH (its arrival counters would have to be zero in the shared
+    array), a bad descriptor its own code; nothing runs, so null pointers are
+    never looked at."""
+    lib = pa.load_library()
+    assert pa.PA_STATIC_SCRATCH_BYTES == 32 << 20
+
+    def call(d):
+        return _lib.decode_static_raw(d, 0, 0, 0, 0, 0, 1.0, 0, 0, 0)
+
+    # the 64-sequence batch on the grid kernel at 512-token partitions: ~130 MiB
+    big = pa.make_desc(batch=64, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
+                       num_blocks=45000, max_blocks_per_seq=2048, kv_dtype="bf16",
+                       k_strides=(8 * 16 * 128, 16 * 128, 128), partition_size=512,
+                       path="mfma_grid")
+    assert pa.workspace_size(big) > pa.PA_STATIC_SCRATCH_BYTES
+    assert call(big) == -16
+    assert lib.paged_attn_strerror(-16).decode().startswith("the call needs more workspace")
+    fused = pa.make_desc(batch=4, num_q_heads=16, num_kv_heads=2, head_dim=128, block_size=16,
+                         num_blocks=100, max_blocks_per_seq=64, kv_dtype="bf16",
+                         k_strides=(2 * 16 * 128, 16 * 128, 128), partition_size=64,
+                         path="mfma_fused")
+    assert call(fused) == -10
+    bad = pa.make_desc(batch=4, num_q_heads=16, num_kv_heads=2, head_dim=96, block_size=16,
+                       num_blocks=100, max_blocks_per_seq=64, kv_dtype="bf16",
+                       k_strides=(2 * 16 * 96, 16 * 96, 96))
+    assert call(bad) == -3
