@@ -65,7 +65,7 @@ class Workload:
     """One generated configuration, copied to the GPU once."""
 
     def __init__(self, k: int, torch, path: str, partition: int | None = None,
-                 layout: str = "HND", case=None):
+                 layout: str = "HND", case=None, seed: int | None = None):
         from paged_gqa_decode_block_amd import workload as W
         import paged_gqa_decode_block_amd as pa
 
@@ -75,6 +75,7 @@ class Workload:
             log(f"[bench] generated config {k} ({case.name}) in {time.time() - t:.1f}s")
         self.case = c = case
         self.k = k
+        self.seed = 1000 + k if seed is None else seed
         self.torch = torch
         self.path = path
 
@@ -134,7 +135,7 @@ class Workload:
             "head_dim": c.D, "block_size": c.bs, "kv_dtype": c.kv_dtype, "layout": self.layout,
             "partition_size": self.part, "path": self.path_name, "kv_shared": self.kv_shared,
             "total_cached_tokens": int(c.seqlens.astype(np.int64).sum()),
-            "num_physical_blocks": c.NB, "seed": 1000 + self.k,
+            "num_physical_blocks": c.NB, "seed": self.seed,
         }
 
 
@@ -231,6 +232,103 @@ def measure(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
         # prefix-shared blocks counted once (equal to kv_gbs when no block is shared)
         "unique_kv_gbs": wl.unique_kv_bytes / t / 1e9,
     }
+
+
+def measure_brief(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
+    """Flushed and warm step times and the partition kernel's average launch
+    duration, for the context legs."""
+    torch = wl.torch
+    for _ in range(warmup):
+        wl.call()
+    cold = float(np.median(time_each(torch, wl.call, steps,
+                                     flush=lambda: flush_caches(flush_buf))))
+    warm = time_steps(torch, wl.call, steps)
+    part = time_steps(torch, lambda: wl.call("partition"), steps)
+    wl.call()
+    torch.cuda.synchronize()
+    return {"step_us": round(cold * 1e3, 2), "warm_step_us": round(warm * 1e3, 2),
+            "partition_kernel_us": round(part * 1e3, 2),
+            "kv_gbs": round(wl.kv_bytes / (cold / 1e3) / 1e9, 1),
+            "partition_kernel_kv_gbs": round(wl.kv_bytes / (part / 1e3) / 1e9, 1),
+            "kv_bytes": wl.kv_bytes, "path": wl.path_name, "partition_size": wl.part}
+
+
+def gqa_sweep(wl: Workload, steps: int, warmup: int, flush_buf) -> dict:
+    """The headline workload's K/V pool and tables with G = H_q / H_kv of 1, 2
+    and 8 (the first 8, 16 and 64 query heads of each sequence): the K/V bytes
+    a call must read do not depend on G (one pass over each KV head's tokens
+    serves all G query heads of its group), so neither should the time."""
+    from paged_gqa_decode_block_amd import workload as W
+
+    c = wl.case
+    out = {}
+    for G in (1, 2, c.G):
+        hq = G * c.Hkv
+        cg = W.Case(**{**c.__dict__, "q": np.ascontiguousarray(c.q[:, :hq]), "Hq": hq,
+                       "name": f"{c.name}_G{G}"})
+        wg = Workload(4, wl.torch, wl.path, None, wl.layout, case=cg)
+        out[f"G{G}"] = {"num_q_heads": hq, **measure_brief(wg, steps, warmup, flush_buf)}
+        log(f"[bench] {c.name} with G = {G}: {out[f'G{G}']['step_us']:.1f} us/step flushed, "
+            f"partition kernel {out[f'G{G}']['partition_kernel_us']:.1f} us")
+        del wg
+        wl.torch.cuda.empty_cache()
+    return out
+
+
+def shard_leg(torch, steps: int, warmup: int, flush_buf, n: int = 8) -> dict:
+    """The 100K-token workload's context split by tokens over n GPUs: what one
+    GPU computes (the partition kernel at one shard's real shape, 12 500
+    tokens for n = 8, plus the merge of its own partitions). The exchange of
+    the shards' partial states and their final merge are not part of it."""
+    from paged_gqa_decode_block_amd import workload as W
+
+    c = W.make_shard(n)
+    r = {"shards": n}
+    # the library's choice (one shard is a small batch), and the streaming
+    # kernel at the whole workload's 512-token partitions
+    for key, path, part in (("auto", "auto", 0), ("stream_512", "mfma_stream", 512)):
+        wl = Workload(3, torch, path, part, case=c, seed=1003 + 100 * n)
+        r[key] = {**wl.describe(), **measure_brief(wl, steps, warmup, flush_buf)}
+        log(f"[bench] {c.name} ({key}): {r[key]['step_us']:.1f} us/step flushed, "
+            f"{r[key]['kv_gbs']:.0f} GB/s")
+        del wl
+    torch.cuda.empty_cache()
+    return r
+
+
+# Throughput table of the paged-attention-runtime design notes (RTX 2070, SM75;
+# Qwen2 shapes, head size 64, 14 query heads): concurrent sequences -> tokens/s.
+RUNTIME_NOTES_RTX2070 = {1: 542981, 2: 844423, 4: 1239648, 8: 2890839}
+
+
+def batch_sweep(torch, steps: int, warmup: int, flush_buf) -> dict:
+    """Qwen2-shaped decode (H_q 14, H_kv 2, d 64, fp16 K/V, 512 cached tokens per
+    sequence) for 1, 2, 4 and 8 sequences, and the speedup over one sequence,
+    next to the design notes' RTX 2070 table for context (other hardware). The
+    notes do not define their tokens/s; both readings are given: decode tokens
+    (one query token per sequence per call) and cached tokens attended, each
+    per second of call time."""
+    from paged_gqa_decode_block_amd import workload as W
+
+    out = {"context": {"source": "paged-attention-runtime design notes, throughput table",
+                       "hardware": "RTX 2070 (SM75)", "tokens_per_s": RUNTIME_NOTES_RTX2070,
+                       "speedup_8_over_1": round(RUNTIME_NOTES_RTX2070[8] / RUNTIME_NOTES_RTX2070[1], 2)}}
+    base = None
+    for B in (1, 2, 4, 8):
+        c = W.make_qwen2_batch(B)
+        wl = Workload(2, torch, "auto", None, case=c, seed=4000 + B)
+        r = measure_brief(wl, steps, warmup, flush_buf)
+        tps = B / (r["step_us"] / 1e6)
+        tps_warm = B / (r["warm_step_us"] / 1e6)
+        ctx_warm = int(c.seqlens.sum()) / (r["warm_step_us"] / 1e6)
+        base = base or tps_warm
+        out[f"B{B}"] = {**r, "tokens_per_s": round(tps, 1), "warm_tokens_per_s": round(tps_warm, 1),
+                        "warm_cached_tokens_per_s": round(ctx_warm, 1),
+                        "warm_speedup": round(tps_warm / base, 2)}
+        log(f"[bench] {c.name}: {r['warm_step_us']:.1f} us/step warm, {tps_warm:.0f} tokens/s")
+        del wl
+    torch.cuda.empty_cache()
+    return out
 
 
 def measure_append_graph(wl: Workload, steps: int) -> dict:
@@ -525,6 +623,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the plain read-rate probes")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context legs (G sweep, one-shard shape, Qwen2 batch sweep)")
+    ap.add_argument("--num-q-heads", type=int, default=None,
+                    help="with --profile: keep the first N query heads of each sequence "
+                         "(G = N / H_kv) of the workload")
     ap.add_argument("--profile", choices=["partition", "both", "copy", "prefill"], default=None)
     ap.add_argument("--prefill", type=str, default="1,2",
                     help="comma-separated prefill workloads to time ('' for none)")
@@ -556,7 +659,17 @@ def main():
             measure_prefill(k, torch, a.steps, a.warmup)
         return
 
-    wl = Workload(a.config, torch, a.path, a.partition, a.layout)
+    case = None
+    if a.num_q_heads is not None:
+        from paged_gqa_decode_block_amd import workload as W
+
+        case = W.make_config(a.config)
+        hq = a.num_q_heads
+        if hq % case.Hkv or hq > case.Hq:
+            sys.exit(f"--num-q-heads must be a multiple of {case.Hkv} up to {case.Hq}")
+        case = W.Case(**{**case.__dict__, "q": np.ascontiguousarray(case.q[:, :hq]), "Hq": hq,
+                         "name": f"{case.name}_G{hq // case.Hkv}"})
+    wl = Workload(a.config, torch, a.path, a.partition, a.layout, case=case)
     if a.profile is not None:
         for _ in range(a.warmup):
             wl.call()
@@ -576,6 +689,9 @@ def main():
     log(f"[bench] {wl.case.name}: {r['ms_per_step'] * 1e3:.1f} us/step flushed "
         f"({r['warm_ms_per_step'] * 1e3:.1f} warm), {r['kv_gbs']:.0f} GB/s")
     rl = roofline(wl, r)
+    context = {}
+    if not a.no_context:
+        context["gqa_bytes_vs_G"] = gqa_sweep(wl, max(10, a.steps // 2), a.warmup, flush_buf)
     also = {}
     for k in [int(x) for x in a.also.split(",") if x.strip()]:
         if k == a.config:
@@ -594,6 +710,9 @@ def main():
                 f"{also[w2.case.name]['parity']['max_abs_err']:.2e}")
         del w2
         torch.cuda.empty_cache()
+    if not a.no_context:
+        context["one_shard_of_8"] = shard_leg(torch, a.steps, a.warmup, flush_buf)
+        context["qwen2_batch_sweep"] = batch_sweep(torch, a.steps, a.warmup, flush_buf)
     prefill = {}
     for k in [int(x) for x in a.prefill.split(",") if x.strip()]:
         r3 = measure_prefill(k, torch, max(5, a.steps // 5), 3)
@@ -639,6 +758,7 @@ def main():
         "parity": parity,
         "read_probe": probe,
         "also": also,
+        "context": context,
         "prefill": prefill,
     }
     print(json.dumps(line), flush=True)

@@ -220,35 +220,45 @@ int validate(const pa_desc* d) {
 // Workspace regions of a valid descriptor, as byte offsets (each 256-byte
 // aligned; off[kWsParts] is the total): for the merged grid variant first an
 // arrival word per (sequence, KV head) (at offset 0 for every descriptor; zero
-// before the first call and left zero by every call), then partition states
-// m, l, acc for every (sequence, query head, partition), then for the
-// streaming kernel the partition links and one continuation state per wave
-// (per pair of waves at head_dim 256).
-// Kernels other than the streaming one need nothing when one partition always
-// suffices.
-enum { kWsCnt, kWsM, kWsL, kWsAcc, kWsLink, kWsCm, kWsCl, kWsCacc, kWsCmore, kWsParts };
+// before the first call and left zero by every call); for the grid and VALU
+// kernels the partition states m, l, acc of every (sequence, query head,
+// partition), nothing when one partition always suffices; for the streaming
+// kernel a record per (sequence, KV head) stream and two state slots (m, l and
+// acc of the G heads) per wave of its grid (per pair of waves at head_dim 256).
+enum { kWsCnt, kWsM, kWsL, kWsAcc, kWsLink, kWsCm, kWsCl, kWsCacc, kWsParts };
 void workspace_layout(const pa_desc* d, size_t* off) {
   const int part = pick_partition(d);
   const int64_t pmax = (max_tokens(d) + part - 1) / part;
   const bool stream = pick_path(d) == PA_PATH_MFMA_STREAM;
   size_t sz[kWsParts] = {0};
-  if (stream || pmax > 1) {
+  if (stream) {
+    const int G = d->num_q_heads / d->num_kv_heads;
+    const size_t slots = 2 * (size_t)stream_waves(d);
+    sz[kWsLink] = (size_t)d->batch * d->num_kv_heads * 2 * sizeof(int32_t);
+    sz[kWsCm] = sz[kWsCl] = slots * G * sizeof(float);
+    sz[kWsCacc] = slots * G * d->head_dim * sizeof(float);
+  } else if (pmax > 1) {
     const size_t rows = (size_t)d->batch * d->num_q_heads * (size_t)pmax;
     sz[kWsM] = sz[kWsL] = rows * sizeof(float);
     sz[kWsAcc] = rows * d->head_dim * sizeof(float);
-  }
-  if (stream) {
-    const int G = d->num_q_heads / d->num_kv_heads;
-    const size_t waves = (size_t)stream_waves(d);
-    sz[kWsLink] = (size_t)d->batch * d->num_kv_heads * (size_t)pmax * sizeof(int32_t);
-    sz[kWsCm] = sz[kWsCl] = waves * G * sizeof(float);
-    sz[kWsCacc] = waves * G * d->head_dim * sizeof(float);
-    sz[kWsCmore] = waves * sizeof(int32_t);
   }
   if (pick_path(d) == PA_PATH_MFMA_FUSED && pmax > 1)
     sz[kWsCnt] = (size_t)d->batch * d->num_kv_heads * sizeof(int32_t);
   off[0] = 0;
   for (int i = 0; i < kWsParts; ++i) off[i + 1] = off[i] + align256(sz[i]);
+}
+
+// Stripe-count hint for the combine after the streaming kernel: about how many
+// waves' states a stream has when every sequence is as long as the table
+// allows (longest stream over the average share), doubled with room for
+// shorter shares. It only sizes the combine's workgroups; any count is merged.
+int stream_states_hint(const pa_desc* d, int waves) {
+  const int64_t per_stream = (max_tokens(d) + 15) / 16;
+  const int64_t total = (int64_t)d->batch * d->num_kv_heads * per_stream;
+  const int64_t share = total / (waves > 0 ? waves : 1);
+  const int64_t n = per_stream / (share > 0 ? share : 1) + 1;
+  const int64_t hint = 2 * n + 2;
+  return (int)(hint < waves ? hint : waves);
 }
 
 }  // namespace
@@ -368,16 +378,17 @@ int prepare(const pa_desc* desc, const void* q, const void* k_cache, const void*
     size_t off[kWsParts + 1];
     workspace_layout(desc, off);
     char* ws = (char*)workspace;
-    p.ws_m = (float*)(ws + off[kWsM]);
-    p.ws_l = (float*)(ws + off[kWsL]);
-    p.ws_acc = (float*)(ws + off[kWsAcc]);
     if (pick_path(desc) == PA_PATH_MFMA_STREAM) {
       p.ws_link = (int32_t*)(ws + off[kWsLink]);
       p.ws_cm = (float*)(ws + off[kWsCm]);
       p.ws_cl = (float*)(ws + off[kWsCl]);
       p.ws_cacc = (float*)(ws + off[kWsCacc]);
-      p.ws_cmore = (int32_t*)(ws + off[kWsCmore]);
       p.nwaves = stream_waves(desc);
+      p.pmax = stream_states_hint(desc, p.nwaves);
+    } else {
+      p.ws_m = (float*)(ws + off[kWsM]);
+      p.ws_l = (float*)(ws + off[kWsL]);
+      p.ws_acc = (float*)(ws + off[kWsAcc]);
     }
     if (pick_path(desc) == PA_PATH_MFMA_FUSED && p.pmax > 1) p.ws_cnt = (int32_t*)(ws + off[kWsCnt]);
   }

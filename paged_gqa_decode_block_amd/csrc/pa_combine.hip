@@ -10,22 +10,23 @@
 // partitions at once; only p < n is read. Sequences with one partition were
 // already written by the partition kernel and are skipped here.
 //
-// After the streaming kernel a partition may have been split between waves:
-// its slot then holds the first piece and its link names the wave holding the
-// next piece (a continuation slot, which says whether a further wave holds
-// more). The pieces are folded into the partition's state with the same op
-// before it joins the merge. With that kernel a sequence's single partition is
-// read here too unless its link says it was written out, and an empty sequence
-// gets zeros.
+// After the streaming kernel the states to merge are not partitions but the
+// waves' states of each (sequence, KV head) stream: the stream's record names
+// the slot of its first wave's state and the number n of consecutive waves
+// whose states make up the stream (0 when its output was written directly);
+// wave w_a + i, i >= 1, left its state in its slot 0. A record is trusted only
+// for a non-empty sequence (every non-empty stream's record is rewritten by
+// each call); an empty sequence gets zeros.
 //
 // Grid (D / 64, H_q, B), 16 x S threads: thread (stripe s, quad u) owns dims
-// 4u .. 4u+3 of a 64-dim slice (float4 loads) and partitions p = s, s + S, ....
-// Each thread folds its partitions with the same max-rescaling op, a batch of
-// partitions' loads in flight per round, so no pass over all maxima has to
-// finish first; the S stripes' states then meet, four per wave by cross-lane
-// exchanges and the waves' through LDS. S is 4 or 8 when there
-// are at most that many partitions, 16 up to 64, and 64 (32 beyond 256) above,
-// so one round usually covers them all.
+// 4u .. 4u+3 of a 64-dim slice (float4 loads) and states i = s, s + S, ....
+// Each thread folds its states with the same max-rescaling op, a batch of
+// states' loads in flight per round, so no pass over all maxima has to finish
+// first; the S stripes' states then meet, four per wave by cross-lane
+// exchanges and the waves' through LDS. S is 4 or 8 when there are at most
+// that many states per (sequence, head), 16 up to 64, and 64 (32 beyond 256)
+// above (the host's bound or estimate of that count), so one round usually
+// covers them all.
 #include "pa_kernels.h"
 
 namespace pa {
@@ -40,17 +41,30 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
   const int tid = threadIdx.x;
   const int u = tid & 15, s = tid >> 4;
   const int d = blockIdx.x * 64 + 4 * u;
-  const int L = clamped_len(p, b, false);
-  const int n = (L + p.part - 1) / p.part;
-  const bool chained = p.ws_link != nullptr;
+  const bool waves = p.ws_link != nullptr;  // states of the streaming kernel's waves
   const int hk = h / p.G, g = h - hk * p.G;
-  const int32_t* link = chained ? p.ws_link + ((int64_t)b * p.Hkv + hk) * p.pmax : nullptr;
-  if (chained ? (n == 1 && link[0] == -2) : n <= 1) return;
+  // both loads issued before either is used
+  const int2 rec = waves ? *(const int2*)(p.ws_link + 2 * ((int64_t)b * p.Hkv + hk)) : make_int2(0, 0);
+  const int L = clamped_len(p, b, false);
+  int n;
+  if (waves) {
+    if (L > 0 && rec.y == 0) return;  // written out by the partition kernel
+    n = L > 0 ? rec.y : 0;
+    // a record is always in range when this call's partition kernel wrote it;
+    // anything else reads nothing (zeros) rather than outside the slots
+    if (rec.x < 0 || rec.x >= 2 * p.nwaves || n < 0 || (rec.x >> 1) + n > p.nwaves) n = 0;
+  } else {
+    n = (L + p.part - 1) / p.part;
+    if (n <= 1) return;
+  }
 
+  // state i of the (sequence, head): its max, sum and unnormalised output
   const int64_t row = ((int64_t)b * p.Hq + h) * p.pmax;
-  const float* mrow = p.ws_m + row;
-  const float* lrow = p.ws_l + row;
-  const float* arow = p.ws_acc + row * p.D + d;
+  auto state_row = [&](int i) -> int64_t {
+    if (!waves) return -1;
+    const int slot = i == 0 ? rec.x : 2 * ((rec.x >> 1) + i);
+    return (int64_t)slot * p.G + g;
+  };
 
   // (m, l, a) <- (m, l, a) merged with (cm, cl, ca)
   auto merge = [](float& m, float& l, float4& a, float cm, float cl, float4 ca) {
@@ -64,67 +78,27 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
     a.w = w0 * a.w + w1 * ca.w;
     m = M;
   };
-  // continuation piece of link lk (a wave index + 1); returns the next link
-  auto piece = [&](int lk, float& cm, float& cl, float4& ca) {
-    const int64_t c = (int64_t)(lk - 1) * p.G + g;
-    cm = p.ws_cm[c];
-    cl = p.ws_cl[c];
-    ca = *(const float4*)(p.ws_cacc + c * p.D + d);
-    return p.ws_cmore[lk - 1] ? lk + 1 : 0;
-  };
-
   float Ms = -INFINITY, Ls = 0.f;
   float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int i0 = s; i0 < n; i0 += kStripes * kBatch) {
     float mv[kBatch], lv[kBatch];
     float4 av[kBatch];
-    int lkv[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int i = i0 + k * kStripes;
       mv[k] = -INFINITY;
       lv[k] = 0.f;
       av[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      lkv[k] = -1;
       if (i < n) {
-        mv[k] = mrow[i];
-        lv[k] = lrow[i];
-        av[k] = *(const float4*)(arow + (int64_t)i * p.D);
-        if (chained) lkv[k] = link[i];
-      }
-    }
-    if (chained) {
-      // The first two pieces of every chain in the batch are loaded together
-      // (the second speculatively: continuation slots of consecutive waves are
-      // adjacent); longer chains are walked after.
-      float cm[kBatch], cl[kBatch], cm2[kBatch], cl2[kBatch];
-      float4 ca[kBatch], ca2[kBatch];
-      int nx[kBatch], nx2[kBatch];
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        cm[k] = cm2[k] = -INFINITY;
-        cl[k] = cl2[k] = 0.f;
-        ca[k] = ca2[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-        nx[k] = nx2[k] = 0;
-        const int lk = lkv[k];
-        if (lk > 0 && lk <= p.nwaves) {
-          nx[k] = piece(lk, cm[k], cl[k], ca[k]);
-          if (lk + 1 <= p.nwaves) nx2[k] = piece(lk + 1, cm2[k], cl2[k], ca2[k]);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        merge(mv[k], lv[k], av[k], cm[k], cl[k], ca[k]);
-        if (nx[k] > 0) {  // the second piece belongs to this partition
-          merge(mv[k], lv[k], av[k], cm2[k], cl2[k], ca2[k]);
-          nx[k] = nx2[k];
-        }
-        for (int lk = nx[k]; lk > 0 && lk <= p.nwaves;) {
-          float m1, l1;
-          float4 a1;
-          const int nl = piece(lk, m1, l1, a1);
-          merge(mv[k], lv[k], av[k], m1, l1, a1);
-          lk = nl;
+        if (waves) {
+          const int64_t sr = state_row(i);
+          mv[k] = p.ws_cm[sr];
+          lv[k] = p.ws_cl[sr];
+          av[k] = *(const float4*)(p.ws_cacc + sr * p.D + d);
+        } else {
+          mv[k] = p.ws_m[row + i];
+          lv[k] = p.ws_l[row + i];
+          av[k] = *(const float4*)(p.ws_acc + (row + i) * p.D + d);
         }
       }
     }

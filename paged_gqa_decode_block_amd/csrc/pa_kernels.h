@@ -18,16 +18,16 @@ struct Params {
   const int32_t* table;     // [B, MBS]
   const int32_t* seqlens;   // [B]
   void* out;                // [B, Hq, D] fp32, or bf16 when qo_bf16
+  // grid and VALU kernels: partition states (NULL on the streaming path)
   float* ws_m;              // [B, Hq, pmax]  running max, base-2 units
   float* ws_l;              // [B, Hq, pmax]  sum of 2^(s - m)
   float* ws_acc;            // [B, Hq, pmax, D] unnormalised output
-  // streaming kernel only (NULL otherwise): partition links and the waves'
-  // continuation states (a piece of a partition that starts inside it)
-  int32_t* ws_link;         // [B, Hkv, pmax] -2 written out, -1 complete, else continuing wave + 1
-  float* ws_cm;             // [waves, G]
-  float* ws_cl;             // [waves, G]
-  float* ws_cacc;           // [waves, G, D]
-  int32_t* ws_cmore;        // [waves] 1 when the partition goes on into the next wave
+  // streaming kernel only (NULL otherwise): a record per stream and two state
+  // slots per wave (the partly covered streams at the ends of its share)
+  int32_t* ws_link;         // [B, Hkv, 2] first state's slot, number of waves (0: written out)
+  float* ws_cm;             // [waves, 2, G] running max, base-2 units
+  float* ws_cl;             // [waves, 2, G] sum of 2^(s - m)
+  float* ws_cacc;           // [waves, 2, G, D] unnormalised output
   // grid kernel with the merge in its last block (NULL otherwise): arrivals per
   // (sequence, KV head), zero between calls
   int32_t* ws_cnt;          // [B, Hkv]
@@ -37,12 +37,13 @@ struct Params {
   int B, Hq, Hkv, G, D;
   int bs_log2, NB, MBS;
   int part;                 // partition size in tokens
-  int pmax;                 // ceil(MBS * bs / part)
+  int pmax;                 // ceil(MBS * bs / part); streaming path: a bound on a
+                            // stream's states, used to size the combine's workgroups
   float qscale;             // scale * log2(e): scores are kept in base-2 units
   int cus;                  // compute units of the device (streaming kernel)
   int len_add;              // tokens attended = cache_seqlens[b] + len_add (1 after an append)
   int qo_bf16;              // q and out are bf16 (else fp32)
-  int nwaves;               // continuation slots in the workspace (streaming kernel)
+  int nwaves;               // the streaming kernel's grid (two state slots per wave)
   int xpacked;              // K [NB, Hkv, D/8, bs, 8] and V [NB, Hkv, D, bs] (16-bit):
                             // element (blk, h, t, i) of K at blk*ksb + h*ksh + (i/8)*8*bs
                             // + 8*t + i%8, of V at blk*vsb + h*vsh + i*bs + t

@@ -89,8 +89,12 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 
-// Cache-policy bit of the merged variant's workspace traffic: stores write
-// through to memory and loads see what other L2s wrote (device scope).
+// Cache-coherence bits of the merged variant's workspace traffic: SC1 set,
+// SC0 clear is device scope on gfx950 (the ISA's SC1:SC0 scope field: wave,
+// group, device, system). A device-scope store is written through the XCD's
+// L2 to the device-coherent level, and the wave's vector-memory counter drops
+// for it only once it is complete there; a device-scope load is served from
+// that level, not from a line another XCD's write left stale in this XCD's L2.
 constexpr int kSc1 = 16;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -134,8 +138,26 @@ __device__ __forceinline__ void publish_and_merge(const Params& p, int b, int hk
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l), rl, (r * pm + part) * 4, 0, kSc1);
     }
   }
-  // All of this wave's stores have completed (and, written through, are visible
-  // device-wide) before it counts in.
+  // Ordering of the states against the arrival counter, by the device-scope
+  // cache bits above rather than by C++ release / acquire fences (which
+  // compile to a write-back and an invalidate of the whole L2 of the XCD, and
+  // made this variant 33-51 % slower on the 64-sequence and prefix-shared
+  // batches):
+  //  1. every state store above is device scope, so it completes only at the
+  //     device-coherent level;
+  //  2. s_waitcnt(0) waits until all of this wave's stores are complete before
+  //     the increment is issued (the signal fences keep the compiler from
+  //     moving memory operations across the wait);
+  //  3. the increment is an agent-scope atomic read-modify-write, so the
+  //     n_part increments of the counter happen one after another in a single
+  //     order at the device's point of coherence for it; the block that reads
+  //     n_part - 1 executes its increment after every other block's, and each
+  //     of those was issued only after that block's stores were complete;
+  //  4. that block's loads below are issued after its increment returned (they
+  //     depend on its value through the branch) and are device scope too, so
+  //     they read the completed states and no stale L2 line.
+  // The same device-scope bits are how agent-scope atomic loads and stores
+  // are made coherent on this target family.
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -144,7 +166,8 @@ __device__ __forceinline__ void publish_and_merge(const Params& p, int b, int hk
   if (lane == 0) prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   prev = __builtin_amdgcn_readfirstlane(prev);
   if (prev != npart - 1) return;
-  // last to arrive: every other block's states were complete before it counted in
+  // last to arrive: reset the counter for the next call (the kernel boundary
+  // orders this store before any later launch)
   if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 

@@ -18,11 +18,18 @@
 // d = 128's registers and two waves per SIMD, so one wave's folding overlaps
 // the other's loads.
 //
-// Partial states stay per partition (PART tokens of a stream): a piece of a
-// partition that starts at the partition's first chunk goes to the partition's
-// slot together with a link; a share that begins inside a partition leaves that
-// first piece in the wave's continuation slot, and the link of the partition
-// names the wave. The combine kernel follows the links.
+// The split of the KV sequence is the waves' shares themselves (the partition
+// size is not used): a stream that lies inside one share is folded whole and
+// its normalised output written directly; a stream that several consecutive
+// waves share leaves one partial state (max, sum, unnormalised output) per
+// wave, written once when the wave's segment of it ends, and the combine
+// kernel merges those states. A share partly covers at most two streams (its
+// first and its last), so each wave has two state slots; the wave holding a
+// stream's first chunk records which slot starts the stream's run of states
+// and how many waves the run spans. Writing one state per wave, not one per
+// fixed-size partition, keeps the bytes written small: on the 64-sequence
+// batch about half of what 4096-token partitions plus continuation pieces
+// wrote, and those writes cost far more time than their share of the traffic.
 //
 // Loads are raw buffer loads of full token rows (each 16-byte lane load is part
 // of a contiguous row segment of 128-512 bytes) with the non-temporal hint. The
@@ -43,11 +50,11 @@
 // Q' and P are split into hi + lo 16-bit parts (two MFMAs each) so products keep
 // ~16 mantissa bits. The running output is rescaled lazily: p = 2^(s - m) uses a
 // reference max m that is only raised (and acc, l rescaled) when a score exceeds
-// it by more than 8, so p <= 256 and most chunks skip the rescale. At every
-// partition boundary and at the end of a share the piece's state is written
-// (partition slot or continuation slot, or the normalised output when the piece
-// is a whole single-partition sequence) and reset. Tokens at or past L_b and
-// chunks behind an invalid table entry are never loaded; their scores are -inf.
+// it by more than 8, so p <= 256 and most chunks skip the rescale. At the end
+// of each of the share's segments the state is written (a state slot, or the
+// normalised output when the segment is a whole stream). Tokens at or past L_b
+// and chunks behind an invalid table entry are never loaded; their scores are
+// -inf.
 //
 // Requires block_size >= 16 (a 16-token chunk lies in one block), at most 1024
 // sequences (the chunk prefix is formed in registers) and fewer than 2^31
@@ -100,8 +107,7 @@ partition_stream_kernel(Params p) {
   const int half = DS == 2 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
   int par = 0;  // chunk parity of the score exchange
   const int r = lane & 15, q = lane >> 4;
-  const int G = p.G, Hkv = p.Hkv, PART = p.part;
-  const int CPP = PART >> 4;  // chunks per partition
+  const int G = p.G, Hkv = p.Hkv;
 
   // ---- 1. chunk counts and this wave's share ---------------------------------
   // Work is counted in 16-token chunks: sequence b has nc(b) = ceil(L_b / 16)
@@ -207,9 +213,11 @@ partition_stream_kernel(Params p) {
 
   // ---- 2. segments: the share's runs of chunks within one (b, KV head) -------
   int bad_block = 0;
+  bool first_seg = true;
   while (g < g_end) {
     const int jA = j;
     const int nch = min(ncb - j, g_end - g);
+    const int cs = Pb * Hkv + hk * ncb;  // the stream's first chunk in the batch
     {
       const int T0 = 16 * jA;
       const int T1 = min(L, 16 * (jA + nch));
@@ -315,61 +323,48 @@ partition_stream_kernel(Params p) {
       for (int k = 0; k < MB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
       float m = -INFINITY, l = 0.f;
 
-      // Write the state of the piece of partition pp = jc / CPP that ends at
-      // chunk jc, and reset. A piece that starts at its partition's first
-      // chunk goes to the partition's slot, with the partition's link: -2 when
-      // it is the sequence's only partition and complete (the output is then
-      // written here, normalised), -1 when complete, else the next wave, whose
-      // share continues it. Only a share's first piece can start inside a
-      // partition; it goes to this wave's continuation slot, flagged when the
-      // partition goes on into the next wave too.
-      auto flush = [&](int jc) {
-        const int pp = jc / CPP;
-        const bool is_main = pp * CPP >= jA;
-        const bool covers_end = jc + 1 == min(ncb, (pp + 1) * CPP);
-        const bool direct = is_main && covers_end && ncb <= CPP;
+      // Write the segment's result once, when its last chunk is folded. A
+      // segment that is the whole stream writes the normalised output. Any
+      // other segment is part of a stream several consecutive waves share: it
+      // leaves its state (max, sum, unnormalised output of the G heads) in
+      // this wave's slot 0 when it is the share's first segment, else slot 1
+      // (a share has at most one partly covered stream at each end). The wave
+      // holding the stream's first chunk also names the stream's states: the
+      // slot of its own state and the number of waves whose states make up
+      // the stream (0 when the output was written here).
+      auto flush = [&]() {
+        const bool whole = jA == 0 && nch == ncb;
+        const int slot = 2 * wx + (first_seg ? 0 : 1);
         const float lt = quad_sum(l);
-        // one store sequence per destination: a select between two argument
-        // pointers would be compiled into a vector load of the selected
-        // argument, which waits for every K/V load in flight
-        auto store = [&](float* ap, float* mp, float* lp) {
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            *(float4*)(ap + 16 * mb) = make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
-          if (q == 0 && half == 0) {
-            *mp = m;
-            *lp = lt;
-          }
-        };
         if (r < G) {
-          const int h = hk * G + r;
-          if (direct) {
+          if (whole) {
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
-            const int64_t orow = ((int64_t)b * p.Hq + h) * D + half * DW + 4 * q;
+            const int64_t orow = ((int64_t)b * p.Hq + hk * G + r) * D + half * DW + 4 * q;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
               const f32x4 o = acc[mb] * inv;
               store_out4<QO>(p, orow + 16 * mb, o[0], o[1], o[2], o[3]);
             }
-          } else if (is_main) {
-            const int64_t row = ((int64_t)b * p.Hq + h) * p.pmax + pp;
-            store(p.ws_acc + row * D + half * DW + 4 * q, p.ws_m + row, p.ws_l + row);
           } else {
-            const int64_t row = (int64_t)blockIdx.x * G + r;
-            store(p.ws_cacc + row * D + half * DW + 4 * q, p.ws_cm + row, p.ws_cl + row);
+            const int64_t row = (int64_t)slot * G + r;
+            float* ap = p.ws_cacc + row * D + half * DW + 4 * q;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              *(float4*)(ap + 16 * mb) = make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
+            if (q == 0 && half == 0) {
+              p.ws_cm[row] = m;
+              p.ws_cl[row] = lt;
+            }
           }
         }
-        if (lane == 0 && half == 0) {
-          if (is_main)
-            p.ws_link[((int64_t)b * Hkv + hk) * p.pmax + pp] =
-                direct ? -2 : covers_end ? -1 : (int)blockIdx.x + 2;  // wave x + 1, plus one
-          else
-            p.ws_cmore[blockIdx.x] = covers_end ? 0 : 1;
+        if (jA == 0 && lane == 0 && half == 0) {
+          // chunks [cs, cs + ncb) of the batch are this stream; the last one
+          // lies in the share of wave wave_of(cs + ncb - 1)
+          const int last = cs + ncb - 1;
+          const int cut = sh_extra * (sh_base + 1);
+          const int wl = last < cut ? last / (sh_base + 1) : sh_extra + (last - cut) / sh_base;
+          *(int2*)(p.ws_link + 2 * ((int64_t)b * Hkv + hk)) = make_int2(slot, whole ? 0 : wl - wx + 1);
         }
-#pragma unroll
-        for (int k = 0; k < MB; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m = -INFINITY;
-        l = 0.f;
       };
 
       // fold one chunk (its rows in a ring slot, `rows` of them attended)
@@ -458,7 +453,6 @@ partition_stream_kernel(Params p) {
         rows[s] = issue(s, rk[s], rv[s], idr[s]);
       });
       make_q();
-      int to_bound = CPP - jA % CPP;  // chunks until the next partition boundary
       for (int cb = 0; cb < nch; cb += NBUF) {
         static_for<0, NBUF>([&](auto S) {
           constexpr int s = decltype(S)::value;
@@ -469,10 +463,7 @@ partition_stream_kernel(Params p) {
           __builtin_amdgcn_sched_barrier(0);
           if (c < nch) {
             consume(rows[s], rk[s], rv[s]);
-            if (--to_bound == 0 || c + 1 == nch) {
-              flush(jA + c);
-              to_bound = CPP;
-            }
+            if (c + 1 == nch) flush();
           }
         });
       }
@@ -481,10 +472,12 @@ partition_stream_kernel(Params p) {
     // advance to the next (b, KV head) with chunks
     g += nch;
     j = jA + nch;
+    first_seg = false;
     if (j == ncb && g < g_end) {
       j = 0;
       if (++hk == Hkv) {
         hk = 0;
+        Pb += ncb;
         do {  // ends: chunks remain, so a non-empty sequence follows
           ++b;
           L = clamped_len(p, b, false);

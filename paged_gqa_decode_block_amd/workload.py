@@ -388,6 +388,29 @@ def make_config(k: int, seed: int | None = None, layout: str = "HND",
     raise ValueError(f"configs are numbered 1..5, got {k}")
 
 
+def make_shard(n: int, seed: int | None = None, layout: str = "HND") -> Case:
+    """One GPU's share when the 100K-token context of decode workload 3 is split
+    by tokens over n GPUs: the same heads and pool layout (H_q 24, H_kv 4,
+    d 256, bf16, blocks of 16, partitions of 512), one sequence of
+    ceil(100000 / n) tokens, seeded with 1003 + 100 n."""
+    if seed is None:
+        seed = 1003 + 100 * n
+    L = -(-100000 // n)
+    return build_case(f"c3_qwen36_100k_bf16_shard_1of{n}", B=1, Hq=24, Hkv=4, D=256, bs=16,
+                      kv_dtype="bf16", MBS=-(-L // 16), seqlens=[L], partition_size=512,
+                      layout=layout, seed=seed)
+
+
+def make_qwen2_batch(B: int, ctx: int = 512, seed: int | None = None) -> Case:
+    """B Qwen2-shaped sequences (H_q 14, H_kv 2, d 64, fp16 K/V, blocks of 16)
+    of ctx cached tokens each, seeded with 4000 + B: the shape of the
+    batch-scaling measurements of the paged-attention-runtime design notes."""
+    if seed is None:
+        seed = 4000 + B
+    return build_case(f"qwen2_fp16_ctx{ctx}_batch{B}", B=B, Hq=14, Hkv=2, D=64, bs=16,
+                      kv_dtype="f16", MBS=-(-ctx // 16), seqlens=[ctx] * B, seed=seed)
+
+
 # Chunked-prefill workloads over the same kind of paged pool: each sequence's
 # cache already holds the new chunk (its last q_len tokens), and the chunk's
 # queries are packed in rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (the varlen

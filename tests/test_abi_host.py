@@ -171,15 +171,14 @@ def test_partition_size_choice_and_workspace():
     assert pa.partition_size(_desc(batch=1, num_q_heads=32, num_kv_heads=2, head_dim=64,
                                    k_strides=(2048, 1024, 64), max_blocks_per_seq=6250,
                                    **fz)) == 4096
-    # the streaming kernel: partition states, links, one continuation state per wave
+    # the streaming kernel: a record (two int32) per (sequence, KV head) stream
+    # and two state slots (max, sum, output of the G = 4 heads) per wave; the
+    # partition size does not change it
     for part, mbs, batch in ((512, 16, 2), (64, 16, 2), (512, 2048, 64)):
         d = _desc(partition_size=part, max_blocks_per_seq=mbs, batch=batch, path="mfma_stream")
         assert pa.PATH_NAME[pa.resolved_path(d)] == "mfma_stream"
-        pmax = -(-mbs * 16 // part)
-        rows = batch * 8 * pmax
         W = _stream_waves(d)
-        want = (2 * _al(rows * 4) + _al(rows * 128 * 4) + _al(batch * 2 * pmax * 4)
-                + 2 * _al(W * 4 * 4) + _al(W * 4 * 128 * 4) + _al(W * 4))
+        want = _al(batch * 2 * 2 * 4) + 2 * _al(2 * W * 4 * 4) + _al(2 * W * 4 * 128 * 4)
         assert pa.workspace_size(d) == want, (part, mbs, batch)
     # automatic choice: 4096 for the streaming kernel; for the others 512,
     # halved while the grid would be small
