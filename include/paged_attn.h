@@ -259,9 +259,11 @@ int paged_attn_decode_append(const pa_desc* desc, const void* q, const void* k_n
  * The two phases of paged_attn_decode, callable separately (same arguments and
  * rules). paged_attn_partition_phase runs the partition kernel: every
  * (sequence, KV head, partition) folds its tokens into a running softmax state
- * (on the streaming path a partition may be folded in pieces by several waves);
- * a sequence whose single partition was folded whole gets its normalised output
- * written to out, the others leave their states in the workspace.
+ * (on the streaming path the split is the waves' equal shares of the batch's
+ * 16-token chunks instead: each wave leaves one state per stream it covers
+ * only in part); a sequence folded whole by one workgroup or wave gets its
+ * normalised output written to out, the others leave their states in the
+ * workspace.
  * paged_attn_combine_phase merges those states into out with the max-rescaling
  * combine (page "Paged Attention Kernel Architecture for BI-V100", section 2
  * level 3 and section 6 phase 2) and reads only cache_seqlens and the
@@ -312,19 +314,22 @@ int paged_attn_prefill(const pa_desc* desc, const void* q, const void* k_cache,
                        int32_t* status, void* stream);
 
 /* Bytes of workspace paged_attn_decode needs for this descriptor on the
- * current device: the partial (max, sum, output) of every possible partition,
- * sized from max_blocks_per_seq * block_size, and on the streaming path
- * (PA_PATH_MFMA_STREAM) also a link per partition and one continuation state per
- * wave of the kernel's grid, which depends on the device's compute-unit count.
- * 0 when one partition always suffices and the path is not the streaming one.
- * The contents need no initialisation and carry nothing between calls.
- * Returns 0 for an invalid descriptor too; call paged_attn_validate first. */
+ * current device. Grid and VALU kernels: the partial (max, sum, output) of
+ * every possible partition, sized from max_blocks_per_seq * block_size; 0 when
+ * one partition always suffices. Streaming path (PA_PATH_MFMA_STREAM): two
+ * state slots per wave of the kernel's grid, which depends on the device's
+ * compute-unit count, and a two-int record per (sequence, KV head); the
+ * partition size does not enter. MFMA_FUSED: its arrival counters first (see
+ * pa_path). Otherwise the contents need no initialisation and carry nothing
+ * between calls. Returns 0 for an invalid descriptor too; call
+ * paged_attn_validate first. */
 size_t paged_attn_workspace_size(const pa_desc* desc);
 
 /* Checks the descriptor alone (host only, no device access). PA_OK or PA_E_*. */
 int paged_attn_validate(const pa_desc* desc);
 
-/* The partition size paged_attn_decode will use (tokens), or a negative PA_E_*. */
+/* The partition size paged_attn_decode will use (tokens), or a negative PA_E_*.
+ * The streaming path splits by the waves' shares and does not use it. */
 int paged_attn_partition_size(const pa_desc* desc);
 
 /* The kernel paged_attn_decode will run (PA_PATH_VALU, PA_PATH_MFMA_GRID or

@@ -112,5 +112,24 @@ __device__ __forceinline__ float quad_sum(float x) {
 // 0..7 (one chunk each) do.
 __device__ __forceinline__ int vswz(int R) { return ((R & 3) << 1) | ((R >> 2) & 1); }
 
+// Row offsets of the padded K and V tiles (16 rows of DW 16-bit elements).
+// Each bank line of the tile (256 bytes: one row at DW = 128, two rows at
+// DW = 64; one row at DW = 256) is followed by 32 bytes of pad. Measured with
+// gfx950's bank-conflict counter (SQ_LDS_BANK_CONFLICT), this layout makes
+// every LDS access of the decode's fold conflict-free: the score MFMA's
+// A-fragment read (one 16-byte chunk from each of the 16 rows, 128-bit), the
+// transposing 64-bit V^T read (32 contiguous bytes from each of 8 rows) and
+// the 128-bit staging writes of whole rows. Unpadded 256-byte rows cost 4 (A
+// fragments) and 2 (V^T) conflict cycles per instruction, rows padded by 16
+// bytes still 4 for the A fragments. Every fragment address is then a per-lane
+// base plus a constant.
+template <int DW>
+struct TileRows {
+  static constexpr int RPL = DW >= 128 ? 1 : 256 / (2 * DW);  // rows per pad
+  static constexpr int PAD = 16;                               // elements (32 bytes)
+  static constexpr int SIZE = 16 * DW + (16 / RPL) * PAD;
+  static __device__ __forceinline__ int row(int r) { return r * DW + (r / RPL) * PAD; }
+};
+
 }  // namespace
 }  // namespace pa

@@ -96,8 +96,9 @@ partition_stream_kernel(Params p) {
   static_assert((NBUF - 1) * 2 * LPC <= 63, "ring deeper than the vector-memory counter");
 
   constexpr bool kQLds = QL;  // Q' fragments in LDS (else in registers)
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[DS][16 * DW];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[DS][16 * DW];
+  typedef TileRows<DW> TR;  // padded K and V tiles (bank-conflict free reads)
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[DS][TR::SIZE];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[DS][TR::SIZE];
   __shared__ __attribute__((aligned(16))) V8 s_q[DS][kQLds ? 2 : 1][kQLds ? KS : 1][64];
   // partial scores of the pair, double-buffered by chunk parity
   __shared__ __attribute__((aligned(16))) f32x4 s_x[DS == 2 ? 2 : 1][DS][64];
@@ -373,14 +374,14 @@ partition_stream_kernel(Params p) {
 #pragma unroll
         for (int s = 0; s < LPC; ++s) {
           const int R = s * C::RPI + rowL;
-          *(uint4*)(s_k[half] + R * DW + 8 * (cc ^ (R & 7))) = rk[s];
-          *(uint4*)(s_v[half] + R * DW + 8 * (cc ^ vswz(R))) = rv[s];
+          *(uint4*)(s_k[half] + TR::row(R) + 8 * cc) = rk[s];
+          *(uint4*)(s_v[half] + TR::row(R) + 8 * cc) = rv[s];
         }
         // scores of the 16 tokens: lane (q, r) gets tokens 4q..4q+3 of head r
         f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const V8 a = *(const V8*)(s_k[half] + r * DW + 8 * ((4 * ks + q) ^ (r & 7)));
+          const V8 a = *(const V8*)(s_k[half] + TR::row(r) + 8 * (4 * ks + q));
           if constexpr (kQLds) {
             st = M::mma32(a, s_q[half][0][ks][lane], st);
             st = M::mma32(a, s_q[half][1][ks][lane], st);
@@ -429,12 +430,13 @@ partition_stream_kernel(Params p) {
         const V4 phi = M::pack(ph), plo = M::pack(pl2);
 
         // O^T += V^T P^T; lane (q, 4j + k) points the transposing read at row
-        // 4q + j, columns 16 mb + 4k .. +3 of the V tile
+        // 4q + j, columns 16 mb + 4k .. +3 of the V tile (logical chunk
+        // 2 mb + k / 2, its half k % 2)
+        const int vbase = TR::row(4 * q + tj) + 8 * (tk >> 1) + 4 * (tk & 1);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int pc = 2 * (mb ^ tj) + ((tk >> 1) ^ (q & 1));
           const s16x4 a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(s_v[half] + (4 * q + tj) * DW + 8 * pc + 4 * (tk & 1)));
+              (lds_s16x4*)(s_v[half] + vbase + 16 * mb));
           const V4 av = __builtin_bit_cast(V4, a4);
           acc[mb] = M::mma16(av, phi, acc[mb]);
           acc[mb] = M::mma16(av, plo, acc[mb]);
