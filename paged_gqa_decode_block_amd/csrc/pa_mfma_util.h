@@ -106,12 +106,6 @@ __device__ __forceinline__ float quad_sum(float x) {
   return __builtin_bit_cast(float, (int)c[0]) + __builtin_bit_cast(float, (int)c[1]);
 }
 
-// V tile swizzle: 16-byte chunk cc of row R lives at cc ^ vswz(R), so the 16
-// lanes of a quad in a transposing read (rows 4q..4q+3, two chunks each) hit 8
-// different bank groups. K tile: cc ^ (R & 7), so the A-fragment reads of rows
-// 0..7 (one chunk each) do.
-__device__ __forceinline__ int vswz(int R) { return ((R & 3) << 1) | ((R >> 2) & 1); }
-
 // Row offsets of the padded K and V tiles (16 rows of DW 16-bit elements).
 // Each bank line of the tile (256 bytes: one row at DW = 128, two rows at
 // DW = 64; one row at DW = 256) is followed by 32 bytes of pad. Measured with

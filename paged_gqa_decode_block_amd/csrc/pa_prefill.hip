@@ -54,8 +54,13 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   constexpr int HPW = kHeadsPerGroup / NW;
   static_assert(PPT * kThreads == 4 * D, "the workgroup loads a chunk in whole pieces");
   static_assert((NBUF - 1) * PPT <= 60, "ring deeper than the vector-memory counter");
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][32 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][32 * D];
+  // 32-row K and V tiles with the decode's padded rows (one 32-byte pad per
+  // 256-byte bank line: conflict-free fragment reads and staging writes)
+  typedef TileRows<D> TR;
+  constexpr int kTile = 32 * D + (32 / TR::RPL) * TR::PAD;
+  constexpr int kHalf = 16 * D + (16 / TR::RPL) * TR::PAD;  // TR::row(16 + x) - TR::row(x)
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kTile];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -131,7 +136,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
     const int jj = pisv[k] ? i - 2 * D : i;
     const int row = jj / (D / 8), cc = jj % (D / 8);
     poff[k] = row * (pisv[k] ? vst_bytes : kst_bytes) + 16 * cc;
-    plds[k] = row * D + 8 * (cc ^ (pisv[k] ? vswz(row) : (row & 7)));
+    plds[k] = TR::row(row) + 8 * cc;
   }
 
   const int32_t* trow = p.table + (int64_t)b * p.MBS;
@@ -193,7 +198,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        const V8 a = *(const V8*)(sk + (16 * tau + r) * D + 8 * ((4 * ks + q) ^ (r & 7)));
+        const V8 a = *(const V8*)(sk + tau * kHalf + TR::row(r) + 8 * (4 * ks + q));
         st[tau] = M::mma32(a, qhi[j][ks], st[tau]);
         st[tau] = M::mma32(a, qlo[j][ks], st[tau]);
       }
@@ -232,12 +237,12 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
       phi[i] = hh;
       plo[i] = (T)(pv[i] - (float)hh);
     }
+    const int vbase = TR::row(4 * q + tj) + 8 * (tk >> 1) + 4 * (tk & 1);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int pcol = 2 * (mb ^ tj) + ((tk >> 1) ^ (q & 1));
-      const int o = (4 * q + tj) * D + 8 * pcol + 4 * (tk & 1);
+      const int o = vbase + 16 * mb;
       const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + o));
-      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + 16 * D + o));
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + kHalf + o));
       const V8 av = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[j][mb] = M::mma32(av, phi, acc[j][mb]);
       acc[j][mb] = M::mma32(av, plo, acc[j][mb]);
@@ -263,7 +268,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
       issue(c + NBUF - 1, ring[sn], idr[sn]);
       __builtin_amdgcn_sched_barrier(0);
       if (c < nch2) {
-        const int buf = (c >> 1) & 1, half = (c & 1) * 16 * D;
+        const int buf = (c >> 1) & 1, half = (c & 1) * kHalf;
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
           uint16_t* dst = pisv[k] ? s_v[buf] : s_k[buf];
