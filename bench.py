@@ -381,9 +381,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 
 def measure_prefill(k: int, torch, steps: int, warmup: int) -> dict:
     """The paged varlen prefill (causal) on prefill workload k: one call per
-    step, inputs resident on the GPU. Useful flops count 2 multiply-adds per
-    attended (query row, head, key, dim) for Q.K and the same for P.V; the
-    kernel's matrix-core work is four times that (Q and P in hi + lo parts)."""
+    step, inputs resident on the GPU, q and out in bf16 (a bf16 model's
+    prefill; the headline fields) and in fp32 (``fp32_q_out``). Useful flops
+    count 2 multiply-adds per attended (query row, head, key, dim) for Q.K and
+    the same for P.V. The matrix cores do exactly that work for bf16 q (Q and
+    P each one 16-bit part); fp32 q goes in hi + lo parts, 1.5 times the
+    work."""
     import paged_gqa_decode_block_amd as pa
     from paged_gqa_decode_block_amd import workload as W
 
@@ -396,11 +399,13 @@ def measure_prefill(k: int, torch, steps: int, warmup: int) -> dict:
             torch.bfloat16).to("cuda")[1:]
 
     qd = torch.from_numpy(q).to("cuda")
+    qd16 = qd.to(torch.bfloat16)
     kp, vp = pool(c.k_store), pool(c.v_store)
     table = torch.from_numpy(c.block_table).to("cuda")
     cud = torch.from_numpy(cu).to("cuda")
     sk = torch.from_numpy(c.seqlens).to("cuda")
     out = torch.empty_like(qd)
+    out16 = torch.empty_like(qd16)
     qlens = np.diff(cu).astype(np.int64)
     max_q = int(qlens.max())
     L = c.seqlens.astype(np.int64)
@@ -408,25 +413,31 @@ def measure_prefill(k: int, torch, steps: int, warmup: int) -> dict:
     flops = 4.0 * c.Hq * c.D * keys
     kv_bytes = int(L.sum()) * c.Hkv * c.D * 2 * 2
 
-    def call():
-        pa.paged_attn_prefill(qd, kp, vp, table, cud, sk, c.scale, out, max_seqlen_q=max_q,
-                              causal=True)
+    def timed(qq, oo):
+        def call():
+            pa.paged_attn_prefill(qq, kp, vp, table, cud, sk, c.scale, oo, max_seqlen_q=max_q,
+                                  causal=True)
+        for _ in range(warmup):
+            call()
+        ms = time_steps(torch, call, steps)
+        return ms, flops / (ms / 1e3) / 1e12
 
-    for _ in range(warmup):
-        call()
-    ms = time_steps(torch, call, steps)
-    tf = flops / (ms / 1e3) / 1e12
-    log(f"[bench] {c.name}: prefill {ms * 1e3:.1f} us/step, {tf:.1f} useful TFLOP/s")
+    ms, tf = timed(qd16, out16)
+    ms32, tf32 = timed(qd, out)
+    log(f"[bench] {c.name}: prefill {ms * 1e3:.1f} us/step, {tf:.1f} useful TFLOP/s (bf16 q/out); "
+        f"{ms32 * 1e3:.1f} us/step, {tf32:.1f} TFLOP/s (fp32 q/out)")
     r = {"workload": c.name, "batch": c.B, "num_q_heads": c.Hq, "num_kv_heads": c.Hkv,
-         "head_dim": c.D, "block_size": c.bs, "kv_dtype": c.kv_dtype, "causal": True,
-         "total_q_rows": int(cu[-1]), "total_cached_tokens": int(L.sum()), "seed": 2000 + k,
-         "us_per_step": round(ms * 1e3, 2), "useful_tflops": round(tf, 2),
+         "head_dim": c.D, "block_size": c.bs, "kv_dtype": c.kv_dtype, "q_out_dtype": "bf16",
+         "causal": True, "total_q_rows": int(cu[-1]), "total_cached_tokens": int(L.sum()),
+         "seed": 2000 + k, "us_per_step": round(ms * 1e3, 2), "useful_tflops": round(tf, 2),
          "kv_bytes": kv_bytes,
+         "fp32_q_out": {"us_per_step": round(ms32 * 1e3, 2), "useful_tflops": round(tf32, 2),
+                        "frac_of_bf16_peak": round(tf32 / MFMA_BF16_PEAK_TFLOPS, 4)},
          "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                       "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                       "traffic": None, "kernel": "prefill_kernel",
                       "algorithmic_flops_per_launch": flops}}
-    del qd, kp, vp, out
+    del qd, qd16, kp, vp, out, out16
     torch.cuda.empty_cache()
     return r
 

@@ -10,11 +10,14 @@
 // One workgroup per eight (16-row query tile, query head) units of one KV
 // head: 8 / hh consecutive tiles of a sequence times hh of the KV head's query
 // heads (hh = 8, or the largest power of two dividing G, so that no unit is
-// empty). Its threads load each 16-token chunk of K and V once (16-byte
-// pieces, raw buffer loads through descriptors cut to the chunk's attended
-// rows, an invalid table entry never dereferenced) into a ring of chunks in
-// registers, and stage two consecutive chunks into one of two 32-token LDS
-// tiles; after one barrier per tile every wave folds its units against it:
+// empty). All the workgroups of one (sequence, KV head) read the same K and V,
+// so they are placed on one XCD, whose L2 serves the repeats (the loads keep
+// the default cache policy). Its threads load each 16-token chunk of K and V
+// once (16-byte pieces, raw buffer loads through descriptors cut to the
+// chunk's attended rows, an invalid table entry never dereferenced) into a
+// ring of chunks in registers, and stage two consecutive chunks into one of
+// two 32-token LDS tiles; after one barrier per tile every wave folds its
+// units against it:
 //
 //   scores  S^T[token, row] = K[token, :] . Q'[row, :]       16x16x32 MFMAs,
 //           two 16-token halves
@@ -23,9 +26,21 @@
 //   output  O^T[dim, row] += V^T[dim, token] . P^T[token, row]  16x16x32 over
 //           the 32 tokens
 //
-// with a tile's 16 rows as the MFMA columns and Q' and P in hi + lo 16-bit
-// parts. (On gfx950 a 16x16x16 bf16 MFMA takes as long as a 16x16x32 one, so
-// the output product runs on 32-token tiles.) The workgroup walks the tokens
+// with a tile's 16 rows as the MFMA columns. (On gfx950 a 16x16x16 bf16 MFMA
+// takes as long as a 16x16x32 one, so the output product runs on 32-token
+// tiles.)
+//
+// Operand precision. Q': bf16 q over bf16 K is exact in bf16 (sign(scale) q),
+// so the scores are exact fp32 sums and |scale| log2 e is applied to them;
+// otherwise Q' = q scale log2 e goes in hi + lo 16-bit parts (~16 significant
+// bits, two MFMAs). P: the probabilities (at most 2^8 with the lazy max) go to
+// fp16, 11 significant bits, and the row sums add the rounded values, so the
+// output is a convex combination of V rows whose weights carry a relative
+// error of at most 2^-11: within the fp16/bf16 tolerance even for a sharply
+// peaked softmax. bf16 V is converted to fp16 as it is staged; a 32-token
+// tile holding a bf16 V value of magnitude 2^16 or more (beyond fp16's
+// finite range), or an infinity, is staged again from memory as bf16 and
+// folded with P in bf16 hi + lo parts (~16 significant bits). The workgroup walks the tokens
 // up to its last tile's last row's key end; a token is masked per column, so
 // each row ends at its own causal bound. No partial state leaves the
 // workgroup: each unit is normalised and written at the end.
@@ -37,6 +52,33 @@ namespace pa {
 namespace {
 
 constexpr int kHeadsPerGroup = 8;  // (tile, head) units per workgroup: 8 / NW per wave
+constexpr int kXcds = 8;            // gfx950 (MI350 series): eight XCDs, each with its own L2
+
+// Eight bf16 values (16 bytes) as fp16, exact where fp16 has the value (below
+// 2^-14 it keeps fp16's subnormal grid); big: one of them is finite with
+// magnitude 2^16 or more, which fp16 cannot hold, or infinite. (A NaN gives
+// NaN on either path.)
+__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 w, bool& big) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out[4];
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __builtin_bit_cast(float, in[i] << 16);
+    f[2 * i + 1] = __builtin_bit_cast(float, in[i] & 0xffff0000u);
+    out[i] = __builtin_bit_cast(uint32_t, h2{(_Float16)f[2 * i], (_Float16)f[2 * i + 1]});
+  }
+  // the largest magnitude, by three-input maxima with |.| on the operands (a
+  // threshold test needs no quieting of the operands first)
+  float m0, m1, m2, m3;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m0) : "v"(f[0]), "v"(f[1]), "v"(f[2]));
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m1) : "v"(f[3]), "v"(f[4]), "v"(f[5]));
+  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(m2) : "v"(f[6]), "v"(f[7]), "v"(m0));
+  asm("v_max_f32 %0, %1, %2" : "=v"(m3) : "v"(m1), "v"(m2));
+  big = m3 >= 65536.f;
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
 
 // NW waves per workgroup (4: two heads per wave; 8: one head per wave, half
 // the registers, so that d = 256 runs two waves per SIMD), NBUF ring slots,
@@ -44,10 +86,14 @@ constexpr int kHeadsPerGroup = 8;  // (tile, head) units per workgroup: 8 / NW p
 template <typename T, int D, int NW, int NBUF, int OCC, int QO>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, int hh,
-               int ntiles) {
+               int ntiles, int per) {
   typedef Mx<T> M;
   typedef typename M::v8 V8;
-  typedef typename M::v4 V4;
+  typedef Mx<_Float16> H;
+  typedef typename H::v8 H8;
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  constexpr bool kBf = std::is_same<T, __bf16>::value;
+  constexpr bool kQ1 = kBf && QO == 1;  // Q' exact in one bf16 part
   constexpr int KS = D / 32, MB = D / 16;
   constexpr int kThreads = 64 * NW;
   constexpr int PPT = 4 * D / kThreads;  // 16-byte pieces of a chunk per thread (4 D of them)
@@ -59,27 +105,38 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   typedef TileRows<D> TR;
   constexpr int kTile = 32 * D + (32 / TR::RPL) * TR::PAD;
   constexpr int kHalf = 16 * D + (16 / TR::RPL) * TR::PAD;  // TR::row(16 + x) - TR::row(x)
+  // V tiles hold fp16 (bf16 V converted while staged) except in a tile with a
+  // value beyond fp16's range, which is staged again as bf16; s_wide[i]: the
+  // index of the last such tile staged in LDS tile i
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kTile];
+  __shared__ int s_wide[2];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // w: the wave's
   const int r = lane & 15, q = lane >> 4;
   // The workgroup's 8 (tile, head) units: tpw = 8 / hh consecutive 16-row
   // tiles times hh query heads of KV head hk (heads g0 .. g0 + hh - 1 of its
   // group). Each K/V chunk it loads serves all eight.
   const int tpw = kHeadsPerGroup / hh;
-  const int b = blockIdx.z;
-  const int hk = (int)blockIdx.y / nhg, g0 = ((int)blockIdx.y % nhg) * hh;
+  // The per work items of one (sequence, KV head) read the same K and V: they
+  // all go to one XCD (workgroup i runs on XCD i mod kXcds), whose L2 then
+  // serves the repeated reads. XCD x takes the pairs x, x + kXcds, ...
+  const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+  const int pair = xcd + kXcds * (slot / per), item = slot % per;
+  if (pair >= p.B * p.Hkv) return;  // padding of the last round
+  const int b = pair / p.Hkv, hk = pair % p.Hkv;
+  const int g0 = (item % nhg) * hh;
   const int hcount = min(hh, p.G - g0);
-  const int pw0 = 16 * tpw * (int)blockIdx.x;  // first row of the workgroup's tiles
+  const int pw0 = 16 * tpw * (item / nhg);  // first row of the workgroup's tiles
   const int r0 = cu_q[b];
   const int ql = cu_q[b + 1] - r0;
+  const bool first = item == 0 && hk == 0 && tid == 0;  // one report per sequence
   // rows beyond the grid would be left unwritten: report
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0 && p.status && (ql < 0 || ql > 16 * ntiles))
-    atomicOr(p.status, kStatusBadSeqlen);
+  if (first && p.status && (ql < 0 || ql > 16 * ntiles)) atomicOr(p.status, kStatusBadSeqlen);
   if (pw0 >= ql) return;  // the whole workgroup
-  const int L = clamped_len(p, b, blockIdx.x == 0 && blockIdx.y == 0 && tid == 0);
+  if (tid < 2) s_wide[tid] = -1;  // visible after the first tile's barrier
+  const int L = clamped_len(p, b, first);
   const int plast = min(pw0 + 16 * tpw - 1, ql - 1);
   const int kend = causal ? min(L, max(0, L - ql + plast + 1)) : L;  // the last tile's
   const int nch = (kend + 15) >> 4;
@@ -91,6 +148,10 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   // kfull[j]: the least key end over slot j's valid columns (the whole wave
   // agrees); a 32-token tile ending at or below it needs no mask
   int kfull[HPW];
+  // kQ1: Q' = sign(scale) q (exact) and the scores are scaled by qmul in fp32;
+  // else Q' = q scale log2 e in hi + lo parts and qmul = 1
+  const float qmul = kQ1 ? (p.qscale != 0.f ? fabsf(p.qscale) : 1.f) : 1.f;
+  const float qfac = kQ1 ? (p.qscale > 0.f ? 1.f : p.qscale < 0.f ? -1.f : 0.f) : p.qscale;
   V8 qhi[HPW][KS], qlo[HPW][KS];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
@@ -113,29 +174,32 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
       const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float y = col_ok[j] ? x[k] * p.qscale : 0.f;
+        const float y = col_ok[j] ? x[k] * qfac : 0.f;
         const T hh = (T)y;
         qhi[j][ks][k] = hh;
-        qlo[j][ks][k] = (T)(y - (float)hh);
+        if constexpr (!kQ1) qlo[j][ks][k] = (T)(y - (float)hh);
       }
     }
   }
 
-  // the pieces this thread loads: piece i = tid + 64 NW k of the chunk's 4 D
-  // (K pieces first): row, 16-byte column and whether it is V
+  // The pieces this thread loads: a chunk's K or V rows are 16 x D / 8
+  // 16-byte pieces, piece 64 (wh PPT + k) + lane taken by wave wh of one half
+  // of the workgroup. The two halves swap K and V from one chunk to the next,
+  // so every wave builds one buffer descriptor per chunk and loads (and, for
+  // bf16, converts) V every other chunk.
   const int bsm = (1 << p.bs_log2) - 1;
   const int kst_bytes = (int)(p.kst * (int)sizeof(T)), vst_bytes = (int)(p.vst * (int)sizeof(T));
-  int poff[PPT], plds[PPT];
-  bool pisv[PPT];
+  const int64_t ksb_bytes = p.ksb * (int64_t)sizeof(T), vsb_bytes = p.vsb * (int64_t)sizeof(T);
+  const int wh = w % (NW / 2);
+  const bool vodd = w < NW / 2;  // this half loads V of the odd chunks, K of the even ones
+  auto chunk_is_v = [&](int cn) -> bool { return vodd == ((cn & 1) != 0); };
+  int poffk[PPT], poffv[PPT], plds[PPT];
 #pragma unroll
   for (int k = 0; k < PPT; ++k) {
-    const int i = tid + kThreads * k;
-    // a wave's 64 pieces are consecutive and 2 D is a multiple of 64, so K or V
-    // is the same across the wave: made visibly uniform for the descriptor choice
-    pisv[k] = __builtin_amdgcn_readfirstlane(i >= 2 * D ? 1 : 0) != 0;
-    const int jj = pisv[k] ? i - 2 * D : i;
+    const int jj = 64 * (wh * PPT + k) + lane;
     const int row = jj / (D / 8), cc = jj % (D / 8);
-    poff[k] = row * (pisv[k] ? vst_bytes : kst_bytes) + 16 * cc;
+    poffk[k] = row * kst_bytes + 16 * cc;
+    poffv[k] = row * vst_bytes + 16 * cc;
     plds[k] = TR::row(row) + 8 * cc;
   }
 
@@ -153,7 +217,21 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   int bad_block = 0;
   // (the lambdas are forced inline: called out of line, their ring arguments
   // would live in scratch memory)
-  auto issue = [&](int cn, uint4 (&pc)[PPT], int& ids) __attribute__((always_inline)) {
+  // descriptor of chunk cn's K or V rows for (validated) block id, empty for
+  // id < 0
+  auto chunk_rsrc = [&](int cn, int id, bool isv) __attribute__((always_inline)) {
+    const int tok0 = 16 * cn;
+    const int rows = id >= 0 ? min(16, kend - tok0) : 0;
+    const int row0 = id >= 0 ? tok0 & bsm : 0;
+    const int64_t idc = id >= 0 ? (int64_t)id : 0;
+    const int st = isv ? vst_bytes : kst_bytes;
+    return uniform_rsrc((isv ? vbase : kbase) + idc * (isv ? vsb_bytes : ksb_bytes) +
+                            (int64_t)row0 * st,
+                        rows * st);
+  };
+  // load this wave's pieces of chunk cn into pc; ids: the chunk's block id on
+  // entry, then the id of chunk cn + NBUF; cid: the id the loads used
+  auto issue = [&](int cn, uint4 (&pc)[PPT], int& ids, int& cid) __attribute__((always_inline)) {
     int id = __builtin_amdgcn_readfirstlane(ids);
     if (cn >= nch) {
       id = -1;
@@ -161,18 +239,11 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
       bad_block = 1;
       id = -1;
     }
-    const int tok0 = 16 * cn;
-    const int rows = id >= 0 ? min(16, kend - tok0) : 0;
-    const int64_t row0 = id >= 0 ? (int64_t)(tok0 & bsm) : 0;
-    const int64_t idc = id >= 0 ? (int64_t)id : 0;
-    const __amdgpu_buffer_rsrc_t rsk =
-        uniform_rsrc(kbase + (idc * p.ksb + row0 * p.kst) * (int)sizeof(T), rows * kst_bytes);
-    const __amdgpu_buffer_rsrc_t rsv =
-        uniform_rsrc(vbase + (idc * p.vsb + row0 * p.vst) * (int)sizeof(T), rows * vst_bytes);
+    cid = id;
+    const bool isv = chunk_is_v(cn);
+    const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(cn, id, isv);
 #pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      pc[k] = buf_load<2>(pisv[k] ? rsv : rsk, poff[k]);  // a scalar select
-    }
+    for (int k = 0; k < PPT; ++k) pc[k] = buf_load<0>(rs, isv ? poffv[k] : poffk[k]);
     ids = fetch_id(cn + NBUF);
   };
 
@@ -188,9 +259,10 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   const int tj = r >> 2, tk = r & 3;
 
   // fold 32-token tile tc (tokens 32 tc .., staged in LDS tile `buf`) into
-  // head slot j. P^T k-slot i of lane (q, r) holds token 16 (i / 4) + 4 q + i % 4,
-  // the score MFMA's output layout of the two halves.
-  auto consume = [&](int tc, int buf, int j) __attribute__((always_inline)) {
+  // head slot j; `wide`: the tile's V has a value beyond fp16. P^T k-slot i of
+  // lane (q, r) holds token 16 (i / 4) + 4 q + i % 4, the score MFMA's output
+  // layout of the two halves.
+  auto consume = [&](int tc, int buf, int j, bool wide) __attribute__((always_inline)) {
     const uint16_t* sk = s_k[buf];
     const uint16_t* sv_ = s_v[buf];
     f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -200,7 +272,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
       for (int tau = 0; tau < 2; ++tau) {
         const V8 a = *(const V8*)(sk + tau * kHalf + TR::row(r) + 8 * (4 * ks + q));
         st[tau] = M::mma32(a, qhi[j][ks], st[tau]);
-        st[tau] = M::mma32(a, qlo[j][ks], st[tau]);
+        if constexpr (!kQ1) st[tau] = M::mma32(a, qlo[j][ks], st[tau]);
       }
     }
     float sv[8];
@@ -215,7 +287,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
     float mx = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-    const float mt = quad_max(mx);
+    const float mt = quad_max(mx) * qmul;
     const bool raise = mt > m[j] + 8.f;
     if (__ballot(raise)) {
       const float mn = raise ? mt : m[j];
@@ -228,24 +300,47 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
     const float mu = m[j] == -INFINITY ? 0.f : m[j];
     float pv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pv[i] = exp2_fast(sv[i] - mu);
-    l[j] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-    V8 phi, plo;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const T hh = (T)pv[i];
-      phi[i] = hh;
-      plo[i] = (T)(pv[i] - (float)hh);
-    }
+    for (int i = 0; i < 8; ++i) pv[i] = exp2_fast(fmaf(sv[i], qmul, -mu));
     const int vbase = TR::row(4 * q + tj) + 8 * (tk >> 1) + 4 * (tk & 1);
+    // P in fp16 against the fp16 V tile, or in bf16 hi + lo parts against a
+    // tile staged as bf16 (two separate loops: a branch inside one would keep
+    // each 16-dim block's LDS reads from being issued ahead of its MFMA)
+    H8 ph;
+    V8 phi, plo;
+    if (kBf && wide) {
+      l[j] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int o = vbase + 16 * mb;
-      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + o));
-      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + kHalf + o));
-      const V8 av = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[j][mb] = M::mma32(av, phi, acc[j][mb]);
-      acc[j][mb] = M::mma32(av, plo, acc[j][mb]);
+      for (int i = 0; i < 8; ++i) {
+        const T hh = (T)pv[i];
+        phi[i] = hh;
+        plo[i] = (T)(pv[i] - (float)hh);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ph[i] = (_Float16)pv[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        l[j] = __builtin_amdgcn_fdot2(h2{ph[2 * i], ph[2 * i + 1]}, h2{1, 1}, l[j], false);
+    }
+    if (kBf && wide) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int o = vbase + 16 * mb;
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + o));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + kHalf + o));
+        const V8 av = __builtin_bit_cast(V8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[j][mb] = M::mma32(av, phi, acc[j][mb]);
+        acc[j][mb] = M::mma32(av, plo, acc[j][mb]);
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int o = vbase + 16 * mb;
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + o));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + kHalf + o));
+        const H8 av = __builtin_bit_cast(H8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[j][mb] = H::mma32(av, ph, acc[j][mb]);
+      }
     }
   };
 
@@ -256,29 +351,51 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   // wave is done with the tile before, so the other tile is free.
   const int nch2 = (nch + 1) & ~1;
   uint4 ring[NBUF][PPT];
+  int cid[NBUF];
+  int id_even = -1;  // the block id of the last even chunk staged
   static_for<0, NBUF - 1>([&](auto S) {
     constexpr int s = decltype(S)::value;
-    issue(s, ring[s], idr[s]);
+    issue(s, ring[s], idr[s], cid[s]);
   });
   for (int cb = 0; cb < nch2; cb += NBUF) {
     static_for<0, NBUF>([&](auto S) {
       constexpr int s = decltype(S)::value;
       constexpr int sn = (s + NBUF - 1) % NBUF;
       const int c = cb + s;
-      issue(c + NBUF - 1, ring[sn], idr[sn]);
+      issue(c + NBUF - 1, ring[sn], idr[sn], cid[sn]);
       __builtin_amdgcn_sched_barrier(0);
       if (c < nch2) {
         const int buf = (c >> 1) & 1, half = (c & 1) * kHalf;
+        const bool isv = chunk_is_v(c);
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
-          uint16_t* dst = pisv[k] ? s_v[buf] : s_k[buf];
-          *(uint4*)(dst + half + plds[k]) = ring[s][k];
+          uint4 x = ring[s][k];
+          if constexpr (kBf) {
+            if (isv) {
+              bool big;
+              x = bf16x8_to_f16(x, big);
+              if (big) s_wide[buf] = c >> 1;
+            }
+          }
+          *(uint4*)((isv ? s_v[buf] : s_k[buf]) + half + plds[k]) = x;
         }
+        if (!(c & 1)) id_even = cid[s];
         if (c & 1) {
           __syncthreads();
+          const bool wide = kBf && __builtin_amdgcn_readfirstlane(s_wide[buf]) == (c >> 1);
+          if (kBf && wide) {
+            // stage the tile's V again, as the bf16 values: each wave reloads
+            // the V pieces it staged (of one of the two chunks)
+            const int cv = chunk_is_v(c) ? c : c - 1;
+            const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(cv, cv == c ? cid[s] : id_even, true);
+#pragma unroll
+            for (int k = 0; k < PPT; ++k)
+              *(uint4*)(s_v[buf] + (cv & 1) * kHalf + plds[k]) = buf_load<0>(rs, poffv[k]);
+            __syncthreads();
+          }
 #pragma unroll
           for (int j = 0; j < HPW; ++j)
-            if (hon[j]) consume(c >> 1, buf, j);
+            if (hon[j]) consume(c >> 1, buf, j, wide);
         }
       }
     });
@@ -301,14 +418,17 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   if (bad_block && tid == 0 && p.status) atomicOr(p.status, kStatusBadBlock);
 }
 
-// {waves per workgroup, ring slots, waves per SIMD} per head_dim
-constexpr int kPrefillCfg[3][3] = {{4, 6, 2}, {8, 4, 4}, {8, 4, 2}};
+// {waves per workgroup, ring slots, waves per SIMD} per q/out type and
+// head_dim (fp32 q at d = 128 holds Q' in two parts: a ring of two slots keeps
+// the loop within the 128 registers of four waves per SIMD)
+constexpr int kPrefillCfg[2][3][3] = {{{4, 6, 2}, {8, 2, 4}, {8, 4, 2}},
+                                      {{4, 6, 2}, {8, 4, 4}, {8, 4, 2}}};
 constexpr int pdim(int D) { return D == 64 ? 0 : D == 128 ? 1 : 2; }
 
 template <typename T, int D, int QO>
 hipError_t launch_p(const Params& p, const int32_t* cu_q, int max_q, int causal, hipStream_t s) {
-  constexpr int NW = kPrefillCfg[pdim(D)][0], NB_ = kPrefillCfg[pdim(D)][1],
-                OCC = kPrefillCfg[pdim(D)][2];
+  constexpr int NW = kPrefillCfg[QO][pdim(D)][0], NB_ = kPrefillCfg[QO][pdim(D)][1],
+                OCC = kPrefillCfg[QO][pdim(D)][2];
   // heads per workgroup: 8 when they divide G; else the largest power of two
   // dividing G, with 8 / hh tiles per workgroup so that no unit is idle, if
   // there are that many tiles (else 8, the last group partly empty)
@@ -321,9 +441,14 @@ hipError_t launch_p(const Params& p, const int32_t* cu_q, int max_q, int causal,
   }
   const int tpw = kHeadsPerGroup / hh;
   const int nhg = (p.G + hh - 1) / hh;
-  dim3 grid((ntiles + tpw - 1) / tpw, p.Hkv * nhg, p.B);
-  hipLaunchKernelGGL((prefill_kernel<T, D, NW, NB_, OCC, QO>), grid, dim3(64 * NW), 0, s, p,
-                     cu_q, causal, nhg, hh, ntiles);
+  // per (sequence, KV head): tile groups x head groups; pairs spread over the
+  // XCDs, the last round padded with empty workgroups
+  const int64_t per = (int64_t)((ntiles + tpw - 1) / tpw) * nhg;
+  const int64_t rounds = ((int64_t)p.B * p.Hkv + kXcds - 1) / kXcds;
+  const int64_t blocks = kXcds * rounds * per;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((prefill_kernel<T, D, NW, NB_, OCC, QO>), dim3((unsigned)blocks),
+                     dim3(64 * NW), 0, s, p, cu_q, causal, nhg, hh, ntiles, (int)per);
   return hipGetLastError();
 }
 

@@ -32,11 +32,11 @@ def _pool(torch, case, store):
     return t.view(torch.bfloat16 if case.kv_dtype == "bf16" else torch.float16).to("cuda")[1:]
 
 
-def _make(rng, *, Hq, Hkv, D, bs, kv_dtype, klens, qlens, layout="HND"):
+def _make(rng, *, Hq, Hkv, D, bs, kv_dtype, klens, qlens, layout="HND", **kw):
     klens = np.asarray(klens, dtype=np.int32)
     qlens = np.asarray(qlens, dtype=np.int32)
     case, _, _ = paged_case(rng, B=len(klens), Hq=Hq, Hkv=Hkv, D=D, bs=bs, kv_dtype=kv_dtype,
-                            seqlens=klens, layout=layout)
+                            seqlens=klens, layout=layout, **kw)
     cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
     q = rng.standard_normal((int(cu[-1]), Hq, D)).astype(np.float32)
     return case, cu, q
@@ -119,9 +119,10 @@ def test_prefill_last_row_is_the_decode(torch_cuda):
 def test_prefill_bf16_q_and_out(torch_cuda, D, Hq, Hkv):
     """q given in bf16 and out written in bf16 (PA_FLAG_QO_BF16): q is drawn as
     values bf16 holds exactly, so the oracle sees the same queries the kernel
-    reads. The bf16 output is the fp32 path's output rounded to nearest even
-    (torch's conversion), bit for bit, and within the K/V tolerance plus half
-    a bf16 ulp of the oracle."""
+    reads. bf16 q over bf16 K gives exact products (the scale is applied to the
+    fp32 scores), fp32 q goes in hi + lo parts with the scale folded in, so the
+    two calls differ in rounding only: each is within the K/V tolerance of the
+    oracle, the bf16 output plus half a bf16 ulp."""
     from paged_gqa_decode_block_amd import workload as W
 
     torch = torch_cuda
@@ -132,10 +133,72 @@ def test_prefill_bf16_q_and_out(torch_cuda, D, Hq, Hkv):
     want = _oracle(case, cu, q, True)
     got16 = _gpu(torch, case, cu, q, True, bf16=True)
     got32 = _gpu(torch, case, cu, q, True)
-    rounded = torch.from_numpy(got32.astype(np.float32)).to(torch.bfloat16).float().numpy()
-    assert np.array_equal(got16, rounded.astype(np.float64))
-    assert np.isfinite(got16).all()
+    assert np.isfinite(got16).all() and np.isfinite(got32).all()
     assert (np.abs(got16 - want) <= 3e-3 + np.abs(want) * 2.0 ** -8).all()
+    assert np.abs(got32 - want).max() <= 3e-3
+
+
+@pytest.mark.parametrize("bf16_q", [False, True], ids=["q32", "q16"])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_prefill_peaked_softmax(torch_cuda, dt, bf16_q):
+    """Scores with a standard deviation of 8 (K and V drawn with std 2, scale
+    4/sqrt(d)): a few keys carry nearly all the weight, the case where the
+    16-bit rounding of the probabilities weighs most. Within the K/V tolerance
+    of the oracle (plus half a bf16 ulp for bf16 out)."""
+    from paged_gqa_decode_block_amd import workload as W
+
+    torch = torch_cuda
+    rng = np.random.default_rng(1310 + (dt == "f16") + 2 * bf16_q)
+    case, cu, q = _make(rng, Hq=16, Hkv=2, D=128, bs=16, kv_dtype=dt, klens=[37, 500, 1200],
+                        qlens=[37, 64, 100], scale=4.0 / np.sqrt(128), kv_std=2.0)
+    if bf16_q:
+        q = W.from_storage(W.to_storage(q, "bf16"), "bf16").astype(np.float32)
+    want = _oracle(case, cu, q, True)
+    got = _gpu(torch, case, cu, q, True, bf16=bf16_q)
+    assert np.isfinite(got).all()
+    tol = 3e-3 + (np.abs(want) * 2.0 ** -8 if bf16_q else 0.0)
+    err = np.abs(got - want)
+    print(f"peaked softmax {dt} {'bf16' if bf16_q else 'fp32'} q: max-abs error {err.max():.3e}")
+    assert (err <= tol).all()
+
+
+def _set_v(case, b, t, h, dim, value):
+    """Set V[token t of sequence b, KV head h, dim] in the pool (HND)."""
+    from paged_gqa_decode_block_amd import workload as W
+
+    blk = 1 + int(case.block_table[b, t // case.bs])
+    case.v_store[blk, h, t % case.bs, dim] = W.to_storage(np.array([value], np.float32),
+                                                          case.kv_dtype)[0]
+
+
+@pytest.mark.parametrize("bf16_q", [False, True], ids=["q32", "q16"])
+def test_prefill_v_beyond_f16_range(torch_cuda, bf16_q):
+    """bf16 V values that fp16 cannot hold: tokens in 32-token tiles 2 and 6
+    of sequence 0 hold +-3e5 and -65536 (the smallest bf16 magnitude beyond
+    fp16's range), tile 4 holds 65280 (the largest bf16 value fp16 holds), and
+    sequence 1 is untouched. Every output is finite and within 3e-3 of the
+    oracle relative to max(1, |want|) (plus half a bf16 ulp for bf16 out)."""
+    from paged_gqa_decode_block_amd import workload as W
+
+    torch = torch_cuda
+    rng = np.random.default_rng(1320 + bf16_q)
+    case, cu, q = _make(rng, Hq=8, Hkv=2, D=128, bs=16, kv_dtype="bf16", klens=[300, 200],
+                        qlens=[40, 20])
+    _set_v(case, 0, 70, 0, 5, 3.0e5)
+    _set_v(case, 0, 71, 1, 100, -3.0e5)
+    _set_v(case, 0, 130, 1, 7, 65280.0)
+    _set_v(case, 0, 200, 0, 64, -65536.0)
+    if bf16_q:
+        q = W.from_storage(W.to_storage(q, "bf16"), "bf16").astype(np.float32)
+    want = _oracle(case, cu, q, True)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = _gpu(torch, case, cu, q, True, bf16=bf16_q, status=status)
+    assert int(status.item()) == 0
+    assert np.isfinite(got).all()
+    assert np.abs(want).max() > 100.0            # the large values do reach the output
+    err = np.abs(got - want) / np.maximum(1.0, np.abs(want))
+    print(f"V beyond fp16: max error relative to max(1, |want|) {err.max():.3e}")
+    assert err.max() <= 3e-3 + (2.0 ** -8 if bf16_q else 0.0)
 
 
 def test_prefill_reports_rows_beyond_max_seqlen_q(torch_cuda):
