@@ -111,9 +111,19 @@ typedef enum pa_path {
 
 /* pa_desc.flags bits. */
 #define PA_FLAG_KV_SHARED 1  /* physical blocks may be listed by several sequences   */
-                             /* (prefix sharing): keep K/V loads cacheable so shared */
-                             /* blocks are reused from cache; without it K/V are     */
-                             /* streamed with non-temporal loads                     */
+                             /* (prefix sharing, as the block manager of the        */
+                             /* paged-attention-runtime design notes does): K/V     */
+                             /* loads stay cacheable (without the flag they are     */
+                             /* non-temporal), and on the streaming path sequences  */
+                             /* are taken in groups of F = 16 / G (G <= 8): the     */
+                             /* leading blocks that all of a group's members list   */
+                             /* (the same valid block ids) and attend whole, at     */
+                             /* least 256 tokens, are read once for the group, its  */
+                             /* F x G query heads filling the score MFMA's 16       */
+                             /* columns; each member's remaining tokens are its own */
+                             /* stream, and the combine merges the two. Results do  */
+                             /* not depend on the grouping beyond rounding. Members */
+                             /* of one family are best adjacent in the batch.       */
 #define PA_FLAG_QO_BF16 2    /* q and out are bf16 instead of fp32 (accumulation,     */
                              /* partial states and the combine stay fp32; out is      */
                              /* rounded to nearest even once, at the end)             */
@@ -212,6 +222,8 @@ int paged_attn_decode(const pa_desc* desc, const void* q, const void* k_cache,
  *     cached tokens below it; a small explicit partition_size raises the need).
  *   - PA_PATH_MFMA_FUSED returns PA_E_PATH: its arrival counters would have to
  *     be zero in the shared array.
+ *   - PA_FLAG_KV_SHARED does not group sequences here (no prefix folding): the
+ *     need is the workspace size of the same descriptor without the flag.
  *   - Every call on a device uses that device's one array, which keeps the last
  *     call's contents (no call relies on them). Calls that may overlap in time
  *     on one device -- on different streams, or from several host threads
@@ -319,7 +331,9 @@ int paged_attn_prefill(const pa_desc* desc, const void* q, const void* k_cache,
  * one partition always suffices. Streaming path (PA_PATH_MFMA_STREAM): two
  * state slots per wave of the kernel's grid, which depends on the device's
  * compute-unit count, and a two-int record per (sequence, KV head); the
- * partition size does not enter. MFMA_FUSED: its arrival counters first (see
+ * partition size does not enter. With PA_FLAG_KV_SHARED grouping (see the
+ * flag) also a record per (group, KV head), the slots' rows sized for the F x G
+ * columns, the groups' lengths and one state's rows per stream. MFMA_FUSED: its arrival counters first (see
  * pa_path). Otherwise the contents need no initialisation and carry nothing
  * between calls. Returns 0 for an invalid descriptor too; call
  * paged_attn_validate first. */

@@ -217,6 +217,31 @@ int validate(const pa_desc* d) {
   return PA_OK;
 }
 
+// Prefix folding (streaming path, blocks shared between sequences): groups of
+// F = 16 / G consecutive sequences (G <= 8), whose shared leading blocks are
+// read once with the F x G query heads in the score MFMA's 16 columns. 0 when
+// it does not apply: another path, no sharing declared, G > 8, or more
+// virtual sequences (groups x (F + 1)) than the kernel's 1024. The
+// PAGEDATTN_FOLD=0 environment switch (read once) turns it off for A/B runs.
+int fold_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("PAGEDATTN_FOLD");
+    v = (e && e[0] == '0') ? 0 : 1;
+  }
+  return v;
+}
+int fold_factor(const pa_desc* d) {
+  if (!(d->flags & PA_FLAG_KV_SHARED) || !fold_enabled() || d->batch < 2) return 0;
+  if (pick_path(d) != PA_PATH_MFMA_STREAM) return 0;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const int F = 16 / G;
+  if (F < 2) return 0;
+  const int64_t groups = ((int64_t)d->batch + F - 1) / F;
+  if (groups * (F + 1) > 1024) return 0;
+  return F;
+}
+
 // Workspace regions of a valid descriptor, as byte offsets (each 256-byte
 // aligned; off[kWsParts] is the total): for the merged grid variant first an
 // arrival word per (sequence, KV head) (at offset 0 for every descriptor; zero
@@ -224,19 +249,32 @@ int validate(const pa_desc* d) {
 // kernels the partition states m, l, acc of every (sequence, query head,
 // partition), nothing when one partition always suffices; for the streaming
 // kernel a record per (sequence, KV head) stream and two state slots (m, l and
-// acc of the G heads) per wave of its grid (per pair of waves at head_dim 256).
-enum { kWsCnt, kWsM, kWsL, kWsAcc, kWsLink, kWsCm, kWsCl, kWsCacc, kWsParts };
-void workspace_layout(const pa_desc* d, size_t* off) {
+// acc of the G heads, or with folding of the F x G prefix columns) per wave of
+// its grid (per pair of waves at head_dim 256), and with folding a record per
+// (group, KV head) prefix stream, the F + 1 virtual sequences' lengths of
+// each group (its prefix, then each member past it) and state rows of every
+// stream for the ones that lie inside one share but are not written out.
+enum { kWsCnt, kWsM, kWsL, kWsAcc, kWsLink, kWsCm, kWsCl, kWsCacc, kWsPre, kWsOm, kWsOl, kWsOacc,
+       kWsParts };
+void workspace_layout(const pa_desc* d, size_t* off, int fold) {
   const int part = pick_partition(d);
   const int64_t pmax = (max_tokens(d) + part - 1) / part;
   const bool stream = pick_path(d) == PA_PATH_MFMA_STREAM;
   size_t sz[kWsParts] = {0};
   if (stream) {
     const int G = d->num_q_heads / d->num_kv_heads;
+    const size_t rps = fold > 0 ? (size_t)fold * G : (size_t)G;
+    const size_t groups = fold > 0 ? ((size_t)d->batch + fold - 1) / fold : 0;
     const size_t slots = 2 * (size_t)stream_waves(d);
-    sz[kWsLink] = (size_t)d->batch * d->num_kv_heads * 2 * sizeof(int32_t);
-    sz[kWsCm] = sz[kWsCl] = slots * G * sizeof(float);
-    sz[kWsCacc] = slots * G * d->head_dim * sizeof(float);
+    sz[kWsLink] = ((size_t)d->batch + groups) * d->num_kv_heads * 2 * sizeof(int32_t);
+    sz[kWsCm] = sz[kWsCl] = slots * rps * sizeof(float);
+    sz[kWsCacc] = slots * rps * d->head_dim * sizeof(float);
+    sz[kWsPre] = groups * (fold + 1) * sizeof(int32_t);
+    if (fold > 0) {
+      const size_t orows = ((size_t)d->batch + groups) * d->num_kv_heads * rps;
+      sz[kWsOm] = sz[kWsOl] = orows * sizeof(float);
+      sz[kWsOacc] = orows * d->head_dim * sizeof(float);
+    }
   } else if (pmax > 1) {
     const size_t rows = (size_t)d->batch * d->num_q_heads * (size_t)pmax;
     sz[kWsM] = sz[kWsL] = rows * sizeof(float);
@@ -282,7 +320,7 @@ int paged_attn_resolved_path(const pa_desc* desc) {
 size_t paged_attn_workspace_size(const pa_desc* desc) {
   if (validate(desc) != PA_OK) return 0;
   size_t off[kWsParts + 1];
-  workspace_layout(desc, off);
+  workspace_layout(desc, off, fold_factor(desc));
   return off[kWsParts];
 }
 
@@ -334,7 +372,7 @@ namespace {
 int prepare(const pa_desc* desc, const void* q, const void* k_cache, const void* v_cache,
             const int32_t* block_table, const int32_t* cache_seqlens, float scale, void* out,
             void* workspace, size_t workspace_bytes, int32_t* status, bool need_inputs,
-            pa::Params& p, bool need_ws = true) {
+            pa::Params& p, bool need_ws = true, bool allow_fold = true) {
   int rc = validate(desc);
   if (rc != PA_OK) return rc;
   memset(&p, 0, sizeof p);
@@ -343,7 +381,10 @@ int prepare(const pa_desc* desc, const void* q, const void* k_cache, const void*
   if (!cache_seqlens || !out) return PA_E_NULL;
   if (need_inputs && (!q || !k_cache || !v_cache || !block_table)) return PA_E_NULL;
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15) return PA_E_ALIGN;
-  const size_t need = need_ws ? paged_attn_workspace_size(desc) : 0;
+  const int fold = allow_fold ? fold_factor(desc) : 0;
+  size_t off[kWsParts + 1];
+  workspace_layout(desc, off, fold);
+  const size_t need = need_ws ? off[kWsParts] : 0;
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255)))
     return PA_E_WORKSPACE;
 
@@ -374,11 +415,18 @@ int prepare(const pa_desc* desc, const void* q, const void* k_cache, const void*
   p.cus = cu_count();
   p.qo_bf16 = (desc->flags & PA_FLAG_QO_BF16) ? 1 : 0;
   p.xpacked = (desc->flags & PA_FLAG_KV_XPACKED) ? 1 : 0;
+  p.rps = p.G;
   if (need > 0) {
-    size_t off[kWsParts + 1];
-    workspace_layout(desc, off);
     char* ws = (char*)workspace;
     if (pick_path(desc) == PA_PATH_MFMA_STREAM) {
+      if (fold > 0) {
+        p.fold = fold;
+        p.rps = fold * p.G;
+        p.ws_vlen = (int32_t*)(ws + off[kWsPre]);
+        p.ws_om = (float*)(ws + off[kWsOm]);
+        p.ws_ol = (float*)(ws + off[kWsOl]);
+        p.ws_oacc = (float*)(ws + off[kWsOacc]);
+      }
       p.ws_link = (int32_t*)(ws + off[kWsLink]);
       p.ws_cm = (float*)(ws + off[kWsCm]);
       p.ws_cl = (float*)(ws + off[kWsCl]);
@@ -399,8 +447,10 @@ int run_partition(const pa_desc* desc, const pa::Params& p, hipStream_t s) {
   hipError_t e;
   switch (pick_path(desc)) {
     case PA_PATH_MFMA_STREAM:
-      e = pa::launch_partition_stream(p, desc->kv_dtype, stream_variant_for(desc),
-                                      !(desc->flags & PA_FLAG_KV_SHARED) && stream_nt(), s);
+      e = pa::launch_fold_scan(p, s);
+      if (e == hipSuccess)
+        e = pa::launch_partition_stream(p, desc->kv_dtype, stream_variant_for(desc),
+                                        !(desc->flags & PA_FLAG_KV_SHARED) && stream_nt(), s);
       break;
     case PA_PATH_MFMA_GRID:
     case PA_PATH_MFMA_FUSED: e = pa::launch_partition_mfma(p, desc->kv_dtype, s); break;
@@ -416,6 +466,19 @@ int run_combine(const pa::Params& p, hipStream_t s) {
   return pa::launch_combine(p, s) == hipSuccess ? PA_OK : PA_E_LAUNCH;
 }
 
+int decode_impl(const pa_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_table, const int32_t* cache_seqlens, float scale, void* out,
+                void* workspace, size_t workspace_bytes, int32_t* status, void* stream,
+                bool allow_fold) {
+  pa::Params p;
+  int rc = prepare(desc, q, k_cache, v_cache, block_table, cache_seqlens, scale, out, workspace,
+                   workspace_bytes, status, true, p, true, allow_fold);
+  if (rc != PA_OK || p.B == 0) return rc;
+  rc = run_partition(desc, p, (hipStream_t)stream);
+  if (rc != PA_OK) return rc;
+  return run_combine(p, (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -424,13 +487,8 @@ int paged_attn_decode(const pa_desc* desc, const void* q, const void* k_cache, c
                       const int32_t* block_table, const int32_t* cache_seqlens, float scale,
                       void* out, void* workspace, size_t workspace_bytes, int32_t* status,
                       void* stream) {
-  pa::Params p;
-  int rc = prepare(desc, q, k_cache, v_cache, block_table, cache_seqlens, scale, out, workspace,
-                   workspace_bytes, status, true, p);
-  if (rc != PA_OK || p.B == 0) return rc;
-  rc = run_partition(desc, p, (hipStream_t)stream);
-  if (rc != PA_OK) return rc;
-  return run_combine(p, (hipStream_t)stream);
+  return decode_impl(desc, q, k_cache, v_cache, block_table, cache_seqlens, scale, out, workspace,
+                     workspace_bytes, status, stream, true);
 }
 
 }  // extern "C"
@@ -475,15 +533,19 @@ int paged_attn_decode_static(const pa_desc* desc, const void* q, const void* k_c
   if (rc != PA_OK) return rc;
   // the merged grid variant keeps arrival counters that would have to be zero
   if (pick_path(desc) == PA_PATH_MFMA_FUSED) return PA_E_PATH;
-  const size_t need = paged_attn_workspace_size(desc);
+  // without prefix folding: its state rows would not fit the scratch for
+  // batches that the unfolded layout does
+  size_t off[kWsParts + 1];
+  workspace_layout(desc, off, 0);
+  const size_t need = off[kWsParts];
   if (need > PA_STATIC_SCRATCH_BYTES) return PA_E_SCRATCH;
   void* ws = nullptr;
   if (need > 0 && desc->batch > 0) {
     ws = scratch_for_current_device();
     if (!ws) return PA_E_LAUNCH;
   }
-  return paged_attn_decode(desc, q, k_cache, v_cache, block_table, cache_seqlens, scale, out, ws,
-                           need > 0 ? PA_STATIC_SCRATCH_BYTES : 0, status, stream);
+  return decode_impl(desc, q, k_cache, v_cache, block_table, cache_seqlens, scale, out, ws,
+                     need > 0 ? PA_STATIC_SCRATCH_BYTES : 0, status, stream, false);
 }
 
 int paged_attn_decode_append(const pa_desc* desc, const void* q, const void* k_new,

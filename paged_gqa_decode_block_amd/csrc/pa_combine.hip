@@ -15,8 +15,10 @@
 // the slot of its first wave's state and the number n of consecutive waves
 // whose states make up the stream (0 when its output was written directly);
 // wave w_a + i, i >= 1, left its state in its slot 0. A record is trusted only
-// for a non-empty sequence (every non-empty stream's record is rewritten by
-// each call); an empty sequence gets zeros.
+// for a non-empty stream (every non-empty stream's record is rewritten by
+// each call); an empty sequence gets zeros. With prefix folding a sequence has
+// two such runs: its group's folded prefix (the states' column for this
+// member and head) and its own stream past the prefix, if not empty.
 //
 // Grid (D / 64, H_q, B), 16 x S threads: thread (stripe s, quad u) owns dims
 // 4u .. 4u+3 of a 64-dim slice (float4 loads) and states i = s, s + S, ....
@@ -43,28 +45,54 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
   const int d = blockIdx.x * 64 + 4 * u;
   const bool waves = p.ws_link != nullptr;  // states of the streaming kernel's waves
   const int hk = h / p.G, g = h - hk * p.G;
-  // both loads issued before either is used
+  const int gi = p.fold > 0 ? b / p.fold : 0;
+  const bool folded = waves && p.fold > 0;
+  // the loads issued before any is used
   const int2 rec = waves ? *(const int2*)(p.ws_link + 2 * ((int64_t)b * p.Hkv + hk)) : make_int2(0, 0);
+  const int2 recf =
+      folded ? *(const int2*)(p.ws_link + 2 * ((int64_t)(p.B + gi) * p.Hkv + hk)) : make_int2(0, 0);
+  const int pre = folded ? p.ws_vlen[gi * (p.fold + 1)] : 0;
   const int L = clamped_len(p, b, false);
-  int n;
+  int n, nf = 0;
+  // a record is always in range when this call's partition kernel wrote it;
+  // anything else reads nothing (zeros) rather than outside the slots. x = -1:
+  // one state in the stream's own rows (folding only)
+  auto in_range = [&](int2 r, int c) {
+    if (r.x == -1) return c == 1 && p.ws_om != nullptr;
+    return r.x >= 0 && r.x < 2 * p.nwaves && c >= 0 && (r.x >> 1) + c <= p.nwaves;
+  };
   if (waves) {
-    if (L > 0 && rec.y == 0) return;  // written out by the partition kernel
-    n = L > 0 ? rec.y : 0;
-    // a record is always in range when this call's partition kernel wrote it;
-    // anything else reads nothing (zeros) rather than outside the slots
-    if (rec.x < 0 || rec.x >= 2 * p.nwaves || n < 0 || (rec.x >> 1) + n > p.nwaves) n = 0;
+    const bool own = L > pre;  // the sequence's own stream has tokens
+    if (own && pre == 0 && rec.y == 0) return;  // written out by the partition kernel
+    n = own ? rec.y : 0;
+    if (!in_range(rec, n)) n = 0;
+    nf = pre > 0 ? recf.y : 0;
+    if (!in_range(recf, nf)) nf = 0;
   } else {
     n = (L + p.part - 1) / p.part;
     if (n <= 1) return;
   }
 
-  // state i of the (sequence, head): its max, sum and unnormalised output
+  // state i of the (sequence, head): its max, sum and unnormalised output;
+  // after the own stream's n states come the folded prefix's nf
   const int64_t row = ((int64_t)b * p.Hq + h) * p.pmax;
+  const int colf = (b - gi * p.fold) * p.G + g;  // this head's column in the prefix states
+  const int nown = n;
+  // the state's row, in the wave slots or (x = -1) in the stream's own rows
+  // (negative: own row -1 - row)
   auto state_row = [&](int i) -> int64_t {
     if (!waves) return -1;
-    const int slot = i == 0 ? rec.x : 2 * ((rec.x >> 1) + i);
-    return (int64_t)slot * p.G + g;
+    if (i < nown) {
+      if (rec.x == -1) return -1 - (((int64_t)b * p.Hkv + hk) * p.rps + g);
+      const int slot = i == 0 ? rec.x : 2 * ((rec.x >> 1) + i);
+      return (int64_t)slot * p.rps + g;
+    }
+    const int k = i - nown;
+    if (recf.x == -1) return -1 - (((int64_t)(p.B + gi) * p.Hkv + hk) * p.rps + colf);
+    const int slot = k == 0 ? recf.x : 2 * ((recf.x >> 1) + k);
+    return (int64_t)slot * p.rps + colf;
   };
+  n += nf;
 
   // (m, l, a) <- (m, l, a) merged with (cm, cl, ca)
   auto merge = [](float& m, float& l, float4& a, float cm, float cl, float4 ca) {
@@ -92,9 +120,16 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
       if (i < n) {
         if (waves) {
           const int64_t sr = state_row(i);
-          mv[k] = p.ws_cm[sr];
-          lv[k] = p.ws_cl[sr];
-          av[k] = *(const float4*)(p.ws_cacc + sr * p.D + d);
+          if (sr >= 0) {
+            mv[k] = p.ws_cm[sr];
+            lv[k] = p.ws_cl[sr];
+            av[k] = *(const float4*)(p.ws_cacc + sr * p.D + d);
+          } else {
+            const int64_t orow = -1 - sr;
+            mv[k] = p.ws_om[orow];
+            lv[k] = p.ws_ol[orow];
+            av[k] = *(const float4*)(p.ws_oacc + orow * p.D + d);
+          }
         } else {
           mv[k] = p.ws_m[row + i];
           lv[k] = p.ws_l[row + i];

@@ -23,11 +23,29 @@ struct Params {
   float* ws_l;              // [B, Hq, pmax]  sum of 2^(s - m)
   float* ws_acc;            // [B, Hq, pmax, D] unnormalised output
   // streaming kernel only (NULL otherwise): a record per stream and two state
-  // slots per wave (the partly covered streams at the ends of its share)
-  int32_t* ws_link;         // [B, Hkv, 2] first state's slot, number of waves (0: written out)
-  float* ws_cm;             // [waves, 2, G] running max, base-2 units
-  float* ws_cl;             // [waves, 2, G] sum of 2^(s - m)
-  float* ws_cacc;           // [waves, 2, G, D] unnormalised output
+  // slots per wave (the partly covered streams at the ends of its share); with
+  // folding, records of the groups' shared-prefix streams follow the B x Hkv
+  // records of the sequences' own streams
+  int32_t* ws_link;         // [B (+ groups), Hkv, 2] first state's slot, number of waves
+                            // (0: written out)
+  float* ws_cm;             // [waves, 2, rps] running max, base-2 units
+  float* ws_cl;             // [waves, 2, rps] sum of 2^(s - m)
+  float* ws_cacc;           // [waves, 2, rps, D] unnormalised output
+  // prefix folding on the streaming path (fold = 0: off): sequences
+  // fold * i .. fold * i + fold - 1 form group i; its first ws_vlen[(fold + 1) i]
+  // tokens, the same physical blocks in every member's table, are read once
+  // for all members (their fold x G query heads in the score MFMA's 16
+  // columns), and ws_vlen[(fold + 1) i + 1 + m] tokens past them as member m's
+  // own stream
+  int fold;
+  int rps;                  // state rows per slot: G, or fold * G with folding
+  int32_t* ws_vlen;         // [groups, fold + 1] token counts of the virtual sequences
+  // with folding, the state of a stream that lies inside one wave's share but
+  // is not written out (a folded prefix, or a member's stream behind one) goes
+  // to the stream's own rows (record x = -1): stream record i, rows i * rps ..
+  float* ws_om;             // [B + groups, Hkv, rps]
+  float* ws_ol;             // [B + groups, Hkv, rps]
+  float* ws_oacc;           // [B + groups, Hkv, rps, D]
   // grid kernel with the merge in its last block (NULL otherwise): arrivals per
   // (sequence, KV head), zero between calls
   int32_t* ws_cnt;          // [B, Hkv]
@@ -68,6 +86,9 @@ hipError_t launch_append(const Params& p, const void* k_new, const void* v_new, 
 // `variant` picks a ring depth / occupancy pair (0 = default), `nt` the
 // non-temporal cache policy for K/V loads.
 hipError_t launch_partition_stream(const Params& p, int dtype, int variant, bool nt, hipStream_t s);
+// Prefix folding: each group's folded prefix and the virtual sequences'
+// lengths (p.ws_vlen), before the streaming kernel.
+hipError_t launch_fold_scan(const Params& p, hipStream_t s);
 bool stream_supports(int dtype, int D, int G, int block_size, int batch);
 // Grid of the streaming kernel (one wave per workgroup) for head_dim D, ring
 // variant `variant`, `cus` compute units and at most `chunk_bound` 16-token

@@ -36,7 +36,7 @@
 // per-chunk buffer descriptor (built in scalar registers) starts at the chunk's
 // first row and its size covers only the attended rows, so rows past L_b and
 // chunks behind an invalid table entry read as zeros without touching memory.
-// Each chunk is then written to two swizzled LDS tiles and read back in MFMA
+// Each chunk is then written to two padded LDS tiles and read back in MFMA
 // operand layout:
 //
 //   scores  S^T[token, head] = K[token, :] . Q'[head, :]      16x16x32 MFMAs
@@ -56,9 +56,20 @@
 // and chunks behind an invalid table entry are never loaded; their scores are
 // -inf.
 //
+// Prefix folding (blocks declared shared): sequences are taken in groups of F
+// = 16 / G, and the streams become those of virtual sequences: per group its
+// folded prefix (the leading blocks every member lists and attends whole,
+// found by fold_scan_kernel), read through the first member's table with the
+// F x G (member, head) pairs as the score MFMA's 16 columns (the padding the
+// G heads alone leave), then each member's tokens past the prefix. Neither
+// kind is written out: a stream inside one share leaves its one state in its
+// own rows, a shared one a state per wave as above, and the combine merges a
+// sequence's own states with its column of the group's prefix states. The
+// prefix is read once per group instead of once per member.
+//
 // Requires block_size >= 16 (a 16-token chunk lies in one block), at most 1024
-// sequences (the chunk prefix is formed in registers) and fewer than 2^31
-// chunks per KV head in the batch.
+// (virtual) sequences (the chunk prefix is formed in registers) and fewer than
+// 2^31 chunks per KV head in the batch.
 #include <type_traits>
 
 #include "pa_mfma_util.h"
@@ -120,26 +131,34 @@ partition_stream_kernel(Params p) {
   // partition; the wave then leaves that piece as a continuation state.
   // All windows' lengths are loaded before any is checked, so the loads travel
   // together; wave 0 reports an out-of-range length once.
-  const int nwin = (p.B + 63) >> 6;
+  //
+  // With prefix folding the streams are those of virtual sequences: group i
+  // (sequences F i .. F i + F - 1) is virtual sequences (F + 1) i (its folded
+  // prefix, read through the first member's table) and (F + 1) i + 1 + m
+  // (member m's own tokens past the prefix), whose lengths the fold scan left
+  // in p.ws_vlen (and which reported any out-of-range length).
+  const int F = p.fold;
+  const int nv = F > 0 ? (p.B + F - 1) / F * (F + 1) : p.B;
+  const int nwin = (nv + 63) >> 6;
   int ncw[kMaxWindows], lw[kMaxWindows];
   int tot = 0;
 #pragma unroll
   for (int wi = 0; wi < kMaxWindows; ++wi) {
-    const int b = wi * 64 + lane;
-    lw[wi] = (wi < nwin && b < p.B) ? p.seqlens[b] : 0;
+    const int v = wi * 64 + lane;
+    lw[wi] = (wi < nwin && v < nv) ? (F > 0 ? p.ws_vlen[v] : p.seqlens[v]) : 0;
   }
   {
     const int lmax = p.MBS << p.bs_log2;
     bool bad_len = false;
 #pragma unroll
     for (int wi = 0; wi < kMaxWindows; ++wi) {
-      const int b = wi * 64 + lane;
-      int Lb = lw[wi] + p.len_add;
-      if (wi < nwin && b < p.B && (Lb < 0 || Lb > lmax)) {
+      const int v = wi * 64 + lane;
+      int Lb = lw[wi] + (F > 0 ? 0 : p.len_add);
+      if (wi < nwin && v < nv && (Lb < 0 || Lb > lmax)) {
         bad_len = true;
         Lb = Lb < 0 ? 0 : lmax;
       }
-      lw[wi] = (wi < nwin && b < p.B) ? Lb : 0;
+      lw[wi] = (wi < nwin && v < nv) ? Lb : 0;
       ncw[wi] = (lw[wi] + 15) >> 4;
     }
     if (blockIdx.x == 0 && __ballot(bad_len) && lane == 0 && p.status)
@@ -166,7 +185,8 @@ partition_stream_kernel(Params p) {
   const int g_end = g + sh_base + (wx < sh_extra ? 1 : 0);
   if (g >= g_end) return;
 
-  // sequence holding chunk g: Hkv * P(b) <= g < Hkv * P(b + 1), P = prefix of nc
+  // (virtual) sequence holding chunk g: Hkv * P(v) <= g < Hkv * P(v + 1), P =
+  // prefix of nc; L is the stream's length in tokens
   int b = 0, ncb = 1, L = 0;
   int Pb = 0;
   {
@@ -180,7 +200,7 @@ partition_stream_kernel(Params p) {
         const uint64_t hit = __ballot(incl > x && ncw[wi] > 0);
         if (hit) {
           const int src = __builtin_ctzll(hit);
-          b = wi * 64 + src;
+          b = wi * 64 + src;  // the virtual sequence, resolved below
           ncb = __shfl(ncw[wi], src);
           L = __shfl(lw[wi], src);
           Pb = __shfl(incl, src) - ncb;
@@ -196,6 +216,10 @@ partition_stream_kernel(Params p) {
     hk = e / ncb;
     j = e - hk * ncb;
   }
+  // virtual sequence v: its table row b, first token toff, and whether it is
+  // a group's folded prefix (fseg, group gi, members nm); set by resolve(v)
+  int v = b, toff = 0, gi = 0, nm = 1;
+  bool fseg = false;
 
   const int bsm = (1 << p.bs_log2) - 1;
   const int rowL = lane / C::CPR;  // row within a load instruction
@@ -216,12 +240,22 @@ partition_stream_kernel(Params p) {
   int bad_block = 0;
   bool first_seg = true;
   while (g < g_end) {
+    if (F > 0) {
+      gi = v / (F + 1);
+      const int k = v - gi * (F + 1);
+      fseg = k == 0;
+      b = gi * F + (fseg ? 0 : k - 1);
+      toff = fseg ? 0 : p.ws_vlen[gi * (F + 1)];
+      nm = min(F, p.B - gi * F);
+    } else {
+      b = v;
+    }
     const int jA = j;
     const int nch = min(ncb - j, g_end - g);
     const int cs = Pb * Hkv + hk * ncb;  // the stream's first chunk in the batch
     {
-      const int T0 = 16 * jA;
-      const int T1 = min(L, 16 * (jA + nch));
+      const int T0 = toff + 16 * jA;
+      const int T1 = toff + min(L, 16 * (jA + nch));
       const int32_t* trow = p.table + (int64_t)b * p.MBS;
       const char* kbase = (const char*)p.k + (int64_t)hk * p.ksh * (int)sizeof(T);
       const char* vbase = (const char*)p.v + (int64_t)hk * p.vsh * (int)sizeof(T);
@@ -245,10 +279,14 @@ partition_stream_kernel(Params p) {
       // Q of head r (zero for padded heads): the loads are issued here, but
       // turned into Q' fragments only after the ring's first K/V loads are
       // issued, so the wave's first HBM requests do not wait for Q.
+      // column r of the score MFMA: head r of sequence b, or in a folded
+      // prefix head r % G of member r / G
+      const bool hv = fseg ? (r < nm * G) : r < G;
       float4 qa[KS], qb[KS];
       {
-        const bool hv = r < G;
-        const int64_t qrow = ((int64_t)b * p.Hq + hk * G + (hv ? r : 0)) * D + half * DW + 8 * q;
+        const int qb_ = fseg && hv ? b + r / G : b;
+        const int qh = hv ? (fseg ? r % G : r) : 0;
+        const int64_t qrow = ((int64_t)qb_ * p.Hq + hk * G + qh) * D + half * DW + 8 * q;
         // every lane loads (padded heads read head 0's row, a valid address)
         // and make_q zeroes padded heads: no branch around the loads
 #pragma unroll
@@ -259,7 +297,6 @@ partition_stream_kernel(Params p) {
       }
       V8 qhi[kQLds ? 1 : KS], qlo[kQLds ? 1 : KS];
       auto make_q = [&]() {
-        const bool hv = r < G;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           float x[8] = {qa[ks].x, qa[ks].y, qa[ks].z, qa[ks].w,
@@ -334,10 +371,17 @@ partition_stream_kernel(Params p) {
       // slot of its own state and the number of waves whose states make up
       // the stream (0 when the output was written here).
       auto flush = [&]() {
-        const bool whole = jA == 0 && nch == ncb;
+        // a stream inside this share is written out, except a folded prefix or
+        // a member's stream behind one: those leave their one state in the
+        // stream's own rows (with folding only); a stream that several waves
+        // share leaves one state per wave in the wave's slots
+        const bool inside = jA == 0 && nch == ncb;
+        const bool whole = inside && !fseg && toff == 0;
+        const bool own = inside && !whole;
+        const int64_t rec = fseg ? (int64_t)(p.B + gi) * Hkv + hk : (int64_t)b * Hkv + hk;
         const int slot = 2 * wx + (first_seg ? 0 : 1);
         const float lt = quad_sum(l);
-        if (r < G) {
+        if (hv) {
           if (whole) {
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
             const int64_t orow = ((int64_t)b * p.Hq + hk * G + r) * D + half * DW + 4 * q;
@@ -347,14 +391,14 @@ partition_stream_kernel(Params p) {
               store_out4<QO>(p, orow + 16 * mb, o[0], o[1], o[2], o[3]);
             }
           } else {
-            const int64_t row = (int64_t)slot * G + r;
-            float* ap = p.ws_cacc + row * D + half * DW + 4 * q;
+            const int64_t row = (own ? rec * p.rps : (int64_t)slot * p.rps) + r;
+            float* ap = (own ? p.ws_oacc : p.ws_cacc) + row * D + half * DW + 4 * q;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
               *(float4*)(ap + 16 * mb) = make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
             if (q == 0 && half == 0) {
-              p.ws_cm[row] = m;
-              p.ws_cl[row] = lt;
+              (own ? p.ws_om : p.ws_cm)[row] = m;
+              (own ? p.ws_ol : p.ws_cl)[row] = lt;
             }
           }
         }
@@ -364,7 +408,8 @@ partition_stream_kernel(Params p) {
           const int last = cs + ncb - 1;
           const int cut = sh_extra * (sh_base + 1);
           const int wl = last < cut ? last / (sh_base + 1) : sh_extra + (last - cut) / sh_base;
-          *(int2*)(p.ws_link + 2 * ((int64_t)b * Hkv + hk)) = make_int2(slot, whole ? 0 : wl - wx + 1);
+          *(int2*)(p.ws_link + 2 * rec) =
+              own ? make_int2(-1, 1) : make_int2(slot, whole ? 0 : wl - wx + 1);
         }
       };
 
@@ -480,9 +525,9 @@ partition_stream_kernel(Params p) {
       if (++hk == Hkv) {
         hk = 0;
         Pb += ncb;
-        do {  // ends: chunks remain, so a non-empty sequence follows
-          ++b;
-          L = clamped_len(p, b, false);
+        do {  // ends: chunks remain, so a non-empty stream follows
+          ++v;
+          L = F > 0 ? p.ws_vlen[v] : clamped_len(p, v, false);
           ncb = (L + 15) >> 4;
         } while (ncb == 0);
       }
@@ -543,7 +588,54 @@ hipError_t launch_d(const Params& p, int variant, bool nt, hipStream_t s) {
   return nt ? launch_v<T, 2>(p, variant, s) : launch_v<T, 0>(p, variant, s);
 }
 
+// One wave per group of p.fold consecutive sequences: the folded prefix is the
+// run of leading blocks that every member attends whole and whose table
+// entries are the same valid block in all members' tables, kept only when it
+// is at least kFoldMinTokens long (else 0: every member streams on its own).
+// Writes the group's F + 1 virtual lengths: the prefix, then each member's
+// clamped length past it (0 for members past the batch).
+constexpr int kFoldMinTokens = 256;
+__global__ void __launch_bounds__(64) fold_scan_kernel(Params p) {
+  const int gi = blockIdx.x, lane = threadIdx.x, F = p.fold;
+  const int b0 = gi * F, nm = min(F, p.B - b0);
+  // member lane's clamped length (an out-of-range one is reported once)
+  const int Lm = lane < nm ? clamped_len(p, b0 + lane, true) : 0x7fffffff;
+  int lmin = Lm;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) lmin = min(lmin, __shfl_xor(lmin, off));
+  int pre = 0;
+  if (nm >= 2) {
+    const int nblk = lmin >> p.bs_log2;  // blocks every member attends whole
+    int common = nblk;
+    for (int j0 = 0; j0 < nblk; j0 += 64) {
+      const int j = j0 + lane;
+      bool ok = true;
+      if (j < nblk) {
+        const int id = p.table[(int64_t)b0 * p.MBS + j];
+        ok = id >= 0 && id < p.NB;
+        for (int m = 1; m < nm; ++m) ok = ok && p.table[(int64_t)(b0 + m) * p.MBS + j] == id;
+      }
+      const uint64_t miss = __ballot(!ok);
+      if (miss) {
+        common = j0 + __builtin_ctzll(miss);
+        break;
+      }
+    }
+    pre = common << p.bs_log2;
+    if (pre < kFoldMinTokens) pre = 0;
+  }
+  const int Lprev = __shfl(Lm, (lane + 63) & 63);  // member lane - 1's length
+  if (lane <= F) p.ws_vlen[gi * (F + 1) + lane] = lane == 0 ? pre : (lane - 1 < nm ? Lprev - pre : 0);
+}
+
 }  // namespace
+
+hipError_t launch_fold_scan(const Params& p, hipStream_t s) {
+  if (p.fold <= 0 || p.B <= 0) return hipSuccess;
+  const int groups = (p.B + p.fold - 1) / p.fold;
+  hipLaunchKernelGGL(fold_scan_kernel, dim3(groups), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
 
 bool stream_supports(int dtype, int D, int G, int block_size, int batch) {
   return mfma_supports(dtype, D, G) && block_size >= 16 && batch <= kMaxWindows * 64;

@@ -180,6 +180,20 @@ def test_partition_size_choice_and_workspace():
         W = _stream_waves(d)
         want = _al(batch * 2 * 2 * 4) + 2 * _al(2 * W * 4 * 4) + _al(2 * W * 4 * 128 * 4)
         assert pa.workspace_size(d) == want, (part, mbs, batch)
+    # prefix folding (declared sharing, streaming path, G = 4 -> groups of 4):
+    # the records of the groups' prefix streams after the sequences', state
+    # rows of the 4 x 4 prefix columns per slot, the virtual lengths (5 per
+    # group) and every stream's own state rows
+    d = _desc(batch=8, path="mfma_stream", kv_shared=True)
+    W, groups, rps = _stream_waves(d), 2, 16
+    orows = (8 + groups) * 2 * rps
+    want = (_al((8 + groups) * 2 * 2 * 4) + 2 * _al(2 * W * rps * 4) + _al(2 * W * rps * 128 * 4)
+            + _al(groups * 5 * 4) + 2 * _al(orows * 4) + _al(orows * 128 * 4))
+    assert pa.workspace_size(d) == want
+    # no folding: one sequence, G = 16, or another kernel
+    for kw in (dict(batch=1), dict(num_q_heads=32), dict(path="mfma_grid", partition_size=64)):
+        args = dict(dict(batch=8, path="mfma_stream"), **kw)
+        assert pa.workspace_size(_desc(kv_shared=True, **args)) == pa.workspace_size(_desc(**args)), kw
     # automatic choice: 4096 for the streaming kernel; for the others 512,
     # halved while the grid would be small
     assert pa.partition_size(_desc(batch=1, max_blocks_per_seq=6250, num_blocks=6250,

@@ -83,6 +83,75 @@ def paged_case(rng, *, B, Hq, Hkv, D, bs, kv_dtype, seqlens, layout="HND", spare
     return case, Kc, Vc
 
 
+def shared_prefix_case(rng, *, Hq, Hkv, D, bs, kv_dtype, families, layout="HND", mismatch=None,
+                       spare=2):
+    """A batch whose sequences come in families sharing leading blocks.
+
+    ``families``: list of (prefix_blocks, [member lengths]). Each member lists
+    its family's prefix blocks first (as many as its length reaches), then
+    blocks of its own. ``mismatch`` = (family, member, block): that member's
+    prefix block is replaced by a private copy (same values, another physical
+    block), which ends what its group can share. Physical blocks are placed at
+    random; every token slot no listing attends is NaN-poisoned.
+    """
+    lens, rows, content = [], [], {}  # content: logical block -> source logical block
+    nlog = 0
+    for pb, members in families:
+        pre = list(range(nlog, nlog + pb))
+        nlog += pb
+        for L in members:
+            n = -(-int(L) // bs)
+            row = pre[:min(pb, n)] + list(range(nlog, nlog + max(0, n - pb)))
+            nlog += max(0, n - pb)
+            rows.append(row)
+            lens.append(int(L))
+    if mismatch is not None:
+        fi, mi, j = mismatch
+        b = sum(len(m) for _, m in families[:fi]) + mi
+        content[nlog] = rows[b][j]
+        rows[b][j] = nlog
+        nlog += 1
+    NB = nlog + spare
+    perm = rng.permutation(NB).astype(np.int32)       # logical -> physical
+    B = len(rows)
+    MBS = max(1, max(len(r) for r in rows) + int(rng.integers(0, 3)))
+    table = np.full((B, MBS), -1, dtype=np.int32)
+    for b, row in enumerate(rows):
+        table[b, :len(row)] = perm[row]
+    # tokens attended in each physical block (max over its listings)
+    att = np.zeros(NB, dtype=np.int64)
+    for b, row in enumerate(rows):
+        for j, lb in enumerate(row):
+            att[perm[lb]] = max(att[perm[lb]], min(bs, lens[b] - j * bs))
+    pool_dtype = np.float32 if kv_dtype == "f32" else np.uint16
+    shape = (NB + 1, Hkv, bs, D) if layout == "HND" else (NB + 1, bs, Hkv, D)
+    nan = np.float32(np.nan) if kv_dtype == "f32" else np.uint16(0x7FC0 if kv_dtype == "bf16" else 0x7E00)
+    k_store = np.full(shape, nan, dtype=pool_dtype)
+    v_store = np.full(shape, nan, dtype=pool_dtype)
+    vals = {}
+    for lb in range(nlog):
+        src = content.get(lb, lb)
+        if src not in vals:
+            vals[src] = tuple(W.to_storage(rng.standard_normal((Hkv, bs, D)).astype(np.float32), kv_dtype)
+                              for _ in range(2))
+    for lb in range(nlog):
+        kb, vb = vals[content.get(lb, lb)]
+        blk, n = 1 + perm[lb], int(att[perm[lb]])
+        if layout == "HND":
+            k_store[blk, :, :n] = kb[:, :n]
+            v_store[blk, :, :n] = vb[:, :n]
+        else:
+            k_store[blk, :n] = kb[:, :n].transpose(1, 0, 2)
+            v_store[blk, :n] = vb[:, :n].transpose(1, 0, 2)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    case = W.Case(
+        name="shared_prefix", kv_dtype=kv_dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB, MBS=MBS,
+        seqlens=np.asarray(lens, dtype=np.int32), block_table=table, q=q, k_store=k_store,
+        v_store=v_store, layout=layout, scale=float(np.float32(1.0 / math.sqrt(D))),
+    )
+    return case
+
+
 def run_oracle(case, **kw):
     from oracle import oracle as O
 
