@@ -35,8 +35,9 @@ namespace pa {
 namespace {
 
 // kStripes: partition stripes (4, 8, 16, 32 or 64); kBatch: partitions per thread per
-// round (1, 4 or 8); both chosen from the partition count.
-template <int kStripes, int kBatch>
+// round (1, 4 or 8); both chosen from the partition count. kFold: after the
+// streaming kernel with prefix folding (its own rows and the prefix states).
+template <int kStripes, int kBatch, bool kFold>
 __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
   static_assert(kStripes % 4 == 0, "whole waves of four stripes");
   const int b = blockIdx.z, h = blockIdx.y;
@@ -46,7 +47,7 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
   const bool waves = p.ws_link != nullptr;  // states of the streaming kernel's waves
   const int hk = h / p.G, g = h - hk * p.G;
   const int gi = p.fold > 0 ? b / p.fold : 0;
-  const bool folded = waves && p.fold > 0;
+  const bool folded = kFold;  // (the host launches kFold only with folding)
   // the loads issued before any is used
   const int2 rec = waves ? *(const int2*)(p.ws_link + 2 * ((int64_t)b * p.Hkv + hk)) : make_int2(0, 0);
   const int2 recf =
@@ -58,7 +59,7 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
   // anything else reads nothing (zeros) rather than outside the slots. x = -1:
   // one state in the stream's own rows (folding only)
   auto in_range = [&](int2 r, int c) {
-    if (r.x == -1) return c == 1 && p.ws_om != nullptr;
+    if (kFold && r.x == -1) return c == 1;
     return r.x >= 0 && r.x < 2 * p.nwaves && c >= 0 && (r.x >> 1) + c <= p.nwaves;
   };
   if (waves) {
@@ -82,8 +83,8 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
   // (negative: own row -1 - row)
   auto state_row = [&](int i) -> int64_t {
     if (!waves) return -1;
-    if (i < nown) {
-      if (rec.x == -1) return -1 - (((int64_t)b * p.Hkv + hk) * p.rps + g);
+    if (!kFold || i < nown) {
+      if (kFold && rec.x == -1) return -1 - (((int64_t)b * p.Hkv + hk) * p.rps + g);
       const int slot = i == 0 ? rec.x : 2 * ((rec.x >> 1) + i);
       return (int64_t)slot * p.rps + g;
     }
@@ -118,18 +119,19 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
       lv[k] = 0.f;
       av[k] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (i < n) {
-        if (waves) {
+        if (waves && kFold) {
+          // one load of each, from the slots or the own rows (selected addresses)
           const int64_t sr = state_row(i);
-          if (sr >= 0) {
-            mv[k] = p.ws_cm[sr];
-            lv[k] = p.ws_cl[sr];
-            av[k] = *(const float4*)(p.ws_cacc + sr * p.D + d);
-          } else {
-            const int64_t orow = -1 - sr;
-            mv[k] = p.ws_om[orow];
-            lv[k] = p.ws_ol[orow];
-            av[k] = *(const float4*)(p.ws_oacc + orow * p.D + d);
-          }
+          const bool o = sr < 0;
+          const int64_t rr = o ? -1 - sr : sr;
+          mv[k] = (o ? p.ws_om : p.ws_cm)[rr];
+          lv[k] = (o ? p.ws_ol : p.ws_cl)[rr];
+          av[k] = *(const float4*)((o ? p.ws_oacc : p.ws_cacc) + rr * p.D + d);
+        } else if (waves) {
+          const int64_t sr = state_row(i);
+          mv[k] = p.ws_cm[sr];
+          lv[k] = p.ws_cl[sr];
+          av[k] = *(const float4*)(p.ws_cacc + sr * p.D + d);
         } else {
           mv[k] = p.ws_m[row + i];
           lv[k] = p.ws_l[row + i];
@@ -205,25 +207,31 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_combine(const Params& p, hipStream_t s) {
+template <bool kFold>
+hipError_t launch_combine_t(const Params& p, hipStream_t s) {
   dim3 grid(p.D / 64, p.Hq, p.B);
   // stripes sized to the partition count: with few partitions per sequence
   // (long partitions over a large batch) small workgroups leave no thread idle
   if (p.pmax <= 4)
-    hipLaunchKernelGGL((combine_kernel<4, 1>), grid, dim3(64), 0, s, p);
+    hipLaunchKernelGGL((combine_kernel<4, 1, kFold>), grid, dim3(64), 0, s, p);
   else if (p.pmax <= 8)
-    hipLaunchKernelGGL((combine_kernel<8, 1>), grid, dim3(128), 0, s, p);
+    hipLaunchKernelGGL((combine_kernel<8, 1, kFold>), grid, dim3(128), 0, s, p);
   else if (p.pmax <= 16)
-    hipLaunchKernelGGL((combine_kernel<16, 1>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((combine_kernel<16, 1, kFold>), grid, dim3(256), 0, s, p);
   else if (p.pmax <= 64)
-    hipLaunchKernelGGL((combine_kernel<16, 4>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((combine_kernel<16, 4, kFold>), grid, dim3(256), 0, s, p);
   else if (p.pmax <= 256)
-    hipLaunchKernelGGL((combine_kernel<64, 4>), grid, dim3(1024), 0, s, p);
+    hipLaunchKernelGGL((combine_kernel<64, 4, kFold>), grid, dim3(1024), 0, s, p);
   else  // 512 threads: a batch of 8 needs more than the 128 registers of 1024-thread blocks
-    hipLaunchKernelGGL((combine_kernel<32, 8>), grid, dim3(512), 0, s, p);
+    hipLaunchKernelGGL((combine_kernel<32, 8, kFold>), grid, dim3(512), 0, s, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Params& p, hipStream_t s) {
+  return p.fold > 0 && p.ws_link && p.ws_om ? launch_combine_t<true>(p, s)
+                                            : launch_combine_t<false>(p, s);
 }
 
 }  // namespace pa

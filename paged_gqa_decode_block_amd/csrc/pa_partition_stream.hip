@@ -391,14 +391,19 @@ partition_stream_kernel(Params p) {
               store_out4<QO>(p, orow + 16 * mb, o[0], o[1], o[2], o[3]);
             }
           } else {
-            const int64_t row = (own ? rec * p.rps : (int64_t)slot * p.rps) + r;
-            float* ap = (own ? p.ws_oacc : p.ws_cacc) + row * D + half * DW + 4 * q;
+            // (own is the same in every lane: the selects stay scalar)
+            const bool ow = __builtin_amdgcn_readfirstlane(own ? 1 : 0) != 0;
+            float* const cacc = ow ? p.ws_oacc : p.ws_cacc;
+            float* const cm = ow ? p.ws_om : p.ws_cm;
+            float* const cl = ow ? p.ws_ol : p.ws_cl;
+            const int64_t row = (ow ? rec * p.rps : (int64_t)slot * p.rps) + r;
+            float* ap = cacc + row * D + half * DW + 4 * q;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
               *(float4*)(ap + 16 * mb) = make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
             if (q == 0 && half == 0) {
-              (own ? p.ws_om : p.ws_cm)[row] = m;
-              (own ? p.ws_ol : p.ws_cl)[row] = lt;
+              cm[row] = m;
+              cl[row] = lt;
             }
           }
         }
