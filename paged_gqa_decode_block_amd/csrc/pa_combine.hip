@@ -28,15 +28,19 @@
 // exchanges and the waves' through LDS. S is 4 or 8 when there are at most
 // that many states per (sequence, head), 16 up to 64, and 64 (32 beyond 256)
 // above (the host's bound or estimate of that count), so one round usually
-// covers them all.
+// covers them all. A grid of many (sequence, head, slice) items instead runs
+// one wave per item up to 64 states (S = 4, a batch of up to 4 states per
+// thread and round): there the launch's waves outnumber what the compute units
+// hold at once, and the fewer of them the sooner the last one ends.
 #include "pa_kernels.h"
 
 namespace pa {
 namespace {
 
-// kStripes: partition stripes (4, 8, 16, 32 or 64); kBatch: partitions per thread per
-// round (1, 4 or 8); both chosen from the partition count. kFold: after the
-// streaming kernel with prefix folding (its own rows and the prefix states).
+// kStripes: partition stripes (4, 8, 16, 32 or 64); kBatch: partitions per
+// thread per round (1, 2, 4 or 8); both chosen from the grid and the partition
+// count. kFold: after the streaming kernel with prefix folding (its own rows
+// and the prefix states).
 template <int kStripes, int kBatch, bool kFold>
 __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
   static_assert(kStripes % 4 == 0, "whole waves of four stripes");
@@ -210,6 +214,16 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
 template <bool kFold>
 hipError_t launch_combine_t(const Params& p, hipStream_t s) {
   dim3 grid(p.D / 64, p.Hq, p.B);
+  // one wave per item when the grid alone fills the GPU (about one wave per
+  // SIMD of 256 compute units); a batch of 2 or 4 states per thread per round
+  const int64_t items = (int64_t)grid.x * grid.y * grid.z;
+  if (items >= 1024 && p.pmax <= 64) {
+    if (p.pmax <= 8)
+      hipLaunchKernelGGL((combine_kernel<4, 2, kFold>), grid, dim3(64), 0, s, p);
+    else
+      hipLaunchKernelGGL((combine_kernel<4, 4, kFold>), grid, dim3(64), 0, s, p);
+    return hipGetLastError();
+  }
   // stripes sized to the partition count: with few partitions per sequence
   // (long partitions over a large batch) small workgroups leave no thread idle
   if (p.pmax <= 4)
