@@ -37,13 +37,16 @@
 // fp16, 11 significant bits, and the row sums add the rounded values, so the
 // output is a convex combination of V rows whose weights carry a relative
 // error of at most 2^-11: within the fp16/bf16 tolerance even for a sharply
-// peaked softmax. bf16 V is converted to fp16 as it is staged; a 32-token
-// tile holding a bf16 V value of magnitude 2^16 or more (beyond fp16's
-// finite range), or an infinity, is staged again from memory as bf16 and
-// folded with P in bf16 hi + lo parts (~16 significant bits). The workgroup walks the tokens
-// up to its last tile's last row's key end; a token is masked per column, so
-// each row ends at its own causal bound. No partial state leaves the
-// workgroup: each unit is normalised and written at the end.
+// peaked softmax. bf16 V is converted to fp16 as it is staged, without a
+// range check: a bf16 value of magnitude 2^16 or more (beyond fp16's finite
+// range) becomes an infinity there, and any product with it (0 x inf
+// included) leaves a non-finite output. A workgroup that finds a non-finite
+// value among its outputs folds all its tiles again with V staged as bf16 and
+// P in bf16 hi + lo parts (~16 significant bits); non-finite inputs lead
+// there too and give the same result on that pass. The workgroup walks the
+// tokens up to its last tile's last row's key end; a token is masked per
+// column, so each row ends at its own causal bound. No partial state leaves
+// the workgroup: each unit is normalised and written at the end.
 //
 // Requires 16-bit K/V and block_size >= 16.
 #include "pa_mfma_util.h"
@@ -55,10 +58,8 @@ constexpr int kHeadsPerGroup = 8;  // (tile, head) units per workgroup: 8 / NW p
 constexpr int kXcds = 8;            // gfx950 (MI350 series): eight XCDs, each with its own L2
 
 // Eight bf16 values (16 bytes) as fp16, exact where fp16 has the value (below
-// 2^-14 it keeps fp16's subnormal grid); big: one of them is finite with
-// magnitude 2^16 or more, which fp16 cannot hold, or infinite. (A NaN gives
-// NaN on either path.)
-__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 w, bool& big) {
+// 2^-14 it keeps fp16's subnormal grid; from 2^16 on, infinite).
+__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 w) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   const uint32_t in[4] = {w.x, w.y, w.z, w.w};
   uint32_t out[4];
@@ -69,14 +70,6 @@ __device__ __forceinline__ uint4 bf16x8_to_f16(uint4 w, bool& big) {
     f[2 * i + 1] = __builtin_bit_cast(float, in[i] & 0xffff0000u);
     out[i] = __builtin_bit_cast(uint32_t, h2{(_Float16)f[2 * i], (_Float16)f[2 * i + 1]});
   }
-  // the largest magnitude, by three-input maxima with |.| on the operands (a
-  // threshold test needs no quieting of the operands first)
-  float m0, m1, m2, m3;
-  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m0) : "v"(f[0]), "v"(f[1]), "v"(f[2]));
-  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m1) : "v"(f[3]), "v"(f[4]), "v"(f[5]));
-  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(m2) : "v"(f[6]), "v"(f[7]), "v"(m0));
-  asm("v_max_f32 %0, %1, %2" : "=v"(m3) : "v"(m1), "v"(m2));
-  big = m3 >= 65536.f;
   return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
@@ -105,12 +98,11 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   typedef TileRows<D> TR;
   constexpr int kTile = 32 * D + (32 / TR::RPL) * TR::PAD;
   constexpr int kHalf = 16 * D + (16 / TR::RPL) * TR::PAD;  // TR::row(16 + x) - TR::row(x)
-  // V tiles hold fp16 (bf16 V converted while staged) except in a tile with a
-  // value beyond fp16's range, which is staged again as bf16; s_wide[i]: the
-  // index of the last such tile staged in LDS tile i
+  // V tiles hold fp16 (bf16 V converted while staged), or bf16 on the second
+  // pass of a workgroup whose first pass left a non-finite output (s_redo)
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kTile];
-  __shared__ int s_wide[2];
+  __shared__ int s_redo;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // w: the wave's
@@ -135,7 +127,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   // rows beyond the grid would be left unwritten: report
   if (first && p.status && (ql < 0 || ql > 16 * ntiles)) atomicOr(p.status, kStatusBadSeqlen);
   if (pw0 >= ql) return;  // the whole workgroup
-  if (tid < 2) s_wide[tid] = -1;  // visible after the first tile's barrier
+  if (tid == 0) s_redo = 0;  // visible after the first tile's barrier
   const int L = clamped_len(p, b, first);
   const int plast = min(pw0 + 16 * tpw - 1, ql - 1);
   const int kend = causal ? min(L, max(0, L - ql + plast + 1)) : L;  // the last tile's
@@ -211,9 +203,6 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   auto fetch_id = [&](int cn) -> int {
     return (int)__builtin_amdgcn_raw_buffer_load_b32(rst, ((16 * cn) >> p.bs_log2) * 4, 0, 0);
   };
-  int idr[NBUF];
-  static_for<0, NBUF>([&](auto S) { idr[decltype(S)::value] = fetch_id(decltype(S)::value); });
-
   int bad_block = 0;
   // (the lambdas are forced inline: called out of line, their ring arguments
   // would live in scratch memory)
@@ -230,8 +219,8 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
                         rows * st);
   };
   // load this wave's pieces of chunk cn into pc; ids: the chunk's block id on
-  // entry, then the id of chunk cn + NBUF; cid: the id the loads used
-  auto issue = [&](int cn, uint4 (&pc)[PPT], int& ids, int& cid) __attribute__((always_inline)) {
+  // entry, then the id of chunk cn + NBUF
+  auto issue = [&](int cn, uint4 (&pc)[PPT], int& ids) __attribute__((always_inline)) {
     int id = __builtin_amdgcn_readfirstlane(ids);
     if (cn >= nch) {
       id = -1;
@@ -239,7 +228,6 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
       bad_block = 1;
       id = -1;
     }
-    cid = id;
     const bool isv = chunk_is_v(cn);
     const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(cn, id, isv);
 #pragma unroll
@@ -259,10 +247,11 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   const int tj = r >> 2, tk = r & 3;
 
   // fold 32-token tile tc (tokens 32 tc .., staged in LDS tile `buf`) into
-  // head slot j; `wide`: the tile's V has a value beyond fp16. P^T k-slot i of
+  // head slot j; WIDE: the V tile holds bf16 (the second pass). P^T k-slot i of
   // lane (q, r) holds token 16 (i / 4) + 4 q + i % 4, the score MFMA's output
   // layout of the two halves.
-  auto consume = [&](int tc, int buf, int j, bool wide) __attribute__((always_inline)) {
+  auto consume = [&](int tc, int buf, int j, auto WIDE) __attribute__((always_inline)) {
+    constexpr bool wide = decltype(WIDE)::value;
     const uint16_t* sk = s_k[buf];
     const uint16_t* sv_ = s_v[buf];
     f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -307,7 +296,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
     // each 16-dim block's LDS reads from being issued ahead of its MFMA)
     H8 ph;
     V8 phi, plo;
-    if (kBf && wide) {
+    if constexpr (kBf && wide) {
       l[j] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -322,7 +311,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
       for (int i = 0; i < 4; ++i)
         l[j] = __builtin_amdgcn_fdot2(h2{ph[2 * i], ph[2 * i + 1]}, h2{1, 1}, l[j], false);
     }
-    if (kBf && wide) {
+    if constexpr (kBf && wide) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int o = vbase + 16 * mb;
@@ -344,61 +333,73 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
     }
   };
 
-  // the ring: chunk c + NBUF - 1 is issued just before chunk c is staged
+  // One pass over the workgroup's tiles (WIDE: V staged as bf16). The ring:
+  // chunk c + NBUF - 1 is issued just before chunk c is staged
   // (unconditionally: past the end the descriptors are empty, so an odd last
   // chunk is paired with zeros). Chunk c goes to half c % 2 of 32-token LDS
   // tile (c / 2) % 2; the barrier after a tile's second half also means every
   // wave is done with the tile before, so the other tile is free.
   const int nch2 = (nch + 1) & ~1;
-  uint4 ring[NBUF][PPT];
-  int cid[NBUF];
-  int id_even = -1;  // the block id of the last even chunk staged
-  static_for<0, NBUF - 1>([&](auto S) {
-    constexpr int s = decltype(S)::value;
-    issue(s, ring[s], idr[s], cid[s]);
-  });
-  for (int cb = 0; cb < nch2; cb += NBUF) {
-    static_for<0, NBUF>([&](auto S) {
+  auto fold_all = [&](auto WIDE) __attribute__((always_inline)) {
+    constexpr bool wide = decltype(WIDE)::value;
+    int idr[NBUF];
+    static_for<0, NBUF>([&](auto S) { idr[decltype(S)::value] = fetch_id(decltype(S)::value); });
+    uint4 ring[NBUF][PPT];
+    static_for<0, NBUF - 1>([&](auto S) {
       constexpr int s = decltype(S)::value;
-      constexpr int sn = (s + NBUF - 1) % NBUF;
-      const int c = cb + s;
-      issue(c + NBUF - 1, ring[sn], idr[sn], cid[sn]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (c < nch2) {
-        const int buf = (c >> 1) & 1, half = (c & 1) * kHalf;
-        const bool isv = chunk_is_v(c);
-#pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-          uint4 x = ring[s][k];
-          if constexpr (kBf) {
-            if (isv) {
-              bool big;
-              x = bf16x8_to_f16(x, big);
-              if (big) s_wide[buf] = c >> 1;
-            }
-          }
-          *(uint4*)((isv ? s_v[buf] : s_k[buf]) + half + plds[k]) = x;
-        }
-        if (!(c & 1)) id_even = cid[s];
-        if (c & 1) {
-          __syncthreads();
-          const bool wide = kBf && __builtin_amdgcn_readfirstlane(s_wide[buf]) == (c >> 1);
-          if (kBf && wide) {
-            // stage the tile's V again, as the bf16 values: each wave reloads
-            // the V pieces it staged (of one of the two chunks)
-            const int cv = chunk_is_v(c) ? c : c - 1;
-            const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(cv, cv == c ? cid[s] : id_even, true);
-#pragma unroll
-            for (int k = 0; k < PPT; ++k)
-              *(uint4*)(s_v[buf] + (cv & 1) * kHalf + plds[k]) = buf_load<0>(rs, poffv[k]);
-            __syncthreads();
-          }
-#pragma unroll
-          for (int j = 0; j < HPW; ++j)
-            if (hon[j]) consume(c >> 1, buf, j, wide);
-        }
-      }
+      issue(s, ring[s], idr[s]);
     });
+    for (int cb = 0; cb < nch2; cb += NBUF) {
+      static_for<0, NBUF>([&](auto S) {
+        constexpr int s = decltype(S)::value;
+        constexpr int sn = (s + NBUF - 1) % NBUF;
+        const int c = cb + s;
+        issue(c + NBUF - 1, ring[sn], idr[sn]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c < nch2) {
+          const int buf = (c >> 1) & 1, half = (c & 1) * kHalf;
+          const bool isv = chunk_is_v(c);
+#pragma unroll
+          for (int k = 0; k < PPT; ++k) {
+            uint4 x = ring[s][k];
+            if constexpr (kBf && !wide) {
+              if (isv) x = bf16x8_to_f16(x);
+            }
+            *(uint4*)((isv ? s_v[buf] : s_k[buf]) + half + plds[k]) = x;
+          }
+          if (c & 1) {
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < HPW; ++j)
+              if (hon[j]) consume(c >> 1, buf, j, WIDE);
+          }
+        }
+      });
+    }
+  };
+  fold_all(std::false_type());
+  if constexpr (kBf) {
+    // a bf16 V value beyond fp16's range (or a non-finite input) left a
+    // non-finite output: fold every tile again with V as bf16
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < HPW; ++j)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bad = bad || !__builtin_isfinite(acc[j][mb][e]);
+    if (__ballot(bad) && lane == 0) s_redo = 1;
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(s_redo)) {
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+#pragma unroll
+        for (int k = 0; k < MB; ++k) acc[j][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+      }
+      fold_all(std::true_type());
+    }
   }
 
 #pragma unroll
