@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 /* Element type of the K and V caches. q and out are always float32. */
 typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype;
@@ -314,16 +314,42 @@ int paged_attn_combine_phase(const pa_desc* desc, const int32_t* cache_seqlens, 
  *                  sequence has its rows past it unwritten and sets
  *                  PA_STATUS_BAD_SEQLEN
  *   out            float32 [total_q, H_q, d], contiguous, 16-byte aligned
+ *   workspace      NULL, or device memory of at least
+ *                  paged_attn_prefill_workspace_size(desc, max_seqlen_q) bytes
+ *                  (256-byte aligned, else PA_E_ALIGN; smaller: PA_E_WORKSPACE)
+ *                  whose leading paged_attn_prefill_workspace_zeroed_bytes()
+ *                  bytes are zero. It holds the key split's arrival counters
+ *                  and half states: when the launch's work items (8 (16-row
+ *                  tile, head) units each) leave the last round of workgroups
+ *                  on the compute units at most half full, that round's items
+ *                  run as two halves of their keys, merged by the second half
+ *                  to finish (the max-rescaling combine of page "Paged
+ *                  Attention Kernel Architecture for BI-V100", section 2).
+ *                  Every call leaves the counters zero. NULL (or a size of 0)
+ *                  runs every item whole.
+ *   workspace_bytes  its size
  *   status         as for the decode (PA_STATUS_BAD_BLOCK, PA_STATUS_BAD_SEQLEN)
  *
- * One pass, no workspace; asynchronous on `stream`, no allocation (graph-
- * capturable). Returns PA_OK or a PA_E_* code (nothing launched then).
+ * One launch; asynchronous on `stream`, no allocation (graph-capturable).
+ * Calls that share a workspace must be ordered on one stream. Returns PA_OK or
+ * a PA_E_* code (nothing launched then).
  */
 int paged_attn_prefill(const pa_desc* desc, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* block_table,
                        const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
                        int32_t max_seqlen_q, int32_t causal, float scale, void* out,
-                       int32_t* status, void* stream);
+                       void* workspace, size_t workspace_bytes, int32_t* status, void* stream);
+
+/* Bytes of workspace paged_attn_prefill uses for the key split with this
+ * descriptor and max_seqlen_q on the current device (the split depends on its
+ * compute-unit count); 0 when no work item is split, for a descriptor the
+ * prefill refuses and for max_seqlen_q <= 0. */
+size_t paged_attn_prefill_workspace_size(const pa_desc* desc, int32_t max_seqlen_q);
+
+/* Leading bytes of that workspace (the arrival counters) that must be zero
+ * when a call starts; every call leaves them zero, so zero them once after
+ * allocating the workspace or after using it for anything else. */
+size_t paged_attn_prefill_workspace_zeroed_bytes(const pa_desc* desc, int32_t max_seqlen_q);
 
 /* Bytes of workspace paged_attn_decode needs for this descriptor on the
  * current device. Grid and VALU kernels: the partial (max, sum, output) of

@@ -14,7 +14,7 @@ from ._lib import (  # noqa: F401
     PA_STATIC_SCRATCH_BYTES, PA_STATUS_BAD_SEQLEN, PATH_NAME,
     PaDesc, PagedAttnError, check_inputs, decode_append_raw, decode_raw, decode_static_raw,
     load_library, make_desc,
-    partition_size, prefill_raw,
+    partition_size, prefill_raw, prefill_workspace_size, prefill_workspace_zeroed_bytes,
     resolved_path, strerror, validate, workspace_size,
 )
 
@@ -140,6 +140,35 @@ def workspace_for(desc: PaDesc, device, stream=None):
     return ws
 
 
+_pf_ws_cache: dict = {}
+
+
+def prefill_workspace_for(desc: PaDesc, max_seqlen_q: int, device, stream=None):
+    """A cached device workspace for paged_attn_prefill's key split (None when
+    the launch splits nothing), for calls enqueued on ``stream``.
+
+    One workspace per (device, stream), allocated zeroed: its leading arrival
+    counters must be zero when a call starts, and every call leaves them zero.
+    A workspace that a later call outgrows is replaced but never freed (a HIP
+    graph captured with it keeps its address)."""
+    import torch
+
+    n = prefill_workspace_size(desc, max_seqlen_q)
+    if n == 0:
+        return None
+    if stream is None:
+        stream = torch.cuda.current_stream(device).cuda_stream
+    key = (str(device), int(stream))
+    ws = _pf_ws_cache.get(key)
+    if ws is None or ws.numel() < n:
+        if ws is not None:
+            _ws_retired.append(ws)
+        with _on_stream(torch, stream, device):
+            ws = torch.zeros(n, dtype=torch.uint8, device=device)
+        _pf_ws_cache[key] = ws
+    return ws
+
+
 def paged_attn_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, out=None, *,
                       layout="HND", partition_size=0, path="auto", workspace=None, status=None,
                       stream=None, phase="both", kv_shared=False):
@@ -252,7 +281,8 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cac
 
 
 def paged_attn_prefill(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, scale, out=None,
-                       *, max_seqlen_q=None, causal=True, layout="HND", status=None, stream=None):
+                       *, max_seqlen_q=None, causal=True, layout="HND", status=None, stream=None,
+                       split=True):
     """Paged varlen prefill; returns ``out`` ([total_q, H_q, d], q's dtype).
 
     Sequence b owns query rows ``cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1`` of the
@@ -262,7 +292,9 @@ def paged_attn_prefill(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k
     ``[0, L - q_len + i]`` (zeros when none), else all L. ``max_seqlen_q`` must
     bound every q_len; when None it is read from ``cu_seqlens_q`` (a device
     synchronisation, so pass it for graph capture). K/V must be float16 or
-    bfloat16.
+    bfloat16. ``split``: give the launch its key-split workspace (cached per
+    device and stream, see prefill_workspace_for); False runs every work item
+    whole.
     """
     import torch
 
@@ -292,9 +324,11 @@ def paged_attn_prefill(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
+    ws = prefill_workspace_for(desc, int(max_seqlen_q), q.device, int(stream)) if split else None
     rc = prefill_raw(desc, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                      block_table.data_ptr(), cu_seqlens_q.data_ptr(), seqlens_k.data_ptr(),
                      int(max_seqlen_q), bool(causal), float(scale), out.data_ptr(),
+                     ws.data_ptr() if ws is not None else 0, ws.numel() if ws is not None else 0,
                      status.data_ptr() if status is not None else 0, int(stream))
     if rc != 0:
         raise PagedAttnError(rc, "paged_attn_prefill: ")

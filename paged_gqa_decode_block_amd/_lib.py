@@ -33,7 +33,8 @@ PA_STATUS_BAD_SEQLEN = 2
 EXPORTED = (
     "paged_attn_decode", "paged_attn_decode_static", "paged_attn_decode_append",
     "paged_attn_partition_phase",
-    "paged_attn_combine_phase", "paged_attn_prefill",
+    "paged_attn_combine_phase", "paged_attn_prefill", "paged_attn_prefill_workspace_size",
+    "paged_attn_prefill_workspace_zeroed_bytes",
     "paged_attn_workspace_size", "paged_attn_validate", "paged_attn_partition_size", "paged_attn_resolved_path", "paged_attn_check_inputs",
     "paged_attn_strerror", "paged_attn_abi_version",
     # include/paged_block_manager.h
@@ -102,8 +103,12 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_combine_phase.argtypes = [dp, vp, vp, vp, sz, vp]
     lib.paged_attn_combine_phase.restype = i32
     lib.paged_attn_prefill.argtypes = [dp, vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp, vp,
-                                       vp]
+                                       sz, vp, vp]
     lib.paged_attn_prefill.restype = i32
+    lib.paged_attn_prefill_workspace_size.argtypes = [dp, i32]
+    lib.paged_attn_prefill_workspace_size.restype = sz
+    lib.paged_attn_prefill_workspace_zeroed_bytes.argtypes = [dp, i32]
+    lib.paged_attn_prefill_workspace_zeroed_bytes.restype = sz
     lib.paged_attn_workspace_size.argtypes = [dp]
     lib.paged_attn_workspace_size.restype = sz
     lib.paged_attn_validate.argtypes = [dp]
@@ -168,6 +173,18 @@ def workspace_size(desc: PaDesc) -> int:
     return int(load_library().paged_attn_workspace_size(ctypes.byref(desc)))
 
 
+def prefill_workspace_size(desc: PaDesc, max_seqlen_q: int) -> int:
+    """Bytes of the prefill's key-split workspace (0: no work item is split)."""
+    return int(load_library().paged_attn_prefill_workspace_size(ctypes.byref(desc),
+                                                                int(max_seqlen_q)))
+
+
+def prefill_workspace_zeroed_bytes(desc: PaDesc, max_seqlen_q: int) -> int:
+    """Leading bytes of that workspace (arrival counters) that must be zero."""
+    return int(load_library().paged_attn_prefill_workspace_zeroed_bytes(ctypes.byref(desc),
+                                                                        int(max_seqlen_q)))
+
+
 def decode_append_raw(desc: PaDesc, q_ptr: int, knew_ptr: int, vnew_ptr: int, k_ptr: int, v_ptr: int,
                       table_ptr: int, seqlens_ptr: int, scale: float, out_ptr: int, ws_ptr: int,
                       ws_bytes: int, status_ptr: int, stream: int) -> int:
@@ -196,12 +213,13 @@ def check_inputs(desc: PaDesc, block_table_host, seqlens_host) -> int:
 
 def prefill_raw(desc: PaDesc, q_ptr: int, k_ptr: int, v_ptr: int, table_ptr: int, cu_q_ptr: int,
                 seqlens_k_ptr: int, max_seqlen_q: int, causal: bool, scale: float, out_ptr: int,
-                status_ptr: int, stream: int) -> int:
+                ws_ptr: int, ws_bytes: int, status_ptr: int, stream: int) -> int:
     """Direct call of paged_attn_prefill with integer device addresses."""
     return int(load_library().paged_attn_prefill(
         ctypes.byref(desc), q_ptr or None, k_ptr or None, v_ptr or None, table_ptr or None,
         cu_q_ptr or None, seqlens_k_ptr or None, int(max_seqlen_q), int(bool(causal)),
-        ctypes.c_float(scale), out_ptr or None, status_ptr or None, stream or None))
+        ctypes.c_float(scale), out_ptr or None, ws_ptr or None, int(ws_bytes), status_ptr or None,
+        stream or None))
 
 
 def decode_static_raw(desc: PaDesc, q_ptr: int, k_ptr: int, v_ptr: int, table_ptr: int,

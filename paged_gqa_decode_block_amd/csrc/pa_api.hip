@@ -324,6 +324,35 @@ size_t paged_attn_workspace_size(const pa_desc* desc) {
   return off[kWsParts];
 }
 
+namespace {
+// the prefill launch's parameters that size its workspace
+pa::Params prefill_shape(const pa_desc* desc) {
+  pa::Params p{};
+  p.B = desc->batch;
+  p.Hq = desc->num_q_heads;
+  p.Hkv = desc->num_kv_heads;
+  p.G = desc->num_q_heads / desc->num_kv_heads;
+  p.D = desc->head_dim;
+  p.qo_bf16 = (desc->flags & PA_FLAG_QO_BF16) ? 1 : 0;
+  p.cus = cu_count();
+  return p;
+}
+bool prefill_kv_ok(const pa_desc* desc) {
+  return desc->kv_dtype != PA_DTYPE_F32 && !(desc->flags & PA_FLAG_KV_XPACKED) &&
+         desc->block_size >= 16;
+}
+}  // namespace
+
+size_t paged_attn_prefill_workspace_size(const pa_desc* desc, int32_t max_seqlen_q) {
+  if (validate(desc) != PA_OK || !prefill_kv_ok(desc) || max_seqlen_q <= 0) return 0;
+  return pa::prefill_workspace_bytes(prefill_shape(desc), max_seqlen_q);
+}
+
+size_t paged_attn_prefill_workspace_zeroed_bytes(const pa_desc* desc, int32_t max_seqlen_q) {
+  if (validate(desc) != PA_OK || !prefill_kv_ok(desc) || max_seqlen_q <= 0) return 0;
+  return pa::prefill_workspace_zeroed_bytes(prefill_shape(desc), max_seqlen_q);
+}
+
 int paged_attn_check_inputs(const pa_desc* desc, const int32_t* table, const int32_t* seqlens) {
   const int rc = validate(desc);
   if (rc != PA_OK) return rc;
@@ -583,7 +612,8 @@ int paged_attn_partition_phase(const pa_desc* desc, const void* q, const void* k
 int paged_attn_prefill(const pa_desc* desc, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_table, const int32_t* cu_seqlens_q,
                        const int32_t* seqlens_k, int32_t max_seqlen_q, int32_t causal, float scale,
-                       void* out, int32_t* status, void* stream) {
+                       void* out, void* workspace, size_t workspace_bytes, int32_t* status,
+                       void* stream) {
   pa::Params p;
   const int rc = prepare(desc, q, k_cache, v_cache, block_table, seqlens_k, scale, out, nullptr, 0,
                          status, true, p, false);
@@ -592,8 +622,12 @@ int paged_attn_prefill(const pa_desc* desc, const void* q, const void* k_cache, 
   if (desc->kv_dtype == PA_DTYPE_F32 || (desc->flags & PA_FLAG_KV_XPACKED)) return PA_E_PATH;
   if (desc->block_size < 16 || max_seqlen_q < 0) return PA_E_SHAPE;
   if (max_seqlen_q == 0) return PA_OK;
+  // the key split needs its workspace; without one every work item runs whole
+  const size_t need = pa::prefill_workspace_bytes(p, max_seqlen_q);
+  if (workspace && need > workspace_bytes) return PA_E_WORKSPACE;
+  if (workspace && ((uintptr_t)workspace & 255)) return PA_E_ALIGN;
   return pa::launch_prefill(p, desc->kv_dtype, cu_seqlens_q, max_seqlen_q, causal != 0,
-                            (hipStream_t)stream) == hipSuccess
+                            need > 0 ? workspace : nullptr, (hipStream_t)stream) == hipSuccess
              ? PA_OK
              : PA_E_LAUNCH;
 }

@@ -48,6 +48,16 @@
 // column, so each row ends at its own causal bound. No partial state leaves
 // the workgroup: each unit is normalised and written at the end.
 //
+// Key split. When the work items (eight units each) would fill the compute
+// units one and a half times or less on a round (the last round at most half
+// full), the items of that last round are split in two halves of their key
+// tiles, so the GPU runs the whole items and then the halves instead of a
+// second full round. Both halves store their state (max, sum and unnormalised
+// output per unit, as the folds left them) in the workspace and count in on
+// the item's arrival counter; the second to arrive merges the two states with
+// the max-rescaling combine (page "Paged Attention Kernel Architecture for
+// BI-V100", section 2), resets the counter and writes the output.
+//
 // Requires 16-bit K/V and block_size >= 16.
 #include "pa_mfma_util.h"
 
@@ -56,6 +66,12 @@ namespace {
 
 constexpr int kHeadsPerGroup = 8;  // (tile, head) units per workgroup: 8 / NW per wave
 constexpr int kXcds = 8;            // gfx950 (MI350 series): eight XCDs, each with its own L2
+
+// Device-scope cache bits (SC1 set, SC0 clear on gfx950) of the key split's
+// state traffic: a store completes only at the device-coherent level, a load
+// is served from there (not from a line another XCD's write left stale in this
+// XCD's L2).
+constexpr int kScDevice = 16;
 
 // Eight bf16 values (16 bytes) as fp16, exact where fp16 has the value (below
 // 2^-14 it keeps fp16's subnormal grid; from 2^16 on, infinite).
@@ -76,10 +92,15 @@ __device__ __forceinline__ uint4 bf16x8_to_f16(uint4 w) {
 // NW waves per workgroup (4: two heads per wave; 8: one head per wave, half
 // the registers, so that d = 256 runs two waves per SIMD), NBUF ring slots,
 // OCC waves per SIMD.
+//
+// Work items per XCD: the first nwhole whole, the next nsplit split in two
+// halves (all first halves dispatched, then all second halves); ws_cnt
+// [kXcds * nsplit] arrival counters, ws_st the halves' states.
 template <typename T, int D, int NW, int NBUF, int OCC, int QO>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, int hh,
-               int ntiles, int per) {
+               int ntiles, int per, int nwhole, int nsplit, int32_t* __restrict__ ws_cnt,
+               float* __restrict__ ws_st) {
   typedef Mx<T> M;
   typedef typename M::v8 V8;
   typedef Mx<_Float16> H;
@@ -103,6 +124,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kTile];
   __shared__ int s_redo;
+  __shared__ int s_arrived;  // the key split: halves of the item before this one
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // w: the wave's
@@ -114,8 +136,16 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   // The per work items of one (sequence, KV head) read the same K and V: they
   // all go to one XCD (workgroup i runs on XCD i mod kXcds), whose L2 then
   // serves the repeated reads. XCD x takes the pairs x, x + kXcds, ...
+  // The XCD's work item i (pair i / per of its list, item i % per of the
+  // pair), whole, or half sp of its key tiles.
   const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
-  const int pair = xcd + kXcds * (slot / per), item = slot % per;
+  int wi = slot, sp = -1;
+  if (slot >= nwhole) {
+    const int h = slot - nwhole;
+    wi = nwhole + h % nsplit;
+    sp = h / nsplit;
+  }
+  const int pair = xcd + kXcds * (wi / per), item = wi % per;
   if (pair >= p.B * p.Hkv) return;  // padding of the last round
   const int b = pair / p.Hkv, hk = pair % p.Hkv;
   const int g0 = (item % nhg) * hh;
@@ -131,7 +161,16 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   const int L = clamped_len(p, b, first);
   const int plast = min(pw0 + 16 * tpw - 1, ql - 1);
   const int kend = causal ? min(L, max(0, L - ql + plast + 1)) : L;  // the last tile's
-  const int nch = (kend + 15) >> 4;
+  // chunks [c0, nch) of the key tiles: all of them, or the first half of the
+  // tiles (rounded up) or the rest
+  int c0 = 0, nch = (kend + 15) >> 4;
+  if (sp >= 0) {
+    const int th = (((nch + 1) >> 1) + 1) >> 1;
+    if (sp == 0)
+      nch = min(nch, 2 * th);
+    else
+      c0 = 2 * th;
+  }
 
   // slot j of this wave: unit u = w + NW j, tile u / hh, head u % hh. Column r
   // is query position p0s + r of the sequence; its keys are [0, kend_r).
@@ -333,7 +372,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
     }
   };
 
-  // One pass over the workgroup's tiles (WIDE: V staged as bf16). The ring:
+  // One pass over the workgroup's tiles [c0, nch) (WIDE: V staged as bf16). The ring:
   // chunk c + NBUF - 1 is issued just before chunk c is staged
   // (unconditionally: past the end the descriptors are empty, so an odd last
   // chunk is paired with zeros). Chunk c goes to half c % 2 of 32-token LDS
@@ -343,13 +382,13 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   auto fold_all = [&](auto WIDE) __attribute__((always_inline)) {
     constexpr bool wide = decltype(WIDE)::value;
     int idr[NBUF];
-    static_for<0, NBUF>([&](auto S) { idr[decltype(S)::value] = fetch_id(decltype(S)::value); });
+    static_for<0, NBUF>([&](auto S) { idr[decltype(S)::value] = fetch_id(c0 + decltype(S)::value); });
     uint4 ring[NBUF][PPT];
     static_for<0, NBUF - 1>([&](auto S) {
       constexpr int s = decltype(S)::value;
-      issue(s, ring[s], idr[s]);
+      issue(c0 + s, ring[s], idr[s]);
     });
-    for (int cb = 0; cb < nch2; cb += NBUF) {
+    for (int cb = c0; cb < nch2; cb += NBUF) {
       static_for<0, NBUF>([&](auto S) {
         constexpr int s = decltype(S)::value;
         constexpr int sn = (s + NBUF - 1) % NBUF;
@@ -402,6 +441,68 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
     }
   }
 
+  if (sp >= 0) {
+    // Key split: store this half's state per unit u = w + NW j (output
+    // fragments in lane order, then m and l per lane), count in, and let the
+    // second half to arrive merge the first's state into its own.
+    constexpr int US = MB * 256 + 128;  // floats per unit and half
+    const int64_t si = (int64_t)xcd * nsplit + (wi - nwhole);
+    const __amdgpu_buffer_rsrc_t rst_ = uniform_rsrc((const char*)(ws_st + si * (2 * 8 * US)),
+                                                     2 * 8 * US * 4);
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const int o = (sp * 8 + w + NW * j) * US;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[j][mb]), rst_,
+                                               (o + (mb * 64 + lane) * 4) * 4, 0, kScDevice);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m[j]), rst_,
+                                            (o + MB * 256 + lane) * 4, 0, kScDevice);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l[j]), rst_,
+                                            (o + MB * 256 + 64 + lane) * 4, 0, kScDevice);
+    }
+    // Ordering: the stores are device scope, so they complete at the
+    // device-coherent level; every wave waits for its own (the signal fences
+    // keep the compiler from moving memory operations across the wait) before
+    // the barrier, and only then does one thread count the workgroup in with an
+    // agent-scope atomic. The two increments of a counter are ordered at its
+    // point of coherence, so the half that reads 1 counts in after the other
+    // half's states were complete; its loads below depend on that value and
+    // are device scope as well.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (tid == 0)
+      s_arrived = __hip_atomic_fetch_add(ws_cnt + si, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(s_arrived) == 0) return;  // the other half merges
+    // second to arrive: reset the counter for the next call (the kernel
+    // boundary orders this store before any later launch)
+    if (tid == 0) __hip_atomic_store(ws_cnt + si, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const int o = ((1 - sp) * 8 + w + NW * j) * US;
+      const float mo = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rst_, (o + MB * 256 + lane) * 4, 0, kScDevice));
+      const float lo = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rst_, (o + MB * 256 + 64 + lane) * 4, 0, kScDevice));
+      const float M = fmaxf(m[j], mo);
+      const float mu = M == -INFINITY ? 0.f : M;
+      const float w0 = exp2_fast(m[j] - mu), w1 = exp2_fast(mo - mu);
+      l[j] = w0 * l[j] + w1 * lo;
+      m[j] = M;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const f32x4 ao = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rst_, (o + (mb * 64 + lane) * 4) * 4, 0,
+                                                         kScDevice));
+        acc[j][mb] = w0 * acc[j][mb] + w1 * ao;
+      }
+    }
+  }
+
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const float lt = quad_sum(l[j]);
@@ -426,43 +527,89 @@ constexpr int kPrefillCfg[2][3][3] = {{{4, 6, 2}, {8, 2, 4}, {8, 4, 2}},
                                       {{4, 6, 2}, {8, 4, 4}, {8, 4, 2}}};
 constexpr int pdim(int D) { return D == 64 ? 0 : D == 128 ? 1 : 2; }
 
-template <typename T, int D, int QO>
-hipError_t launch_p(const Params& p, const int32_t* cu_q, int max_q, int causal, hipStream_t s) {
-  constexpr int NW = kPrefillCfg[QO][pdim(D)][0], NB_ = kPrefillCfg[QO][pdim(D)][1],
-                OCC = kPrefillCfg[QO][pdim(D)][2];
+// The launch's shape: heads per workgroup, work items per (sequence, KV head)
+// and per XCD, and how many of each XCD's items are whole and split.
+struct Plan {
+  int hh = 8, nhg = 1, ntiles = 0, per = 0;
+  int64_t items = 0;  // per XCD (the last round of pairs padded)
+  int64_t nwhole = 0, nsplit = 0;
+  int D = 0;
+};
+
+Plan plan(const Params& p, int max_q) {
+  Plan pl;
+  const int qo = p.qo_bf16 ? 1 : 0, di = pdim(p.D);
+  const int NW = kPrefillCfg[qo][di][0], OCC = kPrefillCfg[qo][di][2];
+  pl.D = p.D;
   // heads per workgroup: 8 when they divide G; else the largest power of two
   // dividing G, with 8 / hh tiles per workgroup so that no unit is idle, if
   // there are that many tiles (else 8, the last group partly empty)
-  const int ntiles = (max_q + 15) / 16;
-  int hh = kHeadsPerGroup;
+  pl.ntiles = (max_q + 15) / 16;
+  pl.hh = kHeadsPerGroup;
   if (p.G % kHeadsPerGroup) {
     int h2 = 1;
     while (2 * h2 < kHeadsPerGroup && p.G % (2 * h2) == 0) h2 *= 2;
-    if (ntiles >= kHeadsPerGroup / h2) hh = h2;
+    if (pl.ntiles >= kHeadsPerGroup / h2) pl.hh = h2;
   }
-  const int tpw = kHeadsPerGroup / hh;
-  const int nhg = (p.G + hh - 1) / hh;
+  const int tpw = kHeadsPerGroup / pl.hh;
+  pl.nhg = (p.G + pl.hh - 1) / pl.hh;
   // per (sequence, KV head): tile groups x head groups; pairs spread over the
   // XCDs, the last round padded with empty workgroups
-  const int64_t per = (int64_t)((ntiles + tpw - 1) / tpw) * nhg;
+  pl.per = (pl.ntiles + tpw - 1) / tpw * pl.nhg;
   const int64_t rounds = ((int64_t)p.B * p.Hkv + kXcds - 1) / kXcds;
-  const int64_t blocks = kXcds * rounds * per;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  pl.items = rounds * pl.per;
+  pl.nwhole = pl.items;
+  // the key split: an XCD holds C workgroups at once; when its items leave a
+  // last round at most half full, that round's items run as two halves each
+  const int64_t C = (int64_t)(p.cus / kXcds) * (4 * OCC / NW);
+  if (C > 0) {
+    const int64_t k = pl.items / C, rem = pl.items - k * C;
+    if (k >= 1 && rem > 0 && 2 * rem <= C) {
+      pl.nwhole = k * C;
+      pl.nsplit = rem;
+    }
+  }
+  return pl;
+}
+
+// floats of one split item's two halves' states: 8 units x (D / 16 output
+// fragments of 64 lanes x 4, then m and l of 64 lanes)
+int64_t split_item_floats(int D) { return 2 * 8 * ((int64_t)(D / 16) * 256 + 128); }
+size_t split_cnt_bytes(const Plan& pl) {
+  return ((size_t)kXcds * pl.nsplit * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
+template <typename T, int D, int QO>
+hipError_t launch_p(const Params& p, const int32_t* cu_q, int max_q, int causal, void* ws,
+                    hipStream_t s) {
+  constexpr int NW = kPrefillCfg[QO][pdim(D)][0], NB_ = kPrefillCfg[QO][pdim(D)][1],
+                OCC = kPrefillCfg[QO][pdim(D)][2];
+  Plan pl = plan(p, max_q);
+  if (!ws) {
+    pl.nwhole = pl.items;
+    pl.nsplit = 0;
+  }
+  const int64_t blocks = kXcds * (pl.nwhole + 2 * pl.nsplit);
+  if (blocks > 0x7fffffff || pl.items > 0x3fffffff) return hipErrorInvalidConfiguration;
+  int32_t* cnt = pl.nsplit > 0 ? (int32_t*)ws : nullptr;
+  float* st = pl.nsplit > 0 ? (float*)((char*)ws + split_cnt_bytes(pl)) : nullptr;
   hipLaunchKernelGGL((prefill_kernel<T, D, NW, NB_, OCC, QO>), dim3((unsigned)blocks),
-                     dim3(64 * NW), 0, s, p, cu_q, causal, nhg, hh, ntiles, (int)per);
+                     dim3(64 * NW), 0, s, p, cu_q, causal, pl.nhg, pl.hh, pl.ntiles, pl.per,
+                     (int)pl.nwhole, (int)pl.nsplit, cnt, st);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_pd(const Params& p, const int32_t* cu_q, int max_q, int causal, hipStream_t s) {
+hipError_t launch_pd(const Params& p, const int32_t* cu_q, int max_q, int causal, void* ws,
+                     hipStream_t s) {
   const bool bf = p.qo_bf16 != 0;
   switch (p.D) {
-    case 64: return bf ? launch_p<T, 64, 1>(p, cu_q, max_q, causal, s)
-                       : launch_p<T, 64, 0>(p, cu_q, max_q, causal, s);
-    case 128: return bf ? launch_p<T, 128, 1>(p, cu_q, max_q, causal, s)
-                        : launch_p<T, 128, 0>(p, cu_q, max_q, causal, s);
-    case 256: return bf ? launch_p<T, 256, 1>(p, cu_q, max_q, causal, s)
-                        : launch_p<T, 256, 0>(p, cu_q, max_q, causal, s);
+    case 64: return bf ? launch_p<T, 64, 1>(p, cu_q, max_q, causal, ws, s)
+                       : launch_p<T, 64, 0>(p, cu_q, max_q, causal, ws, s);
+    case 128: return bf ? launch_p<T, 128, 1>(p, cu_q, max_q, causal, ws, s)
+                        : launch_p<T, 128, 0>(p, cu_q, max_q, causal, ws, s);
+    case 256: return bf ? launch_p<T, 256, 1>(p, cu_q, max_q, causal, ws, s)
+                        : launch_p<T, 256, 0>(p, cu_q, max_q, causal, ws, s);
   }
   return hipErrorInvalidValue;
 }
@@ -470,11 +617,23 @@ hipError_t launch_pd(const Params& p, const int32_t* cu_q, int max_q, int causal
 }  // namespace
 
 hipError_t launch_prefill(const Params& p, int dtype, const int32_t* cu_q, int max_q, int causal,
-                          hipStream_t s) {
+                          void* ws, hipStream_t s) {
   if (max_q <= 0 || p.B <= 0) return hipSuccess;
-  if (dtype == 1) return launch_pd<_Float16>(p, cu_q, max_q, causal, s);
-  if (dtype == 2) return launch_pd<__bf16>(p, cu_q, max_q, causal, s);
+  if (dtype == 1) return launch_pd<_Float16>(p, cu_q, max_q, causal, ws, s);
+  if (dtype == 2) return launch_pd<__bf16>(p, cu_q, max_q, causal, ws, s);
   return hipErrorInvalidValue;
+}
+
+size_t prefill_workspace_bytes(const Params& p, int max_q) {
+  if (max_q <= 0 || p.B <= 0 || (p.D != 64 && p.D != 128 && p.D != 256)) return 0;
+  const Plan pl = plan(p, max_q);
+  if (pl.nsplit == 0) return 0;
+  return split_cnt_bytes(pl) + (size_t)kXcds * pl.nsplit * split_item_floats(p.D) * sizeof(float);
+}
+
+size_t prefill_workspace_zeroed_bytes(const Params& p, int max_q) {
+  if (prefill_workspace_bytes(p, max_q) == 0) return 0;
+  return (size_t)kXcds * plan(p, max_q).nsplit * sizeof(int32_t);
 }
 
 }  // namespace pa

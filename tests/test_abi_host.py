@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), f"{name} not exported"
-    assert lib.paged_attn_abi_version() == 4
+    assert lib.paged_attn_abi_version() == 5
 
 
 def test_descriptor_layout_matches_c(tmp_path):
@@ -308,7 +308,7 @@ def test_prefill_argument_errors():
     good = 1 << 20
     args = dict(q_ptr=good, k_ptr=good, v_ptr=good, table_ptr=good, cu_q_ptr=good,
                 seqlens_k_ptr=good, max_seqlen_q=16, causal=True, scale=1.0, out_ptr=good,
-                status_ptr=0, stream=0)
+                ws_ptr=0, ws_bytes=0, status_ptr=0, stream=0)
     assert pa.prefill_raw(_desc(head_dim=100), **args) == -3              # bad descriptor
     assert pa.prefill_raw(d, **{**args, "cu_q_ptr": 0}) == -1            # no cu_seqlens_q
     assert pa.prefill_raw(d, **{**args, "seqlens_k_ptr": 0}) == -1       # no key lengths
@@ -321,6 +321,52 @@ def test_prefill_argument_errors():
     assert pa.prefill_raw(_desc(batch=0), **{**args, "cu_q_ptr": 0}) == 0  # no sequences
     # no workspace is involved, whatever the decode would need
     assert pa.workspace_size(d) > 0
+    assert pa.prefill_workspace_size(d, 16) == 0
+    # a launch that splits keys: a workspace smaller than its size, or not
+    # 256-byte aligned, is refused
+    p1 = _desc(batch=4, num_q_heads=24, num_kv_heads=4, head_dim=256, max_blocks_per_seq=512,
+               num_blocks=2048, k_strides=(4 * 16 * 256, 16 * 256, 256))
+    n = pa.prefill_workspace_size(p1, 512)
+    assert n > 0
+    a1 = {**args, "max_seqlen_q": 512}
+    assert pa.prefill_raw(p1, **{**a1, "ws_ptr": good, "ws_bytes": n - 1}) == -9
+    assert pa.prefill_raw(p1, **{**a1, "ws_ptr": good + 16, "ws_bytes": n}) == -7
+
+
+def test_prefill_key_split_workspace():
+    """The key split's plan, for 256 compute units (the host's count when no GPU
+    is visible) and 8 XCDs. Work items per XCD: the (sequence, KV head) pairs
+    dealt round robin (ceil(B Hkv / 8) rounds of pairs) times the items per pair
+    (16-row tile groups x head groups); the workgroups an XCD holds at once: 32
+    compute units x (1 at d = 256, 2 at d = 128). A last round at most half full
+    is split: counters (8 x split items int32, 256-byte aligned) then two
+    halves' states (8 units x (d/16 x 256 + 128) floats) per split item."""
+    def desc(B, Hq, Hkv, D, bf=True):
+        return _desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, max_blocks_per_seq=512,
+                     num_blocks=2048, k_strides=(Hkv * 16 * D, 16 * D, D), qo_bf16=bf)
+    def want(nsplit, D):
+        cnt = (8 * nsplit * 4 + 255) // 256 * 256
+        return cnt + 8 * nsplit * 2 * 8 * ((D // 16) * 256 + 128) * 4, 8 * nsplit * 4
+    # d = 256, G = 6 (two heads x four tiles per workgroup): 512 rows -> 24 items
+    # per pair; 16 pairs -> 2 rounds of pairs -> 48 items per XCD = 32 + 16:
+    # the 16 are split (fp32 and bf16 q/out alike)
+    for bf in (True, False):
+        d = desc(4, 24, 4, 256, bf)
+        assert (pa.prefill_workspace_size(d, 512), pa.prefill_workspace_zeroed_bytes(d, 512)) == want(16, 256)
+    # 256 rows -> 12 items per pair, 8 pairs -> 12 items per XCD: fewer than 32
+    assert pa.prefill_workspace_size(desc(2, 24, 4, 256), 256) == 0
+    # 24 pairs -> 72 items per XCD = 2 x 32 + 8: the 8 are split; 32 pairs ->
+    # 96 = 3 x 32: none
+    assert pa.prefill_workspace_size(desc(6, 24, 4, 256), 512) == want(8, 256)[0]
+    assert pa.prefill_workspace_size(desc(8, 24, 4, 256), 512) == 0
+    # d = 128, G = 8 (eight heads x one tile): 256 rows -> 16 items per pair;
+    # 128 pairs -> 256 items per XCD = 4 x 64: none; 40 pairs -> 80 = 64 + 16:
+    # the 16 are split
+    assert pa.prefill_workspace_size(desc(16, 64, 8, 128), 256) == 0
+    assert pa.prefill_workspace_size(desc(5, 64, 8, 128), 256) == want(16, 128)[0]
+    # refused descriptors and no rows: 0
+    assert pa.prefill_workspace_size(desc(4, 24, 4, 256), 0) == 0
+    assert pa.prefill_workspace_size(_desc(kv_dtype="f32", k_strides=(4096, 2048, 128)), 512) == 0
 
 
 def test_decode_static_refuses_before_device_work():

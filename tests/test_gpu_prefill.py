@@ -3,7 +3,8 @@ fp64 oracle, element by element: head sizes 64/128/256, fp16 and bf16 K/V,
 HND and NHD pools, causal and full attention, sequences whose query count is
 below, equal to and above their key count, empty sequences and rows with no
 key to attend (zeros), several 16-row tiles with a ragged last one, bf16 q and
-out, and the status report for a max_seqlen_q below a sequence's row count."""
+out, the status report for a max_seqlen_q below a sequence's row count, and
+the key split of a last round of work items (halves merged in the kernel)."""
 from __future__ import annotations
 
 import numpy as np
@@ -48,7 +49,7 @@ def _oracle(case, cu, q, causal):
                                 block_size=case.bs, num_kv_heads=case.Hkv, layout=case.layout)
 
 
-def _gpu(torch, case, cu, q, causal, *, max_q=None, status=None, bf16=False):
+def _gpu(torch, case, cu, q, causal, *, max_q=None, status=None, bf16=False, split=True):
     qd = torch.from_numpy(q).to("cuda")
     if bf16:
         qd = qd.to(torch.bfloat16)
@@ -56,7 +57,8 @@ def _gpu(torch, case, cu, q, causal, *, max_q=None, status=None, bf16=False):
                                 torch.from_numpy(case.block_table).to("cuda"),
                                 torch.from_numpy(cu).to("cuda"),
                                 torch.from_numpy(case.seqlens).to("cuda"), case.scale,
-                                max_seqlen_q=max_q, causal=causal, layout=case.layout, status=status)
+                                max_seqlen_q=max_q, causal=causal, layout=case.layout, status=status,
+                                split=split)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
 
@@ -233,3 +235,84 @@ def test_prefill_workloads_whole_output(torch_cuda, k):
     err = float(np.abs(got - want).max())
     print(f"prefill workload {k}: max-abs error {err:.3e} over {got.size} values")
     assert err <= 3e-3
+
+
+def _split_case(rng):
+    """24 sequences at d = 256, G = 6, 64 query rows at most: 96 (sequence, KV
+    head) pairs of 3 work items each, 36 per XCD against the 32 workgroups an
+    XCD holds at once, so the last 4 items of every XCD (sequences 20-23) run
+    as two halves of their keys. Sequence 20 (20 keys) and 22 (33 keys) leave
+    the second half of their items without a key tile; 21 has 400 keys."""
+    klens = rng.integers(64, 400, size=24).astype(np.int32)
+    klens[20:] = [20, 400, 33, 64]
+    qlens = np.minimum(klens, 64)
+    return _make(rng, Hq=24, Hkv=4, D=256, bs=16, kv_dtype="bf16", klens=klens, qlens=qlens)
+
+
+def _counters_zero(torch, case, q, max_q):
+    """The cached key-split workspace's arrival counters are zero again."""
+    desc = pa.desc_for(torch.empty(1, case.Hq, case.D, device="cuda"), _pool(torch, case, case.k_store),
+                       _pool(torch, case, case.v_store),
+                       torch.from_numpy(case.block_table).to("cuda"), layout=case.layout)
+    desc.batch = case.B
+    zb = pa.prefill_workspace_zeroed_bytes(desc, max_q)
+    ws = pa.prefill_workspace_for(desc, max_q, torch.device("cuda"))
+    torch.cuda.synchronize()
+    return zb > 0 and ws is not None and int(ws[:zb].count_nonzero().item()) == 0
+
+
+@pytest.mark.parametrize("bf16_q", [False, True], ids=["q32", "q16"])
+def test_prefill_key_split(torch_cuda, bf16_q):
+    """Split work items against the oracle, element by element, twice in a row
+    (the arrival counters are left zero for the next call), and against the
+    same launch with every item whole (no workspace)."""
+    from paged_gqa_decode_block_amd import workload as W
+
+    torch = torch_cuda
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the split plan of this batch assumes 256 compute units")
+    rng = np.random.default_rng(1330 + bf16_q)
+    case, cu, q = _split_case(rng)
+    if bf16_q:
+        q = W.from_storage(W.to_storage(q, "bf16"), "bf16").astype(np.float32)
+    want = _oracle(case, cu, q, True)
+    tol = 3e-3 + (np.abs(want) * 2.0 ** -8 if bf16_q else 0.0)
+    outs = []
+    for split in (True, True, False):
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        got = _gpu(torch, case, cu, q, True, max_q=64, status=status, bf16=bf16_q, split=split)
+        assert int(status.item()) == 0
+        assert np.isfinite(got).all()
+        err = np.abs(got - want)
+        print(f"key split {split}: max-abs error {err.max():.3e}")
+        assert (err <= tol).all(), split
+        outs.append(got)
+    assert _counters_zero(torch, case, q, 64)
+    # the merged halves and the whole items differ in rounding only (which
+    # half merges may differ between calls): fp32 sums, plus one bf16 ulp of
+    # the output for bf16 out
+    ulp = np.abs(want) * 2.0 ** -7 if bf16_q else 0.0
+    assert (np.abs(outs[0] - outs[2]) <= 1e-3 + ulp).all()
+    assert (np.abs(outs[0] - outs[1]) <= 1e-5 + ulp).all()
+
+
+def test_prefill_key_split_v_beyond_f16_range(torch_cuda):
+    """A split item whose first half holds a bf16 V value beyond fp16's range
+    (that half folds its tiles again as bf16) and whose second half does not:
+    the merge of the two is within the oracle's tolerance relative to
+    max(1, |want|)."""
+    torch = torch_cuda
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the split plan of this batch assumes 256 compute units")
+    rng = np.random.default_rng(1340)
+    case, cu, q = _split_case(rng)
+    _set_v(case, 21, 40, 1, 17, 3.0e5)      # sequence 21, key 40: the first half
+    _set_v(case, 21, 41, 3, 200, -65536.0)
+    want = _oracle(case, cu, q, True)
+    got = _gpu(torch, case, cu, q, True, max_q=64)
+    assert np.isfinite(got).all()
+    assert np.abs(want).max() > 100.0
+    err = np.abs(got - want) / np.maximum(1.0, np.abs(want))
+    print(f"key split, V beyond fp16: max error relative to max(1, |want|) {err.max():.3e}")
+    assert err.max() <= 3e-3
+    assert _counters_zero(torch, case, q, 64)
