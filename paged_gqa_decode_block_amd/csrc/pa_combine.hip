@@ -30,8 +30,9 @@
 // above (the host's bound or estimate of that count), so one round usually
 // covers them all. A grid of many (sequence, head, slice) items instead runs
 // one wave per item up to 64 states (S = 4, a batch of up to 4 states per
-// thread and round): there the launch's waves outnumber what the compute units
-// hold at once, and the fewer of them the sooner the last one ends.
+// thread and round), eight items (heads) per workgroup: there the launch's
+// waves outnumber what the compute units hold at once, and the fewer waves and
+// workgroups the sooner the last one ends.
 #include "pa_kernels.h"
 
 namespace pa {
@@ -39,13 +40,17 @@ namespace {
 
 // kStripes: partition stripes (4, 8, 16, 32 or 64); kBatch: partitions per
 // thread per round (1, 2, 4 or 8); both chosen from the grid and the partition
-// count. kFold: after the streaming kernel with prefix folding (its own rows
-// and the prefix states).
-template <int kStripes, int kBatch, bool kFold>
-__global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
+// count. kItems: heads per workgroup, one wave each (with kStripes = 4 only).
+// kFold: after the streaming kernel with prefix folding (its own rows and the
+// prefix states).
+template <int kStripes, int kBatch, bool kFold, int kItems = 1>
+__global__ void __launch_bounds__(16 * kStripes * kItems) combine_kernel(Params p) {
   static_assert(kStripes % 4 == 0, "whole waves of four stripes");
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int tid = threadIdx.x;
+  static_assert(kItems == 1 || kStripes == 4, "one wave per item");
+  const int b = blockIdx.z;
+  const int h = kItems > 1 ? (int)blockIdx.y * kItems + (int)(threadIdx.x >> 6) : (int)blockIdx.y;
+  if (kItems > 1 && h >= p.Hq) return;  // (a whole wave)
+  const int tid = kItems > 1 ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
   const int u = tid & 15, s = tid >> 4;
   const int d = blockIdx.x * 64 + 4 * u;
   const bool waves = p.ws_link != nullptr;  // states of the streaming kernel's waves
@@ -177,6 +182,15 @@ __global__ void __launch_bounds__(16 * kStripes) combine_kernel(Params p) {
     oa.w = __shfl_xor(A.w, off);
     merge(Ms, Ls, A, om, ol, oa);
   }
+  if constexpr (kStripes == 4) {
+    // one wave: every lane holds the merged state of its dims
+    if (tid < 16) {
+      const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+      store_out4(p, ((int64_t)b * p.Hq + h) * p.D + d, A.x * inv, A.y * inv, A.z * inv,
+                 A.w * inv);
+    }
+    return;
+  }
   constexpr int kWaves = kStripes / 4;
   __shared__ float4 s_a[kWaves][16];
   __shared__ float s_m[kWaves], s_l[kWaves];
@@ -215,13 +229,15 @@ template <bool kFold>
 hipError_t launch_combine_t(const Params& p, hipStream_t s) {
   dim3 grid(p.D / 64, p.Hq, p.B);
   // one wave per item when the grid alone fills the GPU (about one wave per
-  // SIMD of 256 compute units); a batch of 2 or 4 states per thread per round
+  // SIMD of 256 compute units), eight heads per workgroup; a batch of 2 or 4
+  // states per thread per round
   const int64_t items = (int64_t)grid.x * grid.y * grid.z;
   if (items >= 1024 && p.pmax <= 64) {
+    const dim3 g8(grid.x, (grid.y + 7) / 8, grid.z);
     if (p.pmax <= 8)
-      hipLaunchKernelGGL((combine_kernel<4, 2, kFold>), grid, dim3(64), 0, s, p);
+      hipLaunchKernelGGL((combine_kernel<4, 2, kFold, 8>), g8, dim3(512), 0, s, p);
     else
-      hipLaunchKernelGGL((combine_kernel<4, 4, kFold>), grid, dim3(64), 0, s, p);
+      hipLaunchKernelGGL((combine_kernel<4, 4, kFold, 8>), g8, dim3(512), 0, s, p);
     return hipGetLastError();
   }
   // stripes sized to the partition count: with few partitions per sequence
