@@ -12,12 +12,13 @@
 // heads (hh = 8, or the largest power of two dividing G, so that no unit is
 // empty). All the workgroups of one (sequence, KV head) read the same K and V,
 // so they are placed on one XCD, whose L2 serves the repeats (the loads keep
-// the default cache policy). Its threads load each 16-token chunk of K and V
-// once (16-byte pieces, raw buffer loads through descriptors cut to the
-// chunk's attended rows, an invalid table entry never dereferenced) into a
-// ring of chunks in registers, and stage two consecutive chunks into one of
-// two 32-token LDS tiles; after one barrier per tile every wave folds its
-// units against it:
+// the default cache policy); an XCD with 4 to 64 pairs takes them longest
+// first, so that its last workgroups are short. Its threads load each
+// 16-token chunk of K and V once (16-byte pieces, raw buffer loads through
+// descriptors cut to the chunk's attended rows, an invalid table entry never
+// dereferenced) into a ring of chunks in registers, and stage two consecutive
+// chunks into one of two 32-token LDS tiles; after one barrier per tile every
+// wave folds its units against it:
 //
 //   scores  S^T[token, row] = K[token, :] . Q'[row, :]       16x16x32 MFMAs,
 //           two 16-token halves
@@ -136,8 +137,8 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   // The per work items of one (sequence, KV head) read the same K and V: they
   // all go to one XCD (workgroup i runs on XCD i mod kXcds), whose L2 then
   // serves the repeated reads. XCD x takes the pairs x, x + kXcds, ...
-  // The XCD's work item i (pair i / per of its list, item i % per of the
-  // pair), whole, or half sp of its key tiles.
+  // The XCD's work item i (item i % per of the pair at position i / per of
+  // its list), whole, or half sp of its key tiles.
   const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
   int wi = slot, sp = -1;
   if (slot >= nwhole) {
@@ -145,7 +146,29 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
     wi = nwhole + h % nsplit;
     sp = h / nsplit;
   }
-  const int pair = xcd + kXcds * (wi / per), item = wi % per;
+  // With 4 to 64 pairs per XCD the list is taken longest first (by key count,
+  // ties in pair order), so that the last workgroups to start are short ones;
+  // every wave ranks the pairs itself (one length per lane).
+  int pos = wi / per;
+  {
+    const int npl = (nwhole + nsplit) / per;
+    if (npl >= 4 && npl <= 64) {
+      const int ln = tid & 63, pr = xcd + kXcds * ln;
+      int Lr = -1;  // padding pairs last
+      if (ln < npl && pr < p.B * p.Hkv) {
+        const int lmax = p.MBS << p.bs_log2;
+        Lr = min(max(p.seqlens[pr / p.Hkv], 0), lmax);
+      }
+      int rank = 0;
+      for (int j = 0; j < npl; ++j) {
+        const int Lj = __shfl(Lr, j);
+        rank += (Lj > Lr || (Lj == Lr && j < ln)) ? 1 : 0;
+      }
+      const uint64_t hit = __ballot(ln < npl && rank == pos);
+      if (hit) pos = (int)__builtin_ctzll(hit);
+    }
+  }
+  const int pair = xcd + kXcds * pos, item = wi % per;
   if (pair >= p.B * p.Hkv) return;  // padding of the last round
   const int b = pair / p.Hkv, hk = pair % p.Hkv;
   const int g0 = (item % nhg) * hh;
