@@ -713,7 +713,10 @@ def main():
             f"({r2['warm_ms_per_step'] * 1e3:.1f} warm), {r2['kv_gbs']:.0f} GB/s")
         also[w2.case.name] = {**w2.describe(), **{k2: (round(v, 4) if isinstance(v, float) else v)
                                                   for k2, v in r2.items()},
-                              "pct_hbm_peak": round(100 * r2["kv_gbs"] / HBM_PEAK_GBS, 2),
+                              # on distinct K/V bytes (a shared block once): the
+                              # logical rate of a prefix-shared batch read with
+                              # folding can pass the HBM peak
+                              "pct_hbm_peak": round(100 * r2["unique_kv_gbs"] / HBM_PEAK_GBS, 2),
                               "roofline": roofline(w2, r2)}
         if not a.no_cpu_baseline:
             also[w2.case.name]["parity"] = cpu_baseline_parity(w2, w2.out.float().cpu().numpy())
@@ -760,7 +763,7 @@ def main():
         "dtype": wl.case.kv_dtype,
         "data": "synthetic (seeded)",
         "config": wl.describe(),
-        "pct_hbm_peak": round(100 * r["kv_gbs"] / HBM_PEAK_GBS, 2),
+        "pct_hbm_peak": round(100 * r["unique_kv_gbs"] / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(r["seq_heads_per_s"], 1),
         "detail": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()},
         "roofline": rl,
