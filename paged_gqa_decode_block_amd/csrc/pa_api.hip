@@ -345,12 +345,12 @@ bool prefill_kv_ok(const pa_desc* desc) {
 
 size_t paged_attn_prefill_workspace_size(const pa_desc* desc, int32_t max_seqlen_q) {
   if (validate(desc) != PA_OK || !prefill_kv_ok(desc) || max_seqlen_q <= 0) return 0;
-  return pa::prefill_workspace_bytes(prefill_shape(desc), max_seqlen_q);
+  return pa::prefill_workspace_bytes(prefill_shape(desc), desc->kv_dtype, max_seqlen_q);
 }
 
 size_t paged_attn_prefill_workspace_zeroed_bytes(const pa_desc* desc, int32_t max_seqlen_q) {
   if (validate(desc) != PA_OK || !prefill_kv_ok(desc) || max_seqlen_q <= 0) return 0;
-  return pa::prefill_workspace_zeroed_bytes(prefill_shape(desc), max_seqlen_q);
+  return pa::prefill_workspace_zeroed_bytes(prefill_shape(desc), desc->kv_dtype, max_seqlen_q);
 }
 
 int paged_attn_check_inputs(const pa_desc* desc, const int32_t* table, const int32_t* seqlens) {
@@ -623,7 +623,7 @@ int paged_attn_prefill(const pa_desc* desc, const void* q, const void* k_cache, 
   if (desc->block_size < 16 || max_seqlen_q < 0) return PA_E_SHAPE;
   if (max_seqlen_q == 0) return PA_OK;
   // the key split needs its workspace; without one every work item runs whole
-  const size_t need = pa::prefill_workspace_bytes(p, max_seqlen_q);
+  const size_t need = pa::prefill_workspace_bytes(p, desc->kv_dtype, max_seqlen_q);
   if (workspace && need > workspace_bytes) return PA_E_WORKSPACE;
   if (workspace && ((uintptr_t)workspace & 255)) return PA_E_ALIGN;
   return pa::launch_prefill(p, desc->kv_dtype, cu_seqlens_q, max_seqlen_q, causal != 0,

@@ -76,15 +76,15 @@ hipError_t launch_combine(const Params& p, hipStream_t s);
 // Paged varlen prefill: query rows cu_q[b] .. cu_q[b+1]-1 of sequence b (at
 // most max_q of them), keys its p.seqlens[b] cached tokens, causal or not;
 // 16-bit K/V only. ws: the key split's arrival counters (zero on entry, left
-// zero) and half states, of prefill_workspace_bytes(p, max_q) bytes; NULL runs
+// zero) and half states, of prefill_workspace_bytes(p, dtype, max_q) bytes; NULL runs
 // every work item whole.
 hipError_t launch_prefill(const Params& p, int dtype, const int32_t* cu_q, int max_q, int causal,
                           void* ws, hipStream_t s);
 // Workspace of the prefill's key split for these parameters (p.B, p.Hkv, p.G,
-// p.D, p.qo_bf16, p.cus) and max_q: 0 when no work item is split.
-size_t prefill_workspace_bytes(const Params& p, int max_q);
+// p.D, p.qo_bf16, p.cus), the K/V dtype and max_q: 0 when no work item is split.
+size_t prefill_workspace_bytes(const Params& p, int dtype, int max_q);
 // Leading bytes of that workspace (arrival counters) that must be zero.
-size_t prefill_workspace_zeroed_bytes(const Params& p, int max_q);
+size_t prefill_workspace_zeroed_bytes(const Params& p, int dtype, int max_q);
 // Write each sequence's new K and V rows ([B, H_kv, d], the cache's element
 // type) at token cache_seqlens[b] of its paged cache.
 hipError_t launch_append(const Params& p, const void* k_new, const void* v_new, int elem_bytes,

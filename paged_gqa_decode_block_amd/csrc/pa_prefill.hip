@@ -90,9 +90,9 @@ __device__ __forceinline__ uint4 bf16x8_to_f16(uint4 w) {
   return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
-// NW waves per workgroup (4: two heads per wave; 8: one head per wave, half
-// the registers, so that d = 256 runs two waves per SIMD), NBUF ring slots,
-// OCC waves per SIMD.
+// NW waves per workgroup (4: two units per wave, each K and V^T fragment read
+// once for both; 8: one unit per wave, half the registers, so that d = 256
+// runs two waves per SIMD), NBUF ring slots, OCC waves per SIMD.
 //
 // Work items per XCD: the first nwhole whole, the next nsplit split in two
 // halves (all first halves dispatched, then all second halves); ws_cnt
@@ -395,6 +395,72 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
     }
   };
 
+  // all of the wave's head slots against tile tc (V in fp16), each K and V^T
+  // fragment read from LDS once for all of them (a wave's units share the
+  // workgroup's keys): half the fragment reads per MFMA of one slot at a time
+  auto consume_all = [&](int tc, int buf) __attribute__((always_inline)) {
+    const uint16_t* sk = s_k[buf];
+    const uint16_t* sv_ = s_v[buf];
+    f32x4 st[HPW][2];
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) st[j][0] = st[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const V8 a = *(const V8*)(sk + tau * kHalf + TR::row(r) + 8 * (4 * ks + q));
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          st[j][tau] = M::mma32(a, qhi[j][ks], st[j][tau]);
+          if constexpr (!kQ1) st[j][tau] = M::mma32(a, qlo[j][ks], st[j][tau]);
+        }
+      }
+    }
+    H8 ph[HPW];
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      float sv[8];
+      if (32 * tc + 32 <= kfull[j]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sv[i] = st[j][i >> 2][i & 3];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          sv[i] = (32 * tc + 16 * (i >> 2) + 4 * q + (i & 3) < kend_r[j]) ? st[j][i >> 2][i & 3]
+                                                                          : -INFINITY;
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+      const float mt = quad_max(mx) * qmul;
+      const bool raise = mt > m[j] + 8.f;
+      if (__ballot(raise)) {
+        const float mn = raise ? mt : m[j];
+        const float alpha = exp2_fast(m[j] - (mn == -INFINITY ? 0.f : mn));
+        l[j] *= alpha;
+#pragma unroll
+        for (int k = 0; k < MB; ++k) acc[j][k] *= alpha;
+        m[j] = mn;
+      }
+      const float mu = m[j] == -INFINITY ? 0.f : m[j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ph[j][i] = (_Float16)exp2_fast(fmaf(sv[i], qmul, -mu));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        l[j] = __builtin_amdgcn_fdot2(h2{ph[j][2 * i], ph[j][2 * i + 1]}, h2{1, 1}, l[j], false);
+    }
+    const int vbase = TR::row(4 * q + tj) + 8 * (tk >> 1) + 4 * (tk & 1);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int o = vbase + 16 * mb;
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + o));
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sv_ + kHalf + o));
+      const H8 av = __builtin_bit_cast(H8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) acc[j][mb] = H::mma32(av, ph[j], acc[j][mb]);
+    }
+  };
+
   // One pass over the workgroup's tiles [c0, nch) (WIDE: V staged as bf16). The ring:
   // chunk c + NBUF - 1 is issued just before chunk c is staged
   // (unconditionally: past the end the descriptors are empty, so an odd last
@@ -431,9 +497,13 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
           }
           if (c & 1) {
             __syncthreads();
+            if constexpr (HPW > 1 && !wide) {
+              consume_all(c >> 1, buf);  // (a slot without a unit folds zeros, unread)
+            } else {
 #pragma unroll
-            for (int j = 0; j < HPW; ++j)
-              if (hon[j]) consume(c >> 1, buf, j, WIDE);
+              for (int j = 0; j < HPW; ++j)
+                if (hon[j]) consume(c >> 1, buf, j, WIDE);
+            }
           }
         }
       });
@@ -543,12 +613,17 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   if (bad_block && tid == 0 && p.status) atomicOr(p.status, kStatusBadBlock);
 }
 
-// {waves per workgroup, ring slots, waves per SIMD} per q/out type and
-// head_dim (fp32 q at d = 128 holds Q' in two parts: a ring of two slots keeps
-// the loop within the 128 registers of four waves per SIMD)
-constexpr int kPrefillCfg[2][3][3] = {{{4, 6, 2}, {8, 2, 4}, {8, 4, 2}},
-                                      {{4, 6, 2}, {8, 4, 4}, {8, 4, 2}}};
+// {waves per workgroup, ring slots, waves per SIMD} per Q' form and head_dim.
+// Q' forms: 0 fp32 q (two parts), 1 bf16 q over fp16 K/V (two parts), 2 bf16 q
+// over bf16 K/V (one exact part). Two parts at d = 128: a ring of two slots
+// (fp32 q) keeps the loop within the 128 registers of four waves per SIMD.
+// One part at d = 128: four waves of two units each (their K and V^T
+// fragments read once for both), three workgroups per compute unit.
+constexpr int kPrefillCfg[3][3][3] = {{{4, 6, 2}, {8, 2, 4}, {8, 4, 2}},
+                                      {{4, 6, 2}, {8, 4, 4}, {8, 4, 2}},
+                                      {{4, 6, 2}, {4, 2, 3}, {8, 4, 2}}};
 constexpr int pdim(int D) { return D == 64 ? 0 : D == 128 ? 1 : 2; }
+constexpr int qform(int dtype, int qo) { return qo == 0 ? 0 : dtype == 2 ? 2 : 1; }
 
 // The launch's shape: heads per workgroup, work items per (sequence, KV head)
 // and per XCD, and how many of each XCD's items are whole and split.
@@ -559,10 +634,10 @@ struct Plan {
   int D = 0;
 };
 
-Plan plan(const Params& p, int max_q) {
+Plan plan(const Params& p, int dtype, int max_q) {
   Plan pl;
-  const int qo = p.qo_bf16 ? 1 : 0, di = pdim(p.D);
-  const int NW = kPrefillCfg[qo][di][0], OCC = kPrefillCfg[qo][di][2];
+  const int qf = qform(dtype, p.qo_bf16 ? 1 : 0), di = pdim(p.D);
+  const int NW = kPrefillCfg[qf][di][0], OCC = kPrefillCfg[qf][di][2];
   pl.D = p.D;
   // heads per workgroup: 8 when they divide G; else the largest power of two
   // dividing G, with 8 / hh tiles per workgroup so that no unit is idle, if
@@ -605,9 +680,10 @@ size_t split_cnt_bytes(const Plan& pl) {
 template <typename T, int D, int QO>
 hipError_t launch_p(const Params& p, const int32_t* cu_q, int max_q, int causal, void* ws,
                     hipStream_t s) {
-  constexpr int NW = kPrefillCfg[QO][pdim(D)][0], NB_ = kPrefillCfg[QO][pdim(D)][1],
-                OCC = kPrefillCfg[QO][pdim(D)][2];
-  Plan pl = plan(p, max_q);
+  constexpr int QF = qform(std::is_same<T, __bf16>::value ? 2 : 1, QO);
+  constexpr int NW = kPrefillCfg[QF][pdim(D)][0], NB_ = kPrefillCfg[QF][pdim(D)][1],
+                OCC = kPrefillCfg[QF][pdim(D)][2];
+  Plan pl = plan(p, std::is_same<T, __bf16>::value ? 2 : 1, max_q);
   if (!ws) {
     pl.nwhole = pl.items;
     pl.nsplit = 0;
@@ -647,16 +723,16 @@ hipError_t launch_prefill(const Params& p, int dtype, const int32_t* cu_q, int m
   return hipErrorInvalidValue;
 }
 
-size_t prefill_workspace_bytes(const Params& p, int max_q) {
+size_t prefill_workspace_bytes(const Params& p, int dtype, int max_q) {
   if (max_q <= 0 || p.B <= 0 || (p.D != 64 && p.D != 128 && p.D != 256)) return 0;
-  const Plan pl = plan(p, max_q);
+  const Plan pl = plan(p, dtype, max_q);
   if (pl.nsplit == 0) return 0;
   return split_cnt_bytes(pl) + (size_t)kXcds * pl.nsplit * split_item_floats(p.D) * sizeof(float);
 }
 
-size_t prefill_workspace_zeroed_bytes(const Params& p, int max_q) {
-  if (prefill_workspace_bytes(p, max_q) == 0) return 0;
-  return (size_t)kXcds * plan(p, max_q).nsplit * sizeof(int32_t);
+size_t prefill_workspace_zeroed_bytes(const Params& p, int dtype, int max_q) {
+  if (prefill_workspace_bytes(p, dtype, max_q) == 0) return 0;
+  return (size_t)kXcds * plan(p, dtype, max_q).nsplit * sizeof(int32_t);
 }
 
 }  // namespace pa

@@ -338,12 +338,13 @@ def test_prefill_key_split_workspace():
     is visible) and 8 XCDs. Work items per XCD: the (sequence, KV head) pairs
     dealt round robin (ceil(B Hkv / 8) rounds of pairs) times the items per pair
     (16-row tile groups x head groups); the workgroups an XCD holds at once: 32
-    compute units x (1 at d = 256, 2 at d = 128). A last round at most half full
-    is split: counters (8 x split items int32, 256-byte aligned) then two
-    halves' states (8 units x (d/16 x 256 + 128) floats) per split item."""
-    def desc(B, Hq, Hkv, D, bf=True):
+    compute units x (1 at d = 256; at d = 128 3 with bf16 q over bf16 K/V, else
+    2). A last round at most half full is split: counters (8 x split items
+    int32, 256-byte aligned) then two halves' states (8 units x (d/16 x 256 +
+    128) floats) per split item."""
+    def desc(B, Hq, Hkv, D, bf=True, kv="bf16"):
         return _desc(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, max_blocks_per_seq=512,
-                     num_blocks=2048, k_strides=(Hkv * 16 * D, 16 * D, D), qo_bf16=bf)
+                     num_blocks=2048, k_strides=(Hkv * 16 * D, 16 * D, D), qo_bf16=bf, kv_dtype=kv)
     def want(nsplit, D):
         cnt = (8 * nsplit * 4 + 255) // 256 * 256
         return cnt + 8 * nsplit * 2 * 8 * ((D // 16) * 256 + 128) * 4, 8 * nsplit * 4
@@ -359,11 +360,17 @@ def test_prefill_key_split_workspace():
     # 96 = 3 x 32: none
     assert pa.prefill_workspace_size(desc(6, 24, 4, 256), 512) == want(8, 256)[0]
     assert pa.prefill_workspace_size(desc(8, 24, 4, 256), 512) == 0
-    # d = 128, G = 8 (eight heads x one tile): 256 rows -> 16 items per pair;
-    # 128 pairs -> 256 items per XCD = 4 x 64: none; 40 pairs -> 80 = 64 + 16:
-    # the 16 are split
+    # d = 128, G = 8 (eight heads x one tile): 256 rows -> 16 items per pair.
+    # bf16 q over bf16 K/V (96 per XCD at once): 128 pairs -> 256 items = 2 x 96
+    # + 64: more than half, none; 112 pairs -> 224 = 2 x 96 + 32: 32 split;
+    # 40 pairs -> 80: fewer than 96
     assert pa.prefill_workspace_size(desc(16, 64, 8, 128), 256) == 0
-    assert pa.prefill_workspace_size(desc(5, 64, 8, 128), 256) == want(16, 128)[0]
+    assert pa.prefill_workspace_size(desc(14, 64, 8, 128), 256) == want(32, 128)[0]
+    assert pa.prefill_workspace_size(desc(5, 64, 8, 128), 256) == 0
+    # fp32 q, or bf16 q over fp16 K/V (64 per XCD at once): 40 pairs -> 80 =
+    # 64 + 16: 16 split
+    assert pa.prefill_workspace_size(desc(5, 64, 8, 128, bf=False), 256) == want(16, 128)[0]
+    assert pa.prefill_workspace_size(desc(5, 64, 8, 128, kv="f16"), 256) == want(16, 128)[0]
     # refused descriptors and no rows: 0
     assert pa.prefill_workspace_size(desc(4, 24, 4, 256), 0) == 0
     assert pa.prefill_workspace_size(_desc(kv_dtype="f32", k_strides=(4096, 2048, 128)), 512) == 0
