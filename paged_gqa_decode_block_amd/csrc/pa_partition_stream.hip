@@ -79,6 +79,29 @@ namespace {
 
 constexpr int kMaxWindows = 16;  // 16 x 64 = 1024 sequences
 
+// Partial-state stores. wt: with the device-scope cache policy (SC1 set, SC0
+// clear on gfx950), written through the XCD's L2 as they are made rather than
+// left dirty there for the write-back at the kernel's end (the combine kernel
+// reads them from the other XCDs anyway). On the one-wave-per-share kernel
+// without prefix folding, whose waves end over a wide spread of times, that
+// measured faster (64-sequence batch, partition kernel -3 us); where the
+// waves end together (pairs at head_dim 256) or with prefix folding it
+// measured slower, so those keep the default policy. The store takes the
+// same per-lane address registers as a plain one (no buffer descriptor held
+// in the loop).
+__device__ __forceinline__ void store_state4(float* ptr, f32x4 v, bool wt) {
+  if (wt)
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(ptr), "v"(v) : "memory");
+  else
+    *(f32x4*)ptr = v;
+}
+__device__ __forceinline__ void store_state1(float* ptr, float v, bool wt) {
+  if (wt)
+    asm volatile("global_store_dword %0, %1, off sc1" : : "v"(ptr), "v"(v) : "memory");
+  else
+    *ptr = v;
+}
+
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -113,6 +136,11 @@ partition_stream_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) V8 s_q[DS][kQLds ? 2 : 1][kQLds ? KS : 1][64];
   // partial scores of the pair, double-buffered by chunk parity
   __shared__ __attribute__((aligned(16))) f32x4 s_x[DS == 2 ? 2 : 1][DS][64];
+  // the share's first segment's partial state while later segments stream
+  // (stored at the share's end: a store in the middle would make the next
+  // chunk's wait cover it)
+  __shared__ __attribute__((aligned(16))) f32x4 s_park[DS][MB][64];
+  __shared__ float s_park_ml[DS][2][64];
 
   const int lane = threadIdx.x & 63;
   // which half of the head dims this wave holds (0 when DS = 1), uniform
@@ -239,6 +267,8 @@ partition_stream_kernel(Params p) {
   // ---- 2. segments: the share's runs of chunks within one (b, KV head) -------
   int bad_block = 0;
   bool first_seg = true;
+  int park_cols = 0;  // the first segment's state waits in s_park: its valid columns
+  const bool wt = DS == 1 && F == 0;  // write-through partial states (store_state4)
   while (g < g_end) {
     if (F > 0) {
       gi = v / (F + 1);
@@ -396,17 +426,25 @@ partition_stream_kernel(Params p) {
             float* const cacc = ow ? p.ws_oacc : p.ws_cacc;
             float* const cm = ow ? p.ws_om : p.ws_cm;
             float* const cl = ow ? p.ws_ol : p.ws_cl;
-            const int64_t row = (ow ? rec * p.rps : (int64_t)slot * p.rps) + r;
-            float* ap = cacc + row * D + half * DW + 4 * q;
+            if (!ow && first_seg && g + nch < g_end) {
+              // more segments follow in this share: park the state
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              *(float4*)(ap + 16 * mb) = make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
-            if (q == 0 && half == 0) {
-              cm[row] = m;
-              cl[row] = lt;
+              for (int mb = 0; mb < MB; ++mb) s_park[half][mb][lane] = acc[mb];
+              s_park_ml[half][0][lane] = m;
+              s_park_ml[half][1][lane] = lt;
+            } else {
+              const int64_t row = (ow ? rec * p.rps : (int64_t)slot * p.rps) + r;
+              float* ap = cacc + row * D + half * DW + 4 * q;
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb) store_state4(ap + 16 * mb, acc[mb], wt);
+              if (q == 0 && half == 0) {
+                store_state1(cm + row, m, wt);
+                store_state1(cl + row, lt, wt);
+              }
             }
           }
         }
+        if (!whole && !own && first_seg && g + nch < g_end) park_cols = fseg ? nm * G : G;
         if (jA == 0 && lane == 0 && half == 0) {
           // chunks [cs, cs + ncb) of the batch are this stream; the last one
           // lies in the share of wave wave_of(cs + ncb - 1)
@@ -535,6 +573,19 @@ partition_stream_kernel(Params p) {
           L = F > 0 ? p.ws_vlen[v] : clamped_len(p, v, false);
           ncb = (L + 15) >> 4;
         } while (ncb == 0);
+      }
+    }
+  }
+  if (park_cols > 0) {
+    // the first segment's state into slot 0, now that no chunk waits follow
+    if (r < park_cols) {
+      const int64_t row = (int64_t)(2 * wx) * p.rps + r;
+      float* ap = p.ws_cacc + row * D + half * DW + 4 * q;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) store_state4(ap + 16 * mb, s_park[half][mb][lane], wt);
+      if (q == 0 && half == 0) {
+        store_state1(p.ws_cm + row, s_park_ml[half][0][lane], wt);
+        store_state1(p.ws_cl + row, s_park_ml[half][1][lane], wt);
       }
     }
   }
