@@ -316,3 +316,53 @@ def test_prefill_key_split_v_beyond_f16_range(torch_cuda):
     print(f"key split, V beyond fp16: max error relative to max(1, |want|) {err.max():.3e}")
     assert err.max() <= 3e-3
     assert _counters_zero(torch, case, q, 64)
+
+
+SPLIT_CASES = [
+    # name, B, Hq, Hkv, D, K/V dtype, bf16 q, causal: each plan splits the last
+    # round (256 compute units): d = 128 bf16 q over bf16 K/V holds 96
+    # workgroups per XCD at once, 14 x 8 pairs x 16 items = 224 per XCD = 2 x 96
+    # + 32; over fp16 K/V 64 at once, 5 x 8 pairs -> 80 = 64 + 16; d = 256
+    # without the causal mask as in test_prefill_key_split
+    ("d128_bf16_q16", 14, 64, 8, 128, "bf16", True, True),
+    ("d128_f16_q16", 5, 64, 8, 128, "f16", True, True),
+    ("d128_bf16_q32", 5, 64, 8, 128, "bf16", False, True),
+    ("d256_full", 24, 24, 4, 256, "bf16", True, False),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SPLIT_CASES)), ids=[c[0] for c in SPLIT_CASES])
+def test_prefill_key_split_shapes(torch_cuda, idx):
+    """The key split on other head sizes, K/V and q types and without the
+    causal mask: 256 query rows per sequence (at most), key counts in 256..700,
+    against the oracle, and the workspace's counters zero again after."""
+    from paged_gqa_decode_block_amd import workload as W
+
+    torch = torch_cuda
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the split plans of these batches assume 256 compute units")
+    name, B, Hq, Hkv, D, dt, bf16_q, causal = SPLIT_CASES[idx]
+    rng = np.random.default_rng(1350 + idx)
+    klens = rng.integers(256, 700, size=B).astype(np.int32)
+    qmax = 64 if D == 256 else 256
+    qlens = np.minimum(klens, qmax)
+    case, cu, q = _make(rng, Hq=Hq, Hkv=Hkv, D=D, bs=16, kv_dtype=dt, klens=klens, qlens=qlens)
+    desc = pa.desc_for(torch.empty(1, Hq, D, device="cuda",
+                                   dtype=torch.bfloat16 if bf16_q else torch.float32),
+                       _pool(torch, case, case.k_store), _pool(torch, case, case.v_store),
+                       torch.from_numpy(case.block_table).to("cuda"))
+    desc.batch = B
+    assert pa.prefill_workspace_size(desc, qmax) > 0, name
+    if bf16_q:
+        q = W.from_storage(W.to_storage(q, "bf16"), "bf16").astype(np.float32)
+    want = _oracle(case, cu, q, causal)
+    got = _gpu(torch, case, cu, q, causal, max_q=qmax, bf16=bf16_q)
+    assert np.isfinite(got).all()
+    tol = 3e-3 + (np.abs(want) * 2.0 ** -8 if bf16_q else 0.0)
+    err = np.abs(got - want)
+    print(f"{name}: max-abs error {err.max():.3e}")
+    assert (err <= tol).all(), name
+    ws = pa.prefill_workspace_for(desc, qmax, torch.device("cuda"))
+    zb = pa.prefill_workspace_zeroed_bytes(desc, qmax)
+    torch.cuda.synchronize()
+    assert int(ws[:zb].count_nonzero().item()) == 0
