@@ -316,7 +316,8 @@ int paged_attn_combine_phase(const pa_desc* desc, const int32_t* cache_seqlens, 
  *   out            float32 [total_q, H_q, d], contiguous, 16-byte aligned
  *   workspace      NULL, or device memory of at least
  *                  paged_attn_prefill_workspace_size(desc, max_seqlen_q) bytes
- *                  (256-byte aligned, else PA_E_ALIGN; smaller: PA_E_WORKSPACE)
+ *                  (smaller: PA_E_WORKSPACE; when that size is not 0, 256-byte
+ *                  aligned, else PA_E_ALIGN)
  *                  whose leading paged_attn_prefill_workspace_zeroed_bytes()
  *                  bytes are zero. It holds the key split's arrival counters
  *                  and half states: when the launch's work items (8 (16-row

@@ -625,7 +625,7 @@ int paged_attn_prefill(const pa_desc* desc, const void* q, const void* k_cache, 
   // the key split needs its workspace; without one every work item runs whole
   const size_t need = pa::prefill_workspace_bytes(p, desc->kv_dtype, max_seqlen_q);
   if (workspace && need > workspace_bytes) return PA_E_WORKSPACE;
-  if (workspace && ((uintptr_t)workspace & 255)) return PA_E_ALIGN;
+  if (workspace && need > 0 && ((uintptr_t)workspace & 255)) return PA_E_ALIGN;
   return pa::launch_prefill(p, desc->kv_dtype, cu_seqlens_q, max_seqlen_q, causal != 0,
                             need > 0 ? workspace : nullptr, (hipStream_t)stream) == hipSuccess
              ? PA_OK
