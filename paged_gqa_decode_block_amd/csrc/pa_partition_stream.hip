@@ -22,8 +22,10 @@
 // size is not used): a stream that lies inside one share is folded whole and
 // its normalised output written directly; a stream that several consecutive
 // waves share leaves one partial state (max, sum, unnormalised output) per
-// wave, written once when the wave's segment of it ends, and the combine
-// kernel merges those states. A share partly covers at most two streams (its
+// wave, written once when the wave's segment of it ends (the share's first
+// segment's state, when more segments follow, waits in LDS until the share
+// ends: a store in the middle of the share would make the next chunk's wait
+// cover it), and the combine kernel merges those states. A share partly covers at most two streams (its
 // first and its last), so each wave has two state slots; the wave holding a
 // stream's first chunk records which slot starts the stream's run of states
 // and how many waves the run spans. Writing one state per wave, not one per
