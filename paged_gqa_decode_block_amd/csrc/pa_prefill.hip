@@ -125,7 +125,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kTile];
   __shared__ int s_redo;
-  __shared__ int s_arrived;  // the key split: halves of the item before this one
+  __shared__ int s_arrived;  // the key split: halves of the item that arrived before this one
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // w: the wave's
