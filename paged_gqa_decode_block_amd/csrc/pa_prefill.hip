@@ -615,11 +615,11 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
 
 // {waves per workgroup, ring slots, waves per SIMD} per Q' form and head_dim.
 // Q' forms: 0 fp32 q (two parts), 1 bf16 q over fp16 K/V (two parts), 2 bf16 q
-// over bf16 K/V (one exact part). Two parts at d = 128: a ring of two slots
-// (fp32 q) keeps the loop within the 128 registers of four waves per SIMD.
-// One part at d = 128: four waves of two units each (their K and V^T
-// fragments read once for both), three workgroups per compute unit.
-constexpr int kPrefillCfg[3][3][3] = {{{4, 6, 2}, {8, 2, 4}, {8, 4, 2}},
+// over bf16 K/V (one exact part). At d = 128 four waves of two units each
+// (their K and V^T fragments read once for both): two workgroups per compute
+// unit with fp32 q, three with one Q' part; bf16 q over fp16 K/V keeps eight
+// waves of one unit.
+constexpr int kPrefillCfg[3][3][3] = {{{4, 6, 2}, {4, 4, 2}, {8, 4, 2}},
                                       {{4, 6, 2}, {8, 4, 4}, {8, 4, 2}},
                                       {{4, 6, 2}, {4, 2, 3}, {8, 4, 2}}};
 constexpr int pdim(int D) { return D == 64 ? 0 : D == 128 ? 1 : 2; }
