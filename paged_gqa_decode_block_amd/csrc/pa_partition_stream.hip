@@ -34,8 +34,10 @@
 // wrote, and those writes cost far more time than their share of the traffic.
 //
 // Loads are raw buffer loads of full token rows (each 16-byte lane load is part
-// of a contiguous row segment of 128-512 bytes) with the non-temporal hint. The
-// per-chunk buffer descriptor (built in scalar registers) starts at the chunk's
+// of a contiguous row segment of 128-512 bytes) with the non-temporal hint,
+// except where blocks are declared shared: there the folded prefixes keep the
+// default policy (several groups read them) and, without folding, every load
+// does. The per-chunk buffer descriptor (built in scalar registers) starts at the chunk's
 // first row and its size covers only the attended rows, so rows past L_b and
 // chunks behind an invalid table entry read as zeros without touching memory.
 // Each chunk is then written to two padded LDS tiles and read back in MFMA
@@ -379,10 +381,21 @@ partition_stream_kernel(Params p) {
             kbase + (idc * p.ksb + row0 * p.kst) * (int)sizeof(T), rows * kst_bytes);
         const __amdgpu_buffer_rsrc_t rsv = uniform_rsrc(
             vbase + (idc * p.vsb + row0 * p.vst) * (int)sizeof(T), rows * vst_bytes);
+        // with prefix folding only the folded prefixes keep POL (their blocks
+        // are read once per group, by several groups); every other segment's
+        // blocks are read once in the whole launch
+        if (POL == 2 || (F > 0 && !fseg)) {
 #pragma unroll
-        for (int s = 0; s < LPC; ++s) {
-          rk[s] = buf_load<POL>(rsk, koffs[s]);
-          rv[s] = buf_load<POL>(rsv, voffs[s]);
+          for (int s = 0; s < LPC; ++s) {
+            rk[s] = buf_load<2>(rsk, koffs[s]);
+            rv[s] = buf_load<2>(rsv, voffs[s]);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < LPC; ++s) {
+            rk[s] = buf_load<POL>(rsk, koffs[s]);
+            rv[s] = buf_load<POL>(rsv, voffs[s]);
+          }
         }
         ids = fetch_id(cn + NBUF);
         return rows;
