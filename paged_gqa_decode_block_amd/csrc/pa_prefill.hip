@@ -16,9 +16,10 @@
 // first, so that its last workgroups are short. Its threads load each
 // 16-token chunk of K and V once (16-byte pieces, raw buffer loads through
 // descriptors cut to the chunk's attended rows, an invalid table entry never
-// dereferenced) into a ring of chunks in registers, and stage two consecutive
-// chunks into one of two 32-token LDS tiles; after one barrier per tile every
-// wave folds its units against it:
+// dereferenced) into a ring of chunks in registers, and stage consecutive
+// chunks into one of two LDS tiles of 32 tokens (64 for bf16 q at d = 256);
+// after one barrier per tile every wave folds its units against each 32-token
+// half of it:
 //
 //   scores  S^T[token, row] = K[token, :] . Q'[row, :]       16x16x32 MFMAs,
 //           two 16-token halves
@@ -115,10 +116,14 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   constexpr int HPW = kHeadsPerGroup / NW;
   static_assert(PPT * kThreads == 4 * D, "the workgroup loads a chunk in whole pieces");
   static_assert((NBUF - 1) * PPT <= 60, "ring deeper than the vector-memory counter");
-  // 32-row K and V tiles with the decode's padded rows (one 32-byte pad per
-  // 256-byte bank line: conflict-free fragment reads and staging writes)
+  // 16 CPT-row K and V tiles with the decode's padded rows (one 32-byte pad
+  // per 256-byte bank line: conflict-free fragment reads and staging writes)
   typedef TileRows<D> TR;
-  constexpr int kTile = 32 * D + (32 / TR::RPL) * TR::PAD;
+  // 16-token chunks per LDS tile: 64-token tiles (one barrier per four
+  // chunks) for bf16 q at d = 256, where a workgroup has the compute unit's
+  // LDS to itself (measured 1-2 % faster there, slower with fp32 q)
+  constexpr int CPT = (D == 256 && QO == 1) ? 4 : 2;
+  constexpr int kTile = 16 * CPT * D + (16 * CPT / TR::RPL) * TR::PAD;
   constexpr int kHalf = 16 * D + (16 / TR::RPL) * TR::PAD;  // TR::row(16 + x) - TR::row(x)
   // V tiles hold fp16 (bf16 V converted while staged), or bf16 on the second
   // pass of a workgroup whose first pass left a non-finite output (s_redo)
@@ -188,11 +193,11 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   // tiles (rounded up) or the rest
   int c0 = 0, nch = (kend + 15) >> 4;
   if (sp >= 0) {
-    const int th = (((nch + 1) >> 1) + 1) >> 1;
+    const int th = ((nch + CPT - 1) / CPT + 1) >> 1;
     if (sp == 0)
-      nch = min(nch, 2 * th);
+      nch = min(nch, CPT * th);
     else
-      c0 = 2 * th;
+      c0 = CPT * th;
   }
 
   // slot j of this wave: unit u = w + NW j, tile u / hh, head u % hh. Column r
@@ -308,14 +313,15 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   }
   const int tj = r >> 2, tk = r & 3;
 
-  // fold 32-token tile tc (tokens 32 tc .., staged in LDS tile `buf`) into
+  // fold 32-token tile tc (tokens 32 tc .., staged in LDS tile `buf` from
+  // element `base` on) into
   // head slot j; WIDE: the V tile holds bf16 (the second pass). P^T k-slot i of
   // lane (q, r) holds token 16 (i / 4) + 4 q + i % 4, the score MFMA's output
   // layout of the two halves.
-  auto consume = [&](int tc, int buf, int j, auto WIDE) __attribute__((always_inline)) {
+  auto consume = [&](int tc, int buf, int base, int j, auto WIDE) __attribute__((always_inline)) {
     constexpr bool wide = decltype(WIDE)::value;
-    const uint16_t* sk = s_k[buf];
-    const uint16_t* sv_ = s_v[buf];
+    const uint16_t* sk = s_k[buf] + base;
+    const uint16_t* sv_ = s_v[buf] + base;
     f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -398,9 +404,9 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
   // all of the wave's head slots against tile tc (V in fp16), each K and V^T
   // fragment read from LDS once for all of them (a wave's units share the
   // workgroup's keys): half the fragment reads per MFMA of one slot at a time
-  auto consume_all = [&](int tc, int buf) __attribute__((always_inline)) {
-    const uint16_t* sk = s_k[buf];
-    const uint16_t* sv_ = s_v[buf];
+  auto consume_all = [&](int tc, int buf, int base) __attribute__((always_inline)) {
+    const uint16_t* sk = s_k[buf] + base;
+    const uint16_t* sv_ = s_v[buf] + base;
     f32x4 st[HPW][2];
 #pragma unroll
     for (int j = 0; j < HPW; ++j) st[j][0] = st[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -463,11 +469,11 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
 
   // One pass over the workgroup's tiles [c0, nch) (WIDE: V staged as bf16). The ring:
   // chunk c + NBUF - 1 is issued just before chunk c is staged
-  // (unconditionally: past the end the descriptors are empty, so an odd last
-  // chunk is paired with zeros). Chunk c goes to half c % 2 of 32-token LDS
-  // tile (c / 2) % 2; the barrier after a tile's second half also means every
+  // (unconditionally: past the end the descriptors are empty, so a short
+  // last tile is filled up with zeros). Chunk c goes to part c % CPT of LDS
+  // tile (c / CPT) % 2; the barrier after a tile's last part also means every
   // wave is done with the tile before, so the other tile is free.
-  const int nch2 = (nch + 1) & ~1;
+  const int nch2 = (nch + CPT - 1) / CPT * CPT;
   auto fold_all = [&](auto WIDE) __attribute__((always_inline)) {
     constexpr bool wide = decltype(WIDE)::value;
     int idr[NBUF];
@@ -485,7 +491,7 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
         issue(c + NBUF - 1, ring[sn], idr[sn]);
         __builtin_amdgcn_sched_barrier(0);
         if (c < nch2) {
-          const int buf = (c >> 1) & 1, half = (c & 1) * kHalf;
+          const int buf = (c / CPT) & 1, half = (c % CPT) * kHalf;
           const bool isv = chunk_is_v(c);
 #pragma unroll
           for (int k = 0; k < PPT; ++k) {
@@ -495,14 +501,18 @@ prefill_kernel(Params p, const int32_t* __restrict__ cu_q, int causal, int nhg, 
             }
             *(uint4*)((isv ? s_v[buf] : s_k[buf]) + half + plds[k]) = x;
           }
-          if (c & 1) {
+          if (c % CPT == CPT - 1) {
             __syncthreads();
-            if constexpr (HPW > 1 && !wide) {
-              consume_all(c >> 1, buf);  // (a slot without a unit folds zeros, unread)
-            } else {
 #pragma unroll
-              for (int j = 0; j < HPW; ++j)
-                if (hon[j]) consume(c >> 1, buf, j, WIDE);
+            for (int st = 0; st < CPT / 2; ++st) {
+              const int tc = (c >> 1) - (CPT / 2 - 1) + st;
+              if constexpr (HPW > 1 && !wide) {
+                consume_all(tc, buf, 2 * st * kHalf);  // (a slot without a unit folds zeros, unread)
+              } else {
+#pragma unroll
+                for (int j = 0; j < HPW; ++j)
+                  if (hon[j]) consume(tc, buf, 2 * st * kHalf, j, WIDE);
+              }
             }
           }
         }
