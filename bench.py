@@ -443,10 +443,17 @@ def measure_prefill(k: int, torch, steps: int, warmup: int) -> dict:
 
 
 def roofline(wl: Workload, r: dict) -> dict:
-    achieved = wl.kv_bytes / (r["partition_kernel_us"] / 1e6) / 1e9
+    """The partition kernel against the HBM peak. Algorithmic bytes: K and V
+    of every distinct cached block once (the logical bytes unless blocks are
+    listed by several sequences, as in the prefix-shared batch, where a kernel
+    that reads a shared block once per listing moves more than it must)."""
+    alg = wl.unique_kv_bytes
+    achieved = alg / (r["partition_kernel_us"] / 1e6) / 1e9
     out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-           "kernel": f"partition_{wl.path_name}", "algorithmic_bytes_per_launch": wl.kv_bytes}
+           "kernel": f"partition_{wl.path_name}", "algorithmic_bytes_per_launch": alg}
+    if alg != wl.kv_bytes:
+        out["logical_bytes_per_launch"] = wl.kv_bytes
     try:
         with open(COUNTERS_FILE) as f:
             cnt = json.load(f)
