@@ -117,19 +117,21 @@ def test_prefill_last_row_is_the_decode(torch_cuda):
     assert np.abs(got[last] - dec).max() <= 3e-3
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 8, 2), (256, 12, 2)])
-def test_prefill_bf16_q_and_out(torch_cuda, D, Hq, Hkv):
+def test_prefill_bf16_q_and_out(torch_cuda, D, Hq, Hkv, dt):
     """q given in bf16 and out written in bf16 (PA_FLAG_QO_BF16): q is drawn as
     values bf16 holds exactly, so the oracle sees the same queries the kernel
     reads. bf16 q over bf16 K gives exact products (the scale is applied to the
-    fp32 scores), fp32 q goes in hi + lo parts with the scale folded in, so the
-    two calls differ in rounding only: each is within the K/V tolerance of the
-    oracle, the bf16 output plus half a bf16 ulp."""
+    fp32 scores); over fp16 K, and fp32 q over either, Q' goes in hi + lo
+    parts with the scale folded in, so the two calls differ in rounding only:
+    each is within the K/V tolerance of the oracle, the bf16 output plus half a
+    bf16 ulp."""
     from paged_gqa_decode_block_amd import workload as W
 
     torch = torch_cuda
-    rng = np.random.default_rng(1301 + D)
-    case, cu, q = _make(rng, Hq=Hq, Hkv=Hkv, D=D, bs=16, kv_dtype="bf16", klens=[200, 50, 700],
+    rng = np.random.default_rng(1301 + D + (dt == "f16"))
+    case, cu, q = _make(rng, Hq=Hq, Hkv=Hkv, D=D, bs=16, kv_dtype=dt, klens=[200, 50, 700],
                         qlens=[40, 50, 33])
     q = W.from_storage(W.to_storage(q, "bf16"), "bf16").astype(np.float32)
     want = _oracle(case, cu, q, True)
