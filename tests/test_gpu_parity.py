@@ -89,6 +89,8 @@ SMALL = [
     # rows, the largest group, 32-token blocks; and one head per group in fp16
     ("bf16_d256_g16_nhd_bs32", 2, 32, 2, 256, 32, "bf16", "NHD", [1500, 47], 512),
     ("f16_d256_g1", 3, 2, 2, 256, 16, "f16", "HND", [33, 700, 1], 64),
+    # the largest block: one 1024-token block holds a whole short sequence
+    ("bf16_d128_g2_bs1024", 3, 4, 2, 128, 1024, "bf16", "HND", [1500, 1024, 3], 512),
 ]
 
 
@@ -231,6 +233,26 @@ def test_stream_kernel_thousand_sequences(torch_cuda):
         got = run_gpu(torch_cuda, case, path="mfma_stream", partition_size=ps)
         assert np.isfinite(got).all(), ps
         assert np.abs(got - want).max() <= 3e-3, ps
+
+
+@pytest.mark.parametrize("B", [1024, 1025])
+def test_batch_at_and_past_the_stream_limit(torch_cuda, B):
+    """1024 sequences fill all 16 windows of the streaming kernel's scan; one
+    more and the library picks the grid kernel (the streaming kernel, asked
+    for by name, is refused before any launch)."""
+    rng = np.random.default_rng(810 + B)
+    L = rng.integers(0, 100, size=B)
+    case, _, _ = paged_case(rng, B=B, Hq=4, Hkv=2, D=64, bs=16, kv_dtype="bf16", seqlens=L)
+    want = run_oracle(case)
+    dev = to_device(torch_cuda, case)
+    paths = ["auto", "mfma_grid"] + (["mfma_stream"] if B <= 1024 else [])
+    for path in paths:
+        got = run_gpu(torch_cuda, case, dev, path=path, partition_size=64)
+        assert np.isfinite(got).all(), path
+        assert np.abs(got - want).max() <= 3e-3, path
+    if B > 1024:
+        with pytest.raises(RuntimeError):
+            run_gpu(torch_cuda, case, dev, path="mfma_stream", partition_size=64)
 
 
 def test_stream_kernel_continuation_chains(torch_cuda):
