@@ -74,6 +74,9 @@ CASES = [
     # units per wave on different tiles
     ("d128_g12", 24, 2, 128, 16, "bf16", "HND", [400, 90], [70, 90]),
     ("d64_g2_tiles", 8, 4, 64, 16, "bf16", "HND", [1000, 20], [200, 20]),
+    # the largest group and the largest block: two 8-head units' groups, a
+    # whole sequence inside one 1024-token block
+    ("d128_g16_bs1024", 32, 2, 128, 1024, "bf16", "HND", [1500, 300], [70, 300]),
 ]
 
 
